@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload switch_bf16]
+
+One step = one moe_forward call over the whole batch (router linear, top-k,
+dispatch, gate_up + SwiGLU grouped GEMM, down grouped GEMM, combine) with inputs
+and weights already resident in HBM.  Prints one JSON line: tokens/s for the
+workload, the roofline of the dominant kernel (timed live with HIP events on the
+library's stream), and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3
+METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % of MFMA bf16 / HBM peak"
+DOMINANT_SOURCES = ["sparse_mixture_experts_level_amd/csrc/gemm_stream.hip",
+                    "sparse_mixture_experts_level_amd/csrc/common.hpp"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="switch_bf16")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle's sample (0: pick by workload)")
+    return p.parse_args()
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this layer runs on a single "
+              f"MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_level_amd.ops as ops
+    from sparse_mixture_experts_level_amd import workloads as wl
+
+    dev = "cuda"
+    w = wl.get_workload(args.workload)
+    inp = wl.make_inputs(w, seed=args.seed, device=dev)
+    cap = ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor)
+    layer = ops.MoELayer(inp, cap, device=dev)
+    T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
+    s_bytes = 2 if w.dtype == "bf16" else 4
+
+    # ---------------------------------------------------------------- whole-path timing
+    for _ in range(args.warmup):
+        layer.forward(with_routing=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(with_routing=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = T * args.steps / (t1 - t0)
+
+    # ---------------------------------------------------------------- routing facts of this batch
+    layer.forward(with_routing=True)
+    torch.cuda.synchronize()
+    off = layer.routing["expert_offsets"].cpu().numpy().astype(np.int64)
+    kept = np.diff(off)
+    R = int(off[-1])
+    E_t = int((kept > 0).sum())
+
+    # ---------------------------------------------------------------- per-stage HIP-event timing
+    # The same kernels as moe_forward, called stage by stage through the C ABI, with events on
+    # the stream the library launches on (torch's current stream).
+    r = layer.routing
+    desc = layer.desc
+    Rmax = ops.moe_max_rows(desc)
+    x_perm = torch.empty((max(Rmax, 1), d), dtype=inp.x.dtype, device=dev)
+    hid = torch.empty((max(Rmax, 1), f), dtype=inp.x.dtype, device=dev)
+    y_perm = torch.empty((max(Rmax, 1), d), dtype=inp.x.dtype, device=dev)
+    out = torch.empty_like(inp.x)
+    grm = max(1, min(T, cap) if cap is not None else T)
+    stages = ["router_logits", "router_topk", "dispatch_permute", "gate_up_swiglu", "down", "combine"]
+    ev = {s: [] for s in stages}
+
+    def staged_step(record):
+        marks = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                marks.append(e)
+
+        mark()
+        ops.moe_router_logits(desc, inp.x, inp.w_router, inp.logit_offset, r["logits"])
+        mark()
+        ops.moe_router_topk(desc, r["logits"], r["topk_ids"], r["topk_gates"])
+        mark()
+        ops.moe_dispatch_permute(desc, r["topk_ids"], inp.x, r["expert_counts"], r["expert_offsets"], r["slot"],
+                                 r["row_token"], x_perm, layer.ws)
+        mark()
+        ops.moe_grouped_gate_up_swiglu(E, Rmax, grm, d, f, inp.x.dtype, x_perm, r["expert_offsets"], inp.w_gate_up,
+                                       hid)
+        mark()
+        ops.moe_grouped_down(E, Rmax, grm, d, f, inp.x.dtype, hid, r["expert_offsets"], inp.w_down, y_perm)
+        mark()
+        ops.moe_combine_unpermute(desc, y_perm, r["topk_ids"], r["topk_gates"], r["slot"], r["expert_offsets"], None,
+                                  out)
+        mark()
+        return marks
+
+    if fs == 0:
+        for _ in range(args.warmup):
+            staged_step(False)
+        all_marks = [staged_step(True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for marks in all_marks:
+            for i, s in enumerate(stages):
+                ev[s].append(marks[i].elapsed_time(marks[i + 1]) * 1e3)  # us
+        stage_us = {s: float(np.mean(v)) for s, v in ev.items()}
+    else:
+        stage_us = {}
+
+    # ---------------------------------------------------------------- roofline of the dominant kernel
+    gate_up_bytes = E_t * 2 * f * d * s_bytes + R * d * s_bytes + R * f * s_bytes
+    gate_up_flop = 2.0 * R * d * 2 * f
+    down_bytes = E_t * d * f * s_bytes + R * f * s_bytes + R * d * s_bytes
+    dom = "gate_up_swiglu"
+    dur = stage_us.get(dom)
+    roofline = None
+    if dur:
+        intensity = gate_up_flop / gate_up_bytes
+        peak_flops = (MFMA_BF16_PEAK_TFLOPS if s_bytes == 2 else MFMA_F32_PEAK_TFLOPS) * 1e12
+        ridge = peak_flops / (HBM_PEAK_GBS * 1e9)
+        if intensity < ridge:
+            achieved = gate_up_bytes / (dur * 1e-6) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        else:
+            achieved = gate_up_flop / (dur * 1e-6) / 1e12
+            peak = peak_flops / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4)}
+        roofline["kernel"] = "grouped_gemm_stream_kernel (gate_up + SwiGLU)" if grm <= 512 else "grouped gate_up GEMM"
+        roofline["avg_launch_us"] = round(dur, 2)
+        roofline["algorithmic_bytes"] = int(gate_up_bytes)
+        roofline["algorithmic_flop"] = int(gate_up_flop)
+        traffic = None
+        tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{args.workload}.json")
+        if os.path.exists(tfile):
+            with open(tfile) as fh:
+                tj = json.load(fh)
+            if tj.get("source_hash") == source_hash(DOMINANT_SOURCES):
+                traffic = tj.get("hbm_bytes_per_launch")
+        roofline["traffic"] = traffic
+
+    # whole-layer algorithmic work (for context next to the kernel roofline)
+    flop = 2.0 * T * d * E + 6.0 * R * d * f + 6.0 * T * d * fs
+    layer_bytes = s_bytes * (T * d + E * d + E_t * 3 * d * f + 3 * d * fs + T * d)
+    rt = max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), layer_bytes / (HBM_PEAK_GBS * 1e9))
+    layer_roofline = {"algorithmic_flop": flop, "algorithmic_bytes": layer_bytes, "roofline_ms": round(rt * 1e3, 4),
+                      "frac_of_roofline": round(rt * 1e3 / ms_per_step, 4),
+                      "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                      "mfma_frac": round(flop / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, cap, args.cpu_sample)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "num_tokens": T, "d_model": d,
+                   "num_experts": E, "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap,
+                   "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R)},
+        "roofline": roofline,
+        "layer_roofline": layer_roofline,
+        "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, cap, sample):
+    """The CPU oracle as it stands, on a bounded sample: routing over the whole batch,
+    expert FFN and combine for `sample` tokens.  Expert weights are copied to the host
+    before the clock starts; their float64 conversion inside the oracle is timed."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w = inp.workload
+    sample = sample or {"switch_bf16": 1024, "tiny_f32": 64}.get(w.name, 64)
+    sample = min(sample, w.num_tokens)
+    h = lambda t: None if t is None else t.float().cpu().numpy()
+    x, wr, off = h(inp.x), h(inp.w_router), h(inp.logit_offset)
+    tokens = np.sort(np.random.default_rng(0).choice(w.num_tokens, sample, replace=False))
+    # experts the sample can reach (host copies, untimed)
+    ids = oracle.topk_select(oracle.router_logits(x, wr, off), w.top_k)
+    need = sorted(set(ids[tokens].reshape(-1).tolist()))
+    gu = {e: h(inp.w_gate_up[e]) for e in need}
+    dn = {e: h(inp.w_down[e]) for e in need}
+    sgu, sd = h(inp.w_shared_gate_up), h(inp.w_shared_down)
+    torch.cuda.synchronize()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, wr, gu, dn, w.top_k, cap, off, w_shared_gate_up=sgu, w_shared_down=sd, tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample} of {w.num_tokens} tokens (routing and capacity fill over all {w.num_tokens}; "
+                      f"expert FFN and combine for the sample), {dt:.1f} s, NumPy float64",
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * moe.h — C ABI of libmoe.so, the MI355X (gfx950) forward pass of a sparse
+ * Mixture-of-Experts layer.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [SMoE]   "Sparse Mixture-of-Experts", bigdataschool.ru wiki.
+ *   [HF-MoE] "Что такое Mixture of Experts (MoE) в трансформерах: архитектура и
+ *            параллелизм", aglamov.biz.
+ *   [GW]     "Архитектура MoE в больших языковых моделях — кто такие «эксперты»?",
+ *            gerwin.io.
+ *
+ * The layer, per token t with hidden state x_t ([SMoE] "Роутер и top-k gating",
+ * "Expert capacity и capacity factor"; [HF-MoE] "Бэкенд для экспертов"):
+ *   logits_t = W_r x_t                       bias-free router linear
+ *   S_t      = top-k experts of softmax(logits_t); equal logits go to the lower index
+ *   g_tj     = p_t[S_tj] / sum_j' p_t[S_tj']   renormalised gates
+ *   capacity C = ceil(capacity_factor * T / E); assignments are filled first come,
+ *   first served in token order; overflow assignments are dropped
+ *   y_t      = [shared expert(x_t)] + sum_{kept j} g_tj * FFN_{S_tj}(x_t)
+ *   FFN_e(x) = W_d[e] (silu(W_g[e] x) * (W_u[e] x))   bias-free SwiGLU
+ *
+ * Conventions for every call below
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise; row-major;
+ *     allocated and owned by the caller.  The library keeps no pointer after a
+ *     call returns and never writes an input.
+ *   - Calls only enqueue work on `stream` (NULL = the default stream).  They never
+ *     synchronise the device and never allocate or free device memory: scratch
+ *     space comes from the caller's workspace `ws` of `ws_bytes` bytes.
+ *   - Arguments are validated on the host before any HIP call.  On failure the
+ *     call returns a non-zero moe_status, enqueues nothing, and moe_last_error()
+ *     describes the problem.  Errors raised by a kernel while it runs surface at
+ *     the caller's next synchronisation.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Stateless and thread-safe: calls on different streams may run concurrently
+ *     as long as their output and workspace buffers do not overlap.
+ *   - Element types: MOE_DTYPE_F32 (float) or MOE_DTYPE_BF16 (bfloat16 stored as
+ *     16-bit words) for x, all weights, expert outputs and the layer output.
+ *     Router logits and gates are always float.  Accumulation is float.
+ *   - bf16 layers need d_model and d_ff (and d_ff_shared) to be multiples of 64
+ *     (otherwise MOE_ERR_UNSUPPORTED); f32 layers accept any positive size.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_NO_CAPACITY (-1)
+#define MOE_MAX_EXPERTS 1024
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* bad argument: NULL/misaligned pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented: dtype, shape granularity */
+  MOE_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes is smaller than required */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Shape of one MoE layer call. */
+typedef struct moe_desc {
+  int32_t num_tokens;  /* T >= 0; T == 0 makes every call a no-op returning MOE_OK */
+  int32_t d_model;     /* d >= 1 */
+  int32_t d_ff;        /* f >= 1: hidden width of each routed expert */
+  int32_t num_experts; /* 1 <= E <= MOE_MAX_EXPERTS */
+  int32_t top_k;       /* 1 <= k <= E */
+  int32_t capacity;    /* C >= 0 rows per expert, or MOE_NO_CAPACITY */
+  int32_t d_ff_shared; /* 0: no shared expert; else hidden width of the always-on expert */
+  int32_t dtype;       /* moe_dtype */
+} moe_desc;
+
+/* Expert weights of one layer (device pointers).  Packed layouts follow the
+ * runtime layout of [HF-MoE] "Рефакторинг загрузки весов": gate_up_proj holds,
+ * per expert, the gate projection rows (w1) followed by the up projection rows
+ * (w3); down_proj holds w2. */
+typedef struct moe_weights {
+  const void *w_router;         /* [E, d] */
+  const void *w_gate_up;        /* [E, 2f, d]: rows 0..f-1 gate, f..2f-1 up */
+  const void *w_down;           /* [E, d, f] */
+  const void *w_shared_gate_up; /* [2 f_s, d] or NULL when d_ff_shared == 0 */
+  const void *w_shared_down;    /* [d, f_s]   or NULL when d_ff_shared == 0 */
+} moe_weights;
+
+/* Optional routing outputs of moe_forward (device pointers; any may be NULL,
+ * in which case the workspace holds that table instead). */
+typedef struct moe_routing {
+  float *logits;           /* [T, E] */
+  int32_t *topk_ids;       /* [T, k] */
+  float *topk_gates;       /* [T, k] */
+  int32_t *expert_counts;  /* [E]   demand per expert, before capacity */
+  int32_t *expert_offsets; /* [E+1] exclusive prefix sum of kept rows per expert */
+  int32_t *slot;           /* [T, k] slot inside the expert's buffer, -1 = dropped */
+  int32_t *row_token;      /* [R_max] token of each kept row (rows sorted by expert, then token) */
+} moe_routing;
+
+/* ---------------------------------------------------------------- host helpers */
+
+/* Expert capacity ceil(capacity_factor * T / E), evaluated in IEEE double in that
+ * order ([SMoE] "Expert capacity и capacity factor").  Returns MOE_NO_CAPACITY
+ * when capacity_factor <= 0 or is not finite; returns 0 for T < 0 or E < 1; values
+ * above INT32_MAX are clamped to INT32_MAX.  Host only, no device access. */
+int32_t moe_capacity(int32_t num_tokens, int32_t num_experts, double capacity_factor);
+
+/* Upper bound R_max on kept rows: min(T*k, E*C), or T*k without capacity.
+ * Returns -1 for an invalid descriptor. */
+int64_t moe_max_rows(const moe_desc *desc);
+
+/* Workspace bytes needed by moe_forward for this descriptor (enough for every
+ * other call with the same descriptor too).  Returns 0 for an invalid descriptor. */
+size_t moe_workspace_size(const moe_desc *desc);
+
+/* Workspace bytes needed by moe_grouped_swiglu_gemm. Returns 0 on invalid input. */
+size_t moe_grouped_gemm_workspace_size(int32_t num_groups, int64_t rows_max, int32_t d_ff, int32_t dtype);
+
+const char *moe_status_string(moe_status status);
+
+/* Detail of the last failure in the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------- hot path */
+
+/* Router linear ([SMoE] "Роутер и top-k gating": logits from a linear layer
+ * without bias).
+ *   x           [T, d] dtype
+ *   w_router    [E, d] dtype
+ *   logit_offset [E] float or NULL: added to every token's logits (synthetic skew)
+ *   logits      [T, E] float, written.  Accumulated in float. */
+moe_status moe_router_logits(const moe_desc *desc, const void *x, const void *w_router,
+                             const float *logit_offset, float *logits, hipStream_t stream);
+
+/* Softmax over experts, top-k and renormalised gates ([SMoE] "Роутер и top-k
+ * gating").  Selection ranks the logits (softmax is increasing); equal logits go
+ * to the lower expert index, and -0.0 equals +0.0.  Logits must be finite or -inf.
+ *   logits     [T, E] float
+ *   topk_ids   [T, k] int32, written in descending logit order
+ *   topk_gates [T, k] float, written: exp(l_j - l_max) / sum over the k selected */
+moe_status moe_router_topk(const moe_desc *desc, const float *logits, int32_t *topk_ids,
+                           float *topk_gates, hipStream_t stream);
+
+/* Capacity-limited dispatch ([SMoE] "Expert capacity и capacity factor",
+ * "Подводные камни collapse экспертов и token dropping"; [HF-MoE] "Бэкенд для
+ * экспертов": tokens sorted by expert id before one grouped GEMM).
+ * Walking assignments (t, j) in token order (t outer, j inner), each takes the next
+ * free slot of its expert while fewer than C are taken; later ones are dropped.
+ *   topk_ids       [T, k] int32, each in [0, E) (precondition, not checked on device)
+ *   x              [T, d] dtype, or NULL when x_perm is NULL
+ *   expert_counts  [E]   int32, written: demand per expert
+ *   expert_offsets [E+1] int32, written: offsets[0] = 0, offsets[e+1] - offsets[e] =
+ *                  min(counts[e], C)
+ *   slot           [T, k] int32, written: slot in the expert's buffer or -1 if dropped
+ *   row_token      [R_max] int32, written for rows < offsets[E]: the row's token
+ *   x_perm         [R_max, d] dtype or NULL: row offsets[e] + slot(t, j) = x[t];
+ *                  rows >= offsets[E] are left unspecified
+ *   ws             at least moe_workspace_size(desc) bytes */
+moe_status moe_dispatch_permute(const moe_desc *desc, const int32_t *topk_ids, const void *x,
+                                int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot,
+                                int32_t *row_token, void *x_perm, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Grouped SwiGLU expert FFN over rows sorted by group ([HF-MoE] "Бэкенд для
+ * экспертов": one grouped GEMM over tokens sorted by expert id; [HF-MoE]
+ * "Рефакторинг загрузки весов": packed gate_up / down layouts).
+ * For every group g and row r in [group_offsets[g], group_offsets[g+1]):
+ *   y_rows[r] = W_d[g] (silu(W_g[g] x_rows[r]) * (W_u[g] x_rows[r]))
+ * The hidden activation is rounded to dtype between the two projections.
+ *   num_groups      G >= 1 (<= MOE_MAX_EXPERTS)
+ *   rows_max        rows available in x_rows / y_rows; group_offsets[G] <= rows_max
+ *   group_rows_max  the caller's bound on any one group's rows (a tiling hint: larger
+ *                   groups are still computed correctly); >= 1
+ *   x_rows          [rows_max, d] dtype
+ *   group_offsets   [G+1] int32 DEVICE array, non-decreasing, group_offsets[0] >= 0
+ *   w_gate_up       [G, 2f, d] dtype;  w_down [G, d, f] dtype
+ *   y_rows          [rows_max, d] dtype, written for rows inside a group
+ *   ws              at least moe_grouped_gemm_workspace_size(G, rows_max, f, dtype) */
+moe_status moe_grouped_swiglu_gemm(int32_t num_groups, int64_t rows_max, int32_t group_rows_max,
+                                   int32_t d_model, int32_t d_ff, int32_t dtype, const void *x_rows,
+                                   const int32_t *group_offsets, const void *w_gate_up,
+                                   const void *w_down, void *y_rows, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* The two halves of moe_grouped_swiglu_gemm as single launches (same contracts):
+ *   moe_grouped_gate_up_swiglu: h_rows[r] = silu(W_g[g] x_rows[r]) * (W_u[g] x_rows[r]),
+ *     h_rows [rows_max, f] dtype (rounded to dtype);
+ *   moe_grouped_down: y_rows[r] = W_d[g] h_rows[r], y_rows [rows_max, d] dtype.
+ * No workspace.  Same sources as moe_grouped_swiglu_gemm. */
+moe_status moe_grouped_gate_up_swiglu(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
+                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *group_offsets,
+                                      const void *w_gate_up, void *h_rows, hipStream_t stream);
+moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
+                            int32_t d_ff, int32_t dtype, const void *h_rows, const int32_t *group_offsets,
+                            const void *w_down, void *y_rows, hipStream_t stream);
+
+/* Gate-weighted combine back to token order, without atomics ([SMoE] "Роутер и
+ * top-k gating": weighted sum of the selected experts' outputs; "Expert capacity и
+ * capacity factor": a dropped assignment contributes nothing; [GW] drawbacks item
+ * 5: shared expert added with weight 1).
+ *   out[t] = shared_out[t] (or 0) + sum_{j: slot[t,j] >= 0} topk_gates[t,j] *
+ *            y_perm[expert_offsets[topk_ids[t,j]] + slot[t,j]], summed in float in
+ *            order j = 0..k-1, then rounded to dtype.
+ *   y_perm [R_max, d] dtype; shared_out [T, d] dtype or NULL; out [T, d] dtype */
+moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const int32_t *topk_ids,
+                                 const float *topk_gates, const int32_t *slot,
+                                 const int32_t *expert_offsets, const void *shared_out, void *out,
+                                 hipStream_t stream);
+
+/* The whole layer: router linear, top-k, dispatch, routed grouped SwiGLU FFN, the
+ * shared expert if desc->d_ff_shared > 0, and combine.
+ *   x [T, d] dtype; logit_offset [E] float or NULL; out [T, d] dtype
+ *   routing: NULL, or a struct whose non-NULL fields receive the routing tables
+ *   ws: at least moe_workspace_size(desc) bytes */
+moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
+                       const float *logit_offset, void *out, moe_routing *routing, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

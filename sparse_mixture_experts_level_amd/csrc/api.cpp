@@ -1,0 +1,426 @@
+// C ABI of libmoe.so: host-side validation, workspace layout and the launch order of
+// the forward pass.  Declarations and contracts are in include/moe.h.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY_HIP(expr, what)                             \
+  do {                                                      \
+    moe_status st_ = hip_status((expr), (what));            \
+    if (st_ != MOE_OK) return st_;                          \
+  } while (0)
+#define MOE_TRY(expr)                 \
+  do {                                \
+    moe_status st_ = (expr);          \
+    if (st_ != MOE_OK) return st_;    \
+  } while (0)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_ptr(const void *p, const char *name) {
+  if (!p) return fail(MOE_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status check_opt_ptr(const void *p, const char *name) { return p ? check_ptr(p, name) : MOE_OK; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+moe_status check_dtype_dims(int32_t dtype, int64_t d, int64_t f, int64_t fs) {
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+  if (dtype == MOE_DTYPE_BF16) {
+    if (d % 64 || f % 64 || fs % 64)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d_model, d_ff and d_ff_shared to be multiples of 64 "
+                                       "(got %lld, %lld, %lld)", (long long)d, (long long)f, (long long)fs);
+  }
+  return MOE_OK;
+}
+
+moe_status check_desc(const moe_desc *desc) {
+  if (!desc) return fail(MOE_ERR_INVALID, "desc is NULL");
+  const moe_desc &D = *desc;
+  if (D.num_tokens < 0) return fail(MOE_ERR_INVALID, "num_tokens %d < 0", D.num_tokens);
+  if (D.d_model < 1 || D.d_ff < 1) return fail(MOE_ERR_INVALID, "d_model and d_ff must be >= 1");
+  if (D.num_experts < 1 || D.num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID, "num_experts %d outside [1, %d]", D.num_experts, MOE_MAX_EXPERTS);
+  if (D.top_k < 1 || D.top_k > D.num_experts)
+    return fail(MOE_ERR_INVALID, "top_k %d outside [1, num_experts=%d]", D.top_k, D.num_experts);
+  if (D.capacity < 0 && D.capacity != MOE_NO_CAPACITY)
+    return fail(MOE_ERR_INVALID, "capacity %d: must be >= 0 or MOE_NO_CAPACITY", D.capacity);
+  if (D.d_ff_shared < 0) return fail(MOE_ERR_INVALID, "d_ff_shared %d < 0", D.d_ff_shared);
+  if ((int64_t)D.num_tokens * D.top_k > INT32_MAX)
+    return fail(MOE_ERR_INVALID, "num_tokens * top_k exceeds INT32_MAX");
+  return check_dtype_dims(D.dtype, D.d_model, D.d_ff, D.d_ff_shared);
+}
+
+int64_t max_rows(const moe_desc &D) {
+  const int64_t tk = (int64_t)D.num_tokens * D.top_k;
+  if (D.capacity == MOE_NO_CAPACITY) return tk;
+  return std::min<int64_t>(tk, (int64_t)D.num_experts * D.capacity);
+}
+
+// Largest number of rows any one expert can hold: min(T, C).
+int32_t group_rows_bound(const moe_desc &D) {
+  if (D.capacity == MOE_NO_CAPACITY) return D.num_tokens;
+  return std::min(D.num_tokens, D.capacity);
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout of moe_forward; every region starts on a 256-byte boundary.
+struct Layout {
+  size_t logits, ids, gates, counts, offsets, slot, row_token, hist, x_perm, hidden, y_perm, sh_hidden, sh_out,
+      sh_offsets, total;
+};
+
+Layout layout(const moe_desc &D) {
+  Layout L{};
+  const size_t T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
+  const size_t R = (size_t)max_rows(D), s = elem_bytes(D.dtype);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.logits = take(T * E * 4);
+  L.ids = take(T * k * 4);
+  L.gates = take(T * k * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.slot = take(T * k * 4);
+  L.row_token = take(R * 4);
+  L.hist = take(moe::dispatch_workspace_bytes((int)T, (int)E));
+  L.x_perm = take(R * d * s);
+  L.hidden = take(R * f * s);
+  L.y_perm = take(R * d * s);
+  L.sh_hidden = take(fs ? T * fs * s : 0);
+  L.sh_out = take(fs ? T * d * s : 0);
+  L.sh_offsets = take(fs ? 2 * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) {
+  return reinterpret_cast<P *>(static_cast<uint8_t *>(ws) + off);
+}
+
+moe::GroupedGemmArgs projection_args(int32_t G, int32_t group_rows_max, int32_t d, int32_t f, const void *in,
+                                     const int32_t *offsets, const void *w, void *out, bool gate_up) {
+  moe::GroupedGemmArgs a{};
+  a.A = in;
+  a.offsets = offsets;
+  a.num_groups = G;
+  a.group_rows_max = group_rows_max;
+  a.W = w;
+  a.w_group_stride = gate_up ? (int64_t)2 * f * d : (int64_t)d * f;
+  a.n_out = gate_up ? f : d;
+  a.K = gate_up ? d : f;
+  a.out = out;
+  a.swiglu = gate_up;
+  return a;
+}
+
+moe_status run_projection(const moe::GroupedGemmArgs &a, int32_t dtype, hipStream_t s, const char *what) {
+  return hip_status(dtype == MOE_DTYPE_BF16 ? moe::launch_grouped_gemm_bf16(a, s) : moe::launch_grouped_gemm_f32(a, s),
+                    what);
+}
+
+moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype) {
+  if (G < 1 || G > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID, "num_groups %d outside [1, %d]", G, MOE_MAX_EXPERTS);
+  if (rows_max < 0 || rows_max > INT32_MAX) return fail(MOE_ERR_INVALID, "rows_max %lld", (long long)rows_max);
+  if (group_rows_max < 1) return fail(MOE_ERR_INVALID, "group_rows_max %d < 1", group_rows_max);
+  if (d < 1 || f < 1) return fail(MOE_ERR_INVALID, "d_model and d_ff must be >= 1");
+  return check_dtype_dims(dtype, d, f, 0);
+}
+
+moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
+                           const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
+                           void *y_rows, void *hidden, hipStream_t s) {
+  (void)rows_max;
+  MOE_TRY(run_projection(projection_args(G, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true), dtype, s,
+                         "gate_up grouped GEMM"));
+  MOE_TRY(run_projection(projection_args(G, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false), dtype, s,
+                         "down grouped GEMM"));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int32_t num_tokens, int32_t num_experts, double capacity_factor) {
+  if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return MOE_NO_CAPACITY;
+  if (num_tokens < 0 || num_experts < 1) return 0;
+  const double c = std::ceil(capacity_factor * (double)num_tokens / (double)num_experts);
+  if (c >= (double)INT32_MAX) return INT32_MAX;
+  return (int32_t)c;
+}
+
+int64_t moe_max_rows(const moe_desc *desc) {
+  if (check_desc(desc) != MOE_OK) return -1;
+  return max_rows(*desc);
+}
+
+size_t moe_workspace_size(const moe_desc *desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return layout(*desc).total;
+}
+
+size_t moe_grouped_gemm_workspace_size(int32_t num_groups, int64_t rows_max, int32_t d_ff, int32_t dtype) {
+  if (num_groups < 1 || num_groups > MOE_MAX_EXPERTS || rows_max < 0 || d_ff < 1) return 0;
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return 0;
+  return align_up((size_t)std::max<int64_t>(rows_max, 1) * d_ff * elem_bytes(dtype));
+}
+
+const char *moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported dtype or shape";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+  }
+  return "unknown moe_status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_router_logits(const moe_desc *desc, const void *x, const void *w_router, const float *logit_offset,
+                             float *logits, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_router, "w_router"));
+  MOE_TRY(check_opt_ptr(logit_offset, "logit_offset"));
+  MOE_TRY(check_ptr(logits, "logits"));
+  if (D.dtype == MOE_DTYPE_BF16)
+    MOE_TRY_HIP(moe::launch_router_logits_bf16(x, w_router, logit_offset, logits, D.num_tokens, D.d_model,
+                                               D.num_experts, stream), "router logits");
+  else
+    MOE_TRY_HIP(moe::launch_router_logits_f32(static_cast<const float *>(x), static_cast<const float *>(w_router),
+                                              logit_offset, logits, D.num_tokens, D.d_model, D.num_experts, stream),
+                "router logits");
+  return ok();
+}
+
+moe_status moe_router_topk(const moe_desc *desc, const float *logits, int32_t *topk_ids, float *topk_gates,
+                           hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+  MOE_TRY(check_ptr(topk_gates, "topk_gates"));
+  MOE_TRY_HIP(moe::launch_router_topk(logits, D.num_tokens, D.num_experts, D.top_k, topk_ids, topk_gates, stream),
+              "router top-k");
+  return ok();
+}
+
+moe_status moe_dispatch_permute(const moe_desc *desc, const int32_t *topk_ids, const void *x, int32_t *expert_counts,
+                                int32_t *expert_offsets, int32_t *slot, int32_t *row_token, void *x_perm, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+  MOE_TRY(check_ptr(expert_counts, "expert_counts"));
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(row_token, "row_token"));
+  MOE_TRY(check_opt_ptr(x_perm, "x_perm"));
+  if (x_perm) MOE_TRY(check_ptr(x, "x"));
+  const size_t need = moe::dispatch_workspace_bytes(D.num_tokens, D.num_experts);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+  MOE_TRY_HIP(moe::launch_dispatch(topk_ids, D.num_tokens, D.top_k, D.num_experts, D.capacity, expert_counts,
+                                   expert_offsets, slot, row_token, static_cast<int32_t *>(ws), stream),
+              "dispatch");
+  if (x_perm)
+    MOE_TRY_HIP(moe::launch_gather_rows(x, row_token, expert_offsets + D.num_experts, max_rows(D), D.d_model,
+                                        (int)elem_bytes(D.dtype), x_perm, stream),
+                "gather rows");
+  return ok();
+}
+
+moe_status moe_grouped_swiglu_gemm(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
+                                   int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *group_offsets,
+                                   const void *w_gate_up, const void *w_down, void *y_rows, void *ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  MOE_TRY(check_projection(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype));
+  if (rows_max == 0) return ok();
+  MOE_TRY(check_ptr(x_rows, "x_rows"));
+  MOE_TRY(check_ptr(group_offsets, "group_offsets"));
+  MOE_TRY(check_ptr(w_gate_up, "w_gate_up"));
+  MOE_TRY(check_ptr(w_down, "w_down"));
+  MOE_TRY(check_ptr(y_rows, "y_rows"));
+  const size_t need = moe_grouped_gemm_workspace_size(num_groups, rows_max, d_ff, dtype);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "grouped GEMM needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+  MOE_TRY(run_grouped_ffn(num_groups, rows_max, std::min<int64_t>(group_rows_max, rows_max), d_model, d_ff, dtype,
+                          x_rows, group_offsets, w_gate_up, w_down, y_rows, ws, stream));
+  return ok();
+}
+
+moe_status moe_grouped_gate_up_swiglu(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
+                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *group_offsets,
+                                      const void *w_gate_up, void *h_rows, hipStream_t stream) {
+  MOE_TRY(check_projection(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype));
+  if (rows_max == 0) return ok();
+  MOE_TRY(check_ptr(x_rows, "x_rows"));
+  MOE_TRY(check_ptr(group_offsets, "group_offsets"));
+  MOE_TRY(check_ptr(w_gate_up, "w_gate_up"));
+  MOE_TRY(check_ptr(h_rows, "h_rows"));
+  MOE_TRY(run_projection(projection_args(num_groups, (int32_t)std::min<int64_t>(group_rows_max, rows_max), d_model,
+                                         d_ff, x_rows, group_offsets, w_gate_up, h_rows, true),
+                         dtype, stream, "gate_up grouped GEMM"));
+  return ok();
+}
+
+moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
+                            int32_t d_ff, int32_t dtype, const void *h_rows, const int32_t *group_offsets,
+                            const void *w_down, void *y_rows, hipStream_t stream) {
+  MOE_TRY(check_projection(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype));
+  if (rows_max == 0) return ok();
+  MOE_TRY(check_ptr(h_rows, "h_rows"));
+  MOE_TRY(check_ptr(group_offsets, "group_offsets"));
+  MOE_TRY(check_ptr(w_down, "w_down"));
+  MOE_TRY(check_ptr(y_rows, "y_rows"));
+  MOE_TRY(run_projection(projection_args(num_groups, (int32_t)std::min<int64_t>(group_rows_max, rows_max), d_model,
+                                         d_ff, h_rows, group_offsets, w_down, y_rows, false),
+                         dtype, stream, "down grouped GEMM"));
+  return ok();
+}
+
+moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const int32_t *topk_ids,
+                                 const float *topk_gates, const int32_t *slot, const int32_t *expert_offsets,
+                                 const void *shared_out, void *out, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_opt_ptr(y_perm, "y_perm"));
+  if (!y_perm && max_rows(D) > 0) return fail(MOE_ERR_INVALID, "y_perm is NULL");
+  MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+  MOE_TRY(check_ptr(topk_gates, "topk_gates"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+  MOE_TRY(check_opt_ptr(shared_out, "shared_out"));
+  MOE_TRY(check_ptr(out, "out"));
+  MOE_TRY_HIP(moe::launch_combine(y_perm, topk_ids, topk_gates, slot, expert_offsets, shared_out, out, D.num_tokens,
+                                  D.d_model, D.top_k, D.dtype == MOE_DTYPE_BF16, stream),
+              "combine");
+  return ok();
+}
+
+moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, const float *logit_offset,
+                       void *out, moe_routing *routing, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (!weights) return fail(MOE_ERR_INVALID, "weights is NULL");
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(out, "out"));
+  MOE_TRY(check_ptr(weights->w_router, "w_router"));
+  MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
+  MOE_TRY(check_ptr(weights->w_down, "w_down"));
+  MOE_TRY(check_opt_ptr(logit_offset, "logit_offset"));
+  if (D.d_ff_shared > 0) {
+    MOE_TRY(check_ptr(weights->w_shared_gate_up, "w_shared_gate_up"));
+    MOE_TRY(check_ptr(weights->w_shared_down, "w_shared_down"));
+  }
+  moe_routing R{};
+  if (routing) {
+    R = *routing;
+    MOE_TRY(check_opt_ptr(R.logits, "routing.logits"));
+    MOE_TRY(check_opt_ptr(R.topk_ids, "routing.topk_ids"));
+    MOE_TRY(check_opt_ptr(R.topk_gates, "routing.topk_gates"));
+    MOE_TRY(check_opt_ptr(R.expert_counts, "routing.expert_counts"));
+    MOE_TRY(check_opt_ptr(R.expert_offsets, "routing.expert_offsets"));
+    MOE_TRY(check_opt_ptr(R.slot, "routing.slot"));
+    MOE_TRY(check_opt_ptr(R.row_token, "routing.row_token"));
+  }
+  const Layout L = layout(D);
+  if (!ws || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes, got %zu", L.total, ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+
+  float *logits = R.logits ? R.logits : at<float>(ws, L.logits);
+  int32_t *ids = R.topk_ids ? R.topk_ids : at<int32_t>(ws, L.ids);
+  float *gates = R.topk_gates ? R.topk_gates : at<float>(ws, L.gates);
+  int32_t *counts = R.expert_counts ? R.expert_counts : at<int32_t>(ws, L.counts);
+  int32_t *offsets = R.expert_offsets ? R.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t *slot = R.slot ? R.slot : at<int32_t>(ws, L.slot);
+  int32_t *row_token = R.row_token ? R.row_token : at<int32_t>(ws, L.row_token);
+  const int T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
+  const bool bf = D.dtype == MOE_DTYPE_BF16;
+  const int64_t rmax = max_rows(D);
+  void *x_perm = at<void>(ws, L.x_perm);
+  void *y_perm = at<void>(ws, L.y_perm);
+
+  if (bf)
+    MOE_TRY_HIP(moe::launch_router_logits_bf16(x, weights->w_router, logit_offset, logits, T, d, E, stream),
+                "router logits");
+  else
+    MOE_TRY_HIP(moe::launch_router_logits_f32(static_cast<const float *>(x),
+                                              static_cast<const float *>(weights->w_router), logit_offset, logits, T,
+                                              d, E, stream),
+                "router logits");
+  MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream), "router top-k");
+  MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, counts, offsets, slot, row_token, at<int32_t>(ws, L.hist),
+                                   stream),
+              "dispatch");
+  if (rmax > 0) {
+    MOE_TRY_HIP(moe::launch_gather_rows(x, row_token, offsets + E, rmax, d, (int)elem_bytes(D.dtype), x_perm, stream),
+                "gather rows");
+    MOE_TRY(run_grouped_ffn(E, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x_perm, offsets,
+                            weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden), stream));
+  }
+  const void *shared = nullptr;
+  if (fs > 0) {
+    int32_t *sh_off = at<int32_t>(ws, L.sh_offsets);
+    MOE_TRY_HIP(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "shared offsets");
+    MOE_TRY(run_grouped_ffn(1, T, T, d, fs, D.dtype, x, sh_off, weights->w_shared_gate_up, weights->w_shared_down,
+                            at<void>(ws, L.sh_out), at<void>(ws, L.sh_hidden), stream));
+    shared = at<void>(ws, L.sh_out);
+  }
+  MOE_TRY_HIP(moe::launch_combine(y_perm, ids, gates, slot, offsets, shared, out, T, d, k, bf, stream), "combine");
+  return ok();
+}
+
+}  // extern "C"

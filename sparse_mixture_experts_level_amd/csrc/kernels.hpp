@@ -1,0 +1,60 @@
+// Host-side launchers of the gfx950 kernels (defined in the .hip files).  Each
+// launcher only enqueues work on `stream` and returns the launch status; argument
+// validation happens in api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (router.hip)
+hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const float *offset, float *logits,
+                                     int T, int d, int E, hipStream_t s);
+hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits,
+                                    int T, int d, int E, hipStream_t s);
+hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s);
+
+// ---- dispatch (dispatch.hip)
+struct DispatchPlan {
+  int tokens_per_block;
+  int num_blocks;
+};
+DispatchPlan dispatch_plan(int T);
+size_t dispatch_workspace_bytes(int T, int E);
+hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int cap /* <0: none */, int32_t *counts,
+                           int32_t *offsets, int32_t *slot, int32_t *row_token, int32_t *hist_ws, hipStream_t s);
+hipError_t launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *offsets_end, int64_t rows_max,
+                              int d, int elem_bytes, void *x_perm, hipStream_t s);
+
+// ---- grouped expert GEMMs (gemm_stream.hip, gemm_f32.hip)
+// Problem: for group g, rows [offsets[g], offsets[g+1]) of A [rows, K] times the
+// group's weight W_g [N_w, K] (K contiguous).  With swiglu, N_w = 2 * n_out and
+// out[r, n] = silu(A_r . W_g[n]) * (A_r . W_g[n_out + n]); otherwise N_w = n_out and
+// out[r, n] = A_r . W_g[n].  `w_group_stride` is in elements.
+struct GroupedGemmArgs {
+  const void *A;
+  const int32_t *offsets;
+  int num_groups;
+  int group_rows_max;  // tiling hint
+  const void *W;
+  int64_t w_group_stride;
+  int n_out;
+  int K;
+  void *out;
+  bool swiglu;
+};
+hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
+hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);
+hipError_t launch_grouped_gemm_f32(const GroupedGemmArgs &a, hipStream_t s);
+
+// ---- combine (combine.hip)
+hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *gates, const int32_t *slot,
+                          const int32_t *offsets, const void *shared, void *out, int T, int d, int k, bool bf16,
+                          hipStream_t s);
+
+// ---- small utilities (combine.hip)
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v0, int32_t step, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,257 @@
+// Router of the sparse MoE layer on gfx950: bias-free linear (logits), then softmax,
+// top-k and renormalised gates ("Sparse Mixture-of-Experts", bigdataschool.ru wiki,
+// section "Роутер и top-k gating").
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------ logits, bf16
+//
+// logits[T, E] = x[T, d] . W_r[E, d]^T (+ offset), bf16 MFMA with float accumulate.
+// A workgroup owns 64 tokens (16 per wave) and every expert, in chunks of up to 256
+// experts.  The router weight chunk for 64 values of d is staged in LDS (double
+// buffered) and shared by the four waves; each wave streams its own 16 token rows
+// straight from HBM into MFMA operand registers.
+namespace {
+
+constexpr int RT_TOK = 64;   // tokens per workgroup
+constexpr int RT_KC = 64;    // d values per LDS stage (8 x 16-byte chunks per row)
+constexpr int RT_EMAX = 256; // experts per pass
+
+template <int NSUB>  // 16-expert subtiles per pass
+__global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *__restrict__ x,
+                                                                 const bf16_t *__restrict__ w,
+                                                                 const float *__restrict__ offset,
+                                                                 float *__restrict__ logits, int T, int d, int E,
+                                                                 int e_base) {
+  constexpr int EC = NSUB * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][EC * RT_KC * 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT_TOK + wave * 16;
+  const int trow = min(t0 + (lane & 15), T - 1);
+  const bf16_t *xrow = x + (size_t)trow * d + (lane >> 4) * 8;
+
+  // staging: EC rows x 8 chunks; each thread moves EC*8/256 chunks per stage
+  constexpr int PER_T = (EC * 8 + 255) / 256;
+  u32x4 stage[PER_T];
+  auto load_stage = [&](int kc) {
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) {
+      const int q = tid + 256 * r;
+      const int row = q >> 3, c = q & 7;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q < EC * 8 && e_base + row < E) v = ldg16(w + (size_t)(e_base + row) * d + kc + c * 8);
+      stage[r] = v;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) {
+      const int q = tid + 256 * r;
+      if (q < EC * 8) {
+        const int row = q >> 3, c = q & 7;
+        *reinterpret_cast<u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]) = stage[r];
+      }
+    }
+  };
+
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = d / RT_KC;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    const int kc = it * RT_KC;
+    const u32x4 a0 = ldg16(xrow + kc), a1 = ldg16(xrow + kc + 32);
+    if (it + 1 < nk) load_stage(kc + RT_KC);
+#pragma unroll
+    for (int n = 0; n < NSUB; ++n) {
+      const int row = n * 16 + (lane & 15);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = s * 4 + (lane >> 4);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]);
+        acc[n] = mfma16(s == 0 ? a0 : a1, b, acc[n]);
+      }
+    }
+    if (it + 1 < nk) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // C layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4) + i.
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) {
+    const int e = e_base + n * 16 + (lane & 15);
+    if (e >= E) continue;
+    const float off = offset ? offset[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + (lane >> 4) * 4 + i;
+      if (t < T) logits[(size_t)t * E + e] = acc[n][i] + off;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void router_logits_f32_kernel(const float *__restrict__ x,
+                                                                const float *__restrict__ w,
+                                                                const float *__restrict__ offset,
+                                                                float *__restrict__ logits, int T, int d, int E) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * E) return;
+  const int t = int(i / E), e = int(i % E);
+  const float *xr = x + (size_t)t * d;
+  const float *wr = w + (size_t)e * d;
+  float s = 0.f;
+  for (int j = 0; j < d; ++j) s = fmaf(xr[j], wr[j], s);
+  logits[i] = s + (offset ? offset[e] : 0.f);
+}
+
+// ------------------------------------------------------------------ top-k
+//
+// One wavefront per token.  Each lane holds VPL logits (expert = lane + 64 * v).
+// A key orders (logit desc, expert asc): the logit's bits mapped to an unsigned
+// order (with -0.0 folded onto +0.0) in the high word, (0xffff - expert) in the low
+// word; k rounds of a wavefront max-reduction pick the experts in descending order.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(ord) << 32) | uint32_t(0xffff - e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = uint32_t(key >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor(uint32_t(v), m, 64);
+    const uint32_t hi = __shfl_xor(uint32_t(v >> 32), m, 64);
+    const uint64_t o = (uint64_t(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+constexpr int TK_WAVES = 4;
+
+// Every lane follows the k rounds identically (same winner, same running sum of
+// exp(l_j - l_max) in the same order); lane (j mod 64) keeps winner j in register
+// slot j / 64 and writes it at the end.  No LDS and no barriers.
+template <int VPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                          int32_t *__restrict__ ids, float *__restrict__ gates) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * TK_WAVES + wave;
+  if (t >= T) return;
+  const float *row = logits + (size_t)t * E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + 64 * v;
+    key[v] = e < E ? topk_key(row[e], e) : 0ull;  // 0 ranks below every real key
+  }
+  int my_id[VPL];
+  float my_z[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    my_id[v] = 0;
+    my_z[v] = 0.f;
+  }
+  float m = 0.f, sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max_u64(best);
+    const int e = 0xffff - int(best & 0xffffu);
+    const float val = key_value(best);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (key[v] == best) key[v] = 0ull;
+    if (j == 0) m = val;
+    const float z = expf(val - m);
+    sum += z;
+    if ((j & 63) == lane) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (v == (j >> 6)) {
+          my_id[v] = e;
+          my_z[v] = z;
+        }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int j = v * 64 + lane;
+    if (j < k) {
+      ids[(size_t)t * k + j] = my_id[v];
+      gates[(size_t)t * k + j] = my_z[v] / sum;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T,
+                                     int d, int E, hipStream_t s) {
+  const int grid = (T + RT_TOK - 1) / RT_TOK;
+  for (int e0 = 0; e0 < E; e0 += RT_EMAX) {
+    const int ec = min(RT_EMAX, E - e0);
+    const int nsub = (ec + 15) / 16;
+    const bf16_t *xp = static_cast<const bf16_t *>(x);
+    const bf16_t *wp = static_cast<const bf16_t *>(w_router);
+#define RT_CASE(N)                                                                                      \
+  case N:                                                                                               \
+    hipLaunchKernelGGL(router_logits_bf16_kernel<N>, dim3(grid), dim3(256), 0, s, xp, wp, offset, logits, \
+                       T, d, E, e0);                                                                    \
+    break;
+    switch (nsub <= 1 ? 1 : nsub <= 2 ? 2 : nsub <= 4 ? 4 : nsub <= 8 ? 8 : 16) {
+      RT_CASE(1)
+      RT_CASE(2)
+      RT_CASE(4)
+      RT_CASE(8)
+      RT_CASE(16)
+    }
+#undef RT_CASE
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits, int T,
+                                    int d, int E, hipStream_t s) {
+  const int64_t n = (int64_t)T * E;
+  const int grid = int((n + 255) / 256);
+  hipLaunchKernelGGL(router_logits_f32_kernel, dim3(grid), dim3(256), 0, s, x, w_router, offset, logits, T, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s) {
+  const int grid = (T + TK_WAVES - 1) / TK_WAVES;
+  const int vpl = (E + 63) / 64;
+#define TK_CASE(V)                                                                                          \
+  case V:                                                                                                   \
+    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates); \
+    break;
+  switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
+    TK_CASE(1)
+    TK_CASE(2)
+    TK_CASE(4)
+    TK_CASE(8)
+    TK_CASE(16)
+  }
+#undef TK_CASE
+  return hipGetLastError();
+}
+
+}  // namespace moe

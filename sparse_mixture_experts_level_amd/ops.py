@@ -1,0 +1,245 @@
+"""Thin Python binding of libmoe.so (C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors living on the GPU (torch provides device
+memory and the current HIP stream); their data pointers are handed to the C
+entry points of the same names.  The library must be built
+(``python -m sparse_mixture_experts_level_amd.build``); a missing library raises
+instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_NO_CAPACITY = -1
+MOE_MAX_EXPERTS = 1024
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+
+SYMBOLS = [
+    "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_grouped_gemm_workspace_size",
+    "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
+    "moe_dispatch_permute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
+    "moe_combine_unpermute", "moe_forward",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func} failed: {detail} (status {status})")
+        self.status = status
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("w_shared_gate_up", ctypes.c_void_p), ("w_shared_down", ctypes.c_void_p)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_gates", ctypes.c_void_p),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+                ("row_token", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmoe.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_level_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    dp = ctypes.POINTER(MoeDesc)
+    L.moe_capacity.argtypes, L.moe_capacity.restype = [i32, i32, ctypes.c_double], i32
+    L.moe_max_rows.argtypes, L.moe_max_rows.restype = [dp], i64
+    L.moe_workspace_size.argtypes, L.moe_workspace_size.restype = [dp], sz
+    L.moe_grouped_gemm_workspace_size.argtypes, L.moe_grouped_gemm_workspace_size.restype = [i32, i64, i32, i32], sz
+    L.moe_status_string.argtypes, L.moe_status_string.restype = [st], ctypes.c_char_p
+    L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
+    L.moe_router_logits.argtypes, L.moe_router_logits.restype = [dp, vp, vp, vp, vp, vp], st
+    L.moe_router_topk.argtypes, L.moe_router_topk.restype = [dp, vp, vp, vp, vp], st
+    L.moe_dispatch_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_permute.restype = st
+    L.moe_grouped_swiglu_gemm.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_grouped_swiglu_gemm.restype = st
+    L.moe_grouped_gate_up_swiglu.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_grouped_gate_up_swiglu.restype = st
+    L.moe_grouped_down.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_grouped_down.restype = st
+    L.moe_combine_unpermute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_combine_unpermute.restype = st
+    L.moe_forward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz, vp]
+    L.moe_forward.restype = st
+    _lib = L
+    return L
+
+
+def _check(status: int, func: str) -> None:
+    if status != MOE_OK:
+        L = lib()
+        raise MoEError(status, func, L.moe_last_error().decode() or L.moe_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MOE_DTYPE_F32
+    if dt == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def make_desc(num_tokens, d_model, d_ff, num_experts, top_k, capacity, d_ff_shared=0, dtype=torch.bfloat16) -> MoeDesc:
+    return MoeDesc(int(num_tokens), int(d_model), int(d_ff), int(num_experts), int(top_k),
+                   MOE_NO_CAPACITY if capacity is None else int(capacity), int(d_ff_shared),
+                   dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype))
+
+
+# ------------------------------------------------------------------------ host helpers
+
+def moe_capacity(num_tokens: int, num_experts: int, capacity_factor: Optional[float]) -> Optional[int]:
+    c = lib().moe_capacity(int(num_tokens), int(num_experts), 0.0 if capacity_factor is None else float(capacity_factor))
+    return None if c == MOE_NO_CAPACITY else int(c)
+
+
+def moe_max_rows(desc: MoeDesc) -> int:
+    return int(lib().moe_max_rows(ctypes.byref(desc)))
+
+
+def moe_workspace_size(desc: MoeDesc) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(desc)))
+
+
+def moe_grouped_gemm_workspace_size(num_groups: int, rows_max: int, d_ff: int, dtype) -> int:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().moe_grouped_gemm_workspace_size(int(num_groups), int(rows_max), int(d_ff), code))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------ hot path
+
+def moe_router_logits(desc, x, w_router, logit_offset, logits, stream=None) -> None:
+    _check(lib().moe_router_logits(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(logit_offset), _ptr(logits),
+                                   _stream(stream)), "moe_router_logits")
+
+
+def moe_router_topk(desc, logits, topk_ids, topk_gates, stream=None) -> None:
+    _check(lib().moe_router_topk(ctypes.byref(desc), _ptr(logits), _ptr(topk_ids), _ptr(topk_gates),
+                                 _stream(stream)), "moe_router_topk")
+
+
+def moe_dispatch_permute(desc, topk_ids, x, expert_counts, expert_offsets, slot, row_token, x_perm, ws,
+                         stream=None) -> None:
+    _check(lib().moe_dispatch_permute(ctypes.byref(desc), _ptr(topk_ids), _ptr(x), _ptr(expert_counts),
+                                      _ptr(expert_offsets), _ptr(slot), _ptr(row_token), _ptr(x_perm), _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_dispatch_permute")
+
+
+def moe_grouped_swiglu_gemm(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, x_rows, group_offsets,
+                            w_gate_up, w_down, y_rows, ws, stream=None) -> None:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    _check(lib().moe_grouped_swiglu_gemm(int(num_groups), int(rows_max), int(group_rows_max), int(d_model), int(d_ff),
+                                         code, _ptr(x_rows), _ptr(group_offsets), _ptr(w_gate_up), _ptr(w_down),
+                                         _ptr(y_rows), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                         _stream(stream)), "moe_grouped_swiglu_gemm")
+
+
+def moe_grouped_gate_up_swiglu(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, x_rows, group_offsets,
+                               w_gate_up, h_rows, stream=None) -> None:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    _check(lib().moe_grouped_gate_up_swiglu(int(num_groups), int(rows_max), int(group_rows_max), int(d_model),
+                                            int(d_ff), code, _ptr(x_rows), _ptr(group_offsets), _ptr(w_gate_up),
+                                            _ptr(h_rows), _stream(stream)), "moe_grouped_gate_up_swiglu")
+
+
+def moe_grouped_down(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, h_rows, group_offsets, w_down,
+                     y_rows, stream=None) -> None:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    _check(lib().moe_grouped_down(int(num_groups), int(rows_max), int(group_rows_max), int(d_model), int(d_ff), code,
+                                  _ptr(h_rows), _ptr(group_offsets), _ptr(w_down), _ptr(y_rows), _stream(stream)),
+           "moe_grouped_down")
+
+
+def moe_combine_unpermute(desc, y_perm, topk_ids, topk_gates, slot, expert_offsets, shared_out, out,
+                          stream=None) -> None:
+    _check(lib().moe_combine_unpermute(ctypes.byref(desc), _ptr(y_perm), _ptr(topk_ids), _ptr(topk_gates), _ptr(slot),
+                                       _ptr(expert_offsets), _ptr(shared_out), _ptr(out), _stream(stream)),
+           "moe_combine_unpermute")
+
+
+def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, routing: Optional[dict] = None,
+                w_shared_gate_up=None, w_shared_down=None, stream=None) -> None:
+    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down))
+    R = None
+    if routing is not None:
+        R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
+    _check(lib().moe_forward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(logit_offset), _ptr(out),
+                             ctypes.byref(R) if R is not None else None, _ptr(ws),
+                             0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+class MoELayer:
+    """Holds one layer's device tensors and a workspace, and runs moe_forward.
+
+    Convenience only: allocation happens here, once, never inside a forward call."""
+
+    def __init__(self, inputs, capacity, device="cuda"):
+        w = inputs.workload
+        self.inputs = inputs
+        self.desc = make_desc(w.num_tokens, w.d_model, w.d_ff, w.num_experts, w.top_k, capacity,
+                              w.d_ff_shared, w.torch_dtype)
+        self.ws = workspace(moe_workspace_size(self.desc), device)
+        self.out = torch.empty_like(inputs.x)
+        T, E, k = w.num_tokens, w.num_experts, w.top_k
+        R = moe_max_rows(self.desc)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.routing = {
+            "logits": torch.empty((T, E), dtype=torch.float32, device=device),
+            "topk_ids": torch.empty((T, k), **i32),
+            "topk_gates": torch.empty((T, k), dtype=torch.float32, device=device),
+            "expert_counts": torch.empty((E,), **i32),
+            "expert_offsets": torch.empty((E + 1,), **i32),
+            "slot": torch.empty((T, k), **i32),
+            "row_token": torch.empty((max(R, 1),), **i32),
+        }
+
+    def forward(self, with_routing=True, stream=None):
+        i = self.inputs
+        moe_forward(self.desc, i.w_router, i.w_gate_up, i.w_down, i.x, i.logit_offset, self.out, self.ws,
+                    routing=self.routing if with_routing else None, w_shared_gate_up=i.w_shared_gate_up,
+                    w_shared_down=i.w_shared_down, stream=stream)
+        return self.out

@@ -1,0 +1,232 @@
+"""GPU parity of each hot-path stage against the CPU oracle, called through the C ABI.
+
+Sizes span several tiles and ragged tails while the oracle still finishes in seconds.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.moe_testlib import (GATE_TOL, HostExperts, check_dispatch_exact, row_rel_err, say, to_np, tol_for)
+
+pytestmark = pytest.mark.gpu
+ops = pytest.importorskip("sparse_mixture_experts_level_amd.ops")
+DEV = "cuda"
+
+
+def _desc(T, E, k, cap=None, d=64, f=64, fs=0, dtype=torch.float32):
+    return ops.make_desc(T, d, f, E, k, cap, fs, dtype)
+
+
+# ------------------------------------------------------------------------------------- top-k
+
+def _topk_case(logits_np, k):
+    T, E = logits_np.shape
+    say(f"topk T={T} E={E} k={k}")
+    lg = torch.from_numpy(logits_np.astype(np.float32)).to(DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ops.moe_router_topk(_desc(T, E, k), lg, ids, gates)
+    torch.cuda.synchronize()
+    ref_l = logits_np.astype(np.float32).astype(np.float64)
+    ref_ids = oracle.topk_select(ref_l, k)
+    ref_g = oracle.topk_gates(ref_l, ref_ids)
+    assert np.array_equal(to_np(ids), ref_ids)
+    assert np.abs(to_np(gates) - ref_g).max() <= GATE_TOL
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (257, 64, 1), (100, 32, 4), (130, 256, 8), (33, 5, 5),
+                                   (40, 1024, 70), (17, 130, 3), (1, 1, 1)])
+def test_topk_bitexact_random(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    _topk_case(rng.normal(size=(T, E)) * 2.0, k)
+
+
+def test_topk_ties_signed_zero_and_neg_inf():
+    rng = np.random.default_rng(11)
+    l = rng.integers(-2, 3, size=(200, 12)).astype(np.float64)
+    l[0] = 0.0
+    l[1, :6] = -0.0
+    l[2] = -np.inf
+    l[2, 7] = 1.0
+    l[3, ::2] = -np.inf
+    for k in (1, 3, 6, 12):
+        _topk_case(l, k)
+
+
+# ------------------------------------------------------------------------------------- dispatch
+
+def _dispatch_case(ids_np, E, cap, d=64, dtype=torch.bfloat16, tag=""):
+    T, k = ids_np.shape
+    say(f"dispatch {tag} T={T} E={E} k={k} cap={cap}")
+    desc = _desc(T, E, k, cap, d=d, f=64, dtype=dtype)
+    R = ops.moe_max_rows(desc)
+    ids = torch.from_numpy(ids_np.astype(np.int32)).to(DEV)
+    x = torch.randn((T, d), device=DEV).to(dtype)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    row_token = torch.full((max(R, 1),), -7, dtype=torch.int32, device=DEV)
+    x_perm = torch.zeros((max(R, 1), d), dtype=dtype, device=DEV)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    ops.moe_dispatch_permute(desc, ids, x, counts, offsets, slot, row_token, x_perm, ws)
+    torch.cuda.synchronize()
+    ref = check_dispatch_exact(ids_np, E, cap, to_np(counts), to_np(offsets), to_np(slot), to_np(row_token))
+    Rk = int(ref["offsets"][-1])
+    assert torch.equal(x_perm[:Rk], x[torch.from_numpy(ref["row_token"]).long().to(DEV)])
+    return ref
+
+
+def _ids(rng, T, E, k, skew=0.0):
+    p = np.exp(-skew * np.log(np.arange(1, E + 1)))
+    p /= p.sum()
+    return np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,cap,skew", [
+    (300, 8, 2, 10, 0.0), (300, 8, 2, None, 1.0), (5000, 64, 1, 78, 1.1), (3000, 256, 8, 40, 1.1),
+    (777, 1024, 3, 2, 0.5), (64, 8, 2, 0, 0.0), (1, 4, 4, 1, 0.0), (4100, 32, 4, None, 0.0),
+])
+def test_dispatch_bitexact(T, E, k, cap, skew):
+    rng = np.random.default_rng(T + E + k)
+    _dispatch_case(_ids(rng, T, E, k, skew), E, cap)
+
+
+def test_dispatch_float_rows_and_everyone_on_one_expert():
+    ids = np.zeros((500, 1), dtype=np.int32)
+    ref = _dispatch_case(ids, 8, 17, d=24, dtype=torch.float32, tag="collapse")
+    assert ref["drops"] == 500 - 17
+
+
+def test_demo_worked_example_on_gpu():
+    """The page's demo: drops 8/5 (balanced) and 11/9 (collapsed) at C = 4/5."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "demo2_capacity_dropping.json")))
+    torch.manual_seed(42)
+    x = torch.randn(32, 64)
+    balanced = torch.nn.Linear(64, 8, bias=False)
+    collapsed = torch.nn.Linear(64, 8, bias=False)
+    with torch.no_grad():
+        collapsed.weight[0] += 5.0
+        logits = {"balanced": balanced(x), "collapsed": collapsed(x)}
+    for name, lg in logits.items():
+        say(f"demo {name}")
+        lg = lg.float().contiguous().to(DEV)
+        ids = torch.empty((32, 1), dtype=torch.int32, device=DEV)
+        gates = torch.empty((32, 1), dtype=torch.float32, device=DEV)
+        ops.moe_router_topk(_desc(32, 8, 1), lg, ids, gates)
+        for i, cf in enumerate(g["capacity_factors"]):
+            cap = ops.moe_capacity(32, 8, cf)
+            assert cap == g[name]["capacity"][i]
+            desc = _desc(32, 8, 1, cap)
+            counts = torch.empty(8, dtype=torch.int32, device=DEV)
+            offsets = torch.empty(9, dtype=torch.int32, device=DEV)
+            slot = torch.empty((32, 1), dtype=torch.int32, device=DEV)
+            row_token = torch.empty(32, dtype=torch.int32, device=DEV)
+            ops.moe_dispatch_permute(desc, ids, None, counts, offsets, slot, row_token, None,
+                                     ops.workspace(ops.moe_workspace_size(desc)))
+            torch.cuda.synchronize()
+            assert int((slot < 0).sum()) == g[name]["dropped"][i]
+            if "counts" in g[name]:
+                assert to_np(counts).tolist() == g[name]["counts"]
+        assert torch.all(gates == 1.0)
+
+
+# ------------------------------------------------------------------------------------- router logits
+
+@pytest.mark.parametrize("T,d,E,dtype", [(300, 256, 8, torch.bfloat16), (129, 128, 64, torch.bfloat16),
+                                         (70, 192, 256, torch.bfloat16), (65, 64, 300, torch.bfloat16),
+                                         (77, 100, 9, torch.float32)])
+def test_router_logits(T, d, E, dtype):
+    say(f"router_logits T={T} d={d} E={E} {dtype}")
+    g = torch.Generator(device=DEV).manual_seed(T + d + E)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dtype)
+    w = (torch.randn((E, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
+    off = torch.randn((E,), generator=g, device=DEV)
+    logits = torch.full((T, E), float("nan"), device=DEV)
+    ops.moe_router_logits(_desc(T, E, 1, d=d, f=64, dtype=dtype), x, w, off, logits)
+    torch.cuda.synchronize()
+    xn, wn = to_np(x).astype(np.float64), to_np(w).astype(np.float64)
+    ref = oracle.router_logits(xn, wn, to_np(off))
+    bound = np.abs(xn) @ np.abs(wn).T
+    err = np.abs(to_np(logits) - ref)
+    assert np.all(err <= 4e-6 * bound + 1e-6), err.max()
+
+
+# ------------------------------------------------------------------------------------- grouped GEMM
+
+def _gemm_case(sizes, d, f, dtype, hint, seed=0):
+    G = len(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offs[-1]) + 5  # spare rows beyond the last group stay untouched
+    say(f"grouped_gemm G={G} sizes={sizes} d={d} f={f} {dtype} hint={hint}")
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = torch.randn((R, d), generator=g, device=DEV).to(dtype)
+    wgu = (torch.randn((G, 2 * f, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
+    wd = (torch.randn((G, d, f), generator=g, device=DEV) / math.sqrt(f)).to(dtype)
+    y = torch.full((R, d), 3.0, dtype=dtype, device=DEV)
+    go = torch.from_numpy(offs).to(DEV)
+    ws = ops.workspace(ops.moe_grouped_gemm_workspace_size(G, R, f, dtype))
+    ops.moe_grouped_swiglu_gemm(G, R, hint, d, f, dtype, x, go, wgu, wd, y, ws)
+    torch.cuda.synchronize()
+    xn, yn = to_np(x).astype(np.float64), to_np(y)
+    W1, W2 = HostExperts(wgu), HostExperts(wd)
+    worst = 0.0
+    for e in range(G):
+        lo, hi = offs[e], offs[e + 1]
+        if hi > lo:
+            ref = oracle.swiglu_ffn(xn[lo:hi], W1[e], W2[e])
+            worst = max(worst, row_rel_err(yn[lo:hi], ref))
+    assert np.all(yn[offs[-1]:] == 3.0), "rows outside every group were written"
+    assert worst <= tol_for(dtype), worst
+    return worst
+
+
+@pytest.mark.parametrize("sizes,hint", [
+    ([0, 1, 17, 130, 5, 0, 64, 33], 128), ([16, 3, 0, 9], 16), ([40, 31, 64], 64),
+    ([300, 2], 16),  # groups larger than the tiling hint are still computed
+    ([7], 7),
+])
+def test_grouped_gemm_bf16(sizes, hint):
+    _gemm_case(sizes, 256, 192, torch.bfloat16, hint)
+
+
+def test_grouped_gemm_bf16_wide():
+    _gemm_case([33, 0, 129], 1024, 320, torch.bfloat16, 129, seed=3)
+
+
+@pytest.mark.parametrize("sizes,d,f", [([0, 1, 17, 70, 5], 100, 72), ([10], 128, 256), ([3, 4], 7, 5)])
+def test_grouped_gemm_f32(sizes, d, f):
+    _gemm_case(sizes, d, f, torch.float32, max(sizes))
+
+
+# ------------------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("T,E,k,cap,d,dtype,shared", [
+    (300, 8, 2, 40, 256, torch.bfloat16, False), (300, 8, 2, 40, 256, torch.bfloat16, True),
+    (100, 64, 1, 2, 1024, torch.bfloat16, False), (50, 32, 8, None, 64, torch.float32, True),
+    (10, 4, 4, 1, 30, torch.float32, False),
+])
+def test_combine(T, E, k, cap, d, dtype, shared):
+    say(f"combine T={T} E={E} k={k} cap={cap} d={d} {dtype} shared={shared}")
+    rng = np.random.default_rng(T + k)
+    ids_np = _ids(rng, T, E, k)
+    fill = oracle.capacity_fill(ids_np, E, cap)
+    R = max(int(fill["offsets"][-1]), 1)
+    gates_np = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    y = torch.randn((R, d), generator=g, device=DEV).to(dtype)
+    sh = torch.randn((T, d), generator=g, device=DEV).to(dtype) if shared else None
+    out = torch.full((T, d), 7.0, dtype=dtype, device=DEV)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    ops.moe_combine_unpermute(_desc(T, E, k, cap, d=d, dtype=dtype), y, t(ids_np.astype(np.int32)), t(gates_np),
+                              t(fill["slot"]), t(fill["offsets"].astype(np.int32)), sh, out)
+    torch.cuda.synchronize()
+    yn = to_np(y).astype(np.float64)
+    rows = lambda tt, j: yn[fill["offsets"][ids_np[tt, j]] + fill["slot"][tt, j]]
+    ref = oracle.combine(T, d, ids_np, gates_np.astype(np.float64), fill["slot"], rows,
+                         shared=to_np(sh).astype(np.float64) if shared else None)
+    assert row_rel_err(to_np(out), ref) <= (2 ** -8 if dtype == torch.bfloat16 else 1e-6)
