@@ -63,6 +63,9 @@ moe_status check_dtype_dims(int32_t dtype, int64_t d, int64_t f, int64_t fs) {
     if (d % 64 || f % 64 || fs % 64)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d_model, d_ff and d_ff_shared to be multiples of 64 "
                                        "(got %lld, %lld, %lld)", (long long)d, (long long)f, (long long)fs);
+    // one expert's weights are addressed through 32-bit buffer offsets
+    if (2 * std::max(f, fs) * d * 2 >= ((int64_t)1 << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "one expert's gate_up weights must be smaller than 2 GiB");
   }
   return MOE_OK;
 }

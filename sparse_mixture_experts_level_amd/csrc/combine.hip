@@ -11,89 +11,94 @@ namespace moe {
 
 namespace {
 
-constexpr int CB_KMAX = 64;  // assignments per token staged in LDS per pass
+constexpr int CB_TOK = 4;  // tokens per workgroup, one wavefront each
+constexpr int CB_U = 4;    // 16-byte vectors per lane per pass
 
+// One wavefront per token.  Lanes j < k fetch assignment j's slot, expert and gate in
+// parallel and resolve its row; the wave then streams the row vectors, each lane
+// summing its columns over j in order.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ gates,
                                                       const int32_t *__restrict__ slot,
                                                       const int32_t *__restrict__ offsets,
-                                                      const void *__restrict__ shared, void *__restrict__ out, int d,
-                                                      int k) {
+                                                      const void *__restrict__ shared, void *__restrict__ out, int T,
+                                                      int d, int k) {
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte vector
-  __shared__ int64_t s_row[CB_KMAX];
-  __shared__ float s_gate[CB_KMAX];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * CB_TOK + (threadIdx.x >> 6);
+  if (t >= T) return;
   const int nvec = d / VEC;
-  // chunks of up to CB_KMAX assignments; acc lives in registers across chunks
-  constexpr int MAXV = 8;  // vectors per thread kept in registers: d <= 256*MAXV*VEC
-  float acc[MAXV][VEC];
+  const size_t es = BF16 ? 2 : 4;
+  const uint8_t *yb = static_cast<const uint8_t *>(y_perm);
+  for (int v0 = 0; v0 < nvec; v0 += 64 * CB_U) {
+    float acc[CB_U][VEC];
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const int c = tid + 256 * v;
+    for (int u = 0; u < CB_U; ++u) {
+      const int c = v0 + lane + 64 * u;
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[v][i] = 0.f;
-    if (shared && c < nvec) {
-      if constexpr (BF16) {
-        const u32x4 q = ldg16(static_cast<const bf16_t *>(shared) + (size_t)t * d + c * VEC);
+      for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
+      if (shared && c < nvec) {
+        const u32x4 q = ldg16(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[v][2 * i] = __uint_as_float(q[i] << 16);
-          acc[v][2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+          if constexpr (BF16) {
+            acc[u][2 * i] = __uint_as_float(q[i] << 16);
+            acc[u][2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+          } else {
+            acc[u][i] = __uint_as_float(q[i]);
+          }
         }
-      } else {
-        const u32x4 q = ldg16(static_cast<const float *>(shared) + (size_t)t * d + c * VEC);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[v][i] = __uint_as_float(q[i]);
       }
     }
-  }
-  for (int j0 = 0; j0 < k; j0 += CB_KMAX) {
-    const int kn = min(CB_KMAX, k - j0);
-    __syncthreads();
-    if (tid < kn) {
-      const size_t q = (size_t)t * k + j0 + tid;
-      const int sl = slot[q];
-      s_row[tid] = sl >= 0 ? (int64_t)offsets[ids[q]] + sl : -1;
-      s_gate[tid] = gates[q];
-    }
-    __syncthreads();
-    for (int j = 0; j < kn; ++j) {
-      const int64_t row = s_row[j];
-      if (row < 0) continue;
-      const float gj = s_gate[j];
+    for (int j0 = 0; j0 < k; j0 += 64) {
+      // lane j holds assignment j0 + j: its row (or -1) and gate
+      int64_t my_row = -1;
+      float my_gate = 0.f;
+      if (j0 + lane < k) {
+        const size_t q = (size_t)t * k + j0 + lane;
+        const int sl = slot[q];
+        const int e = ids[q];
+        my_gate = gates[q];
+        if (sl >= 0) my_row = (int64_t)offsets[e] + sl;
+      }
+      const int kn = min(64, k - j0);
+      for (int j = 0; j < kn; ++j) {
+        const int64_t row = __shfl(my_row, j, 64);
+        const float gj = __shfl(my_gate, j, 64);
+        if (row < 0) continue;
+        const uint8_t *yr = yb + (size_t)row * d * es;
 #pragma unroll
-      for (int v = 0; v < MAXV; ++v) {
-        const int c = tid + 256 * v;
-        if (c >= nvec) continue;
-        if constexpr (BF16) {
-          const u32x4 q = ldg16(static_cast<const bf16_t *>(y_perm) + (size_t)row * d + c * VEC);
+        for (int u = 0; u < CB_U; ++u) {
+          const int c = v0 + lane + 64 * u;
+          if (c >= nvec) continue;
+          const u32x4 q = ldg16(yr + (size_t)c * VEC * es);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[v][2 * i] = fmaf(gj, __uint_as_float(q[i] << 16), acc[v][2 * i]);
-            acc[v][2 * i + 1] = fmaf(gj, __uint_as_float(q[i] & 0xffff0000u), acc[v][2 * i + 1]);
+            if constexpr (BF16) {
+              acc[u][2 * i] = fmaf(gj, __uint_as_float(q[i] << 16), acc[u][2 * i]);
+              acc[u][2 * i + 1] = fmaf(gj, __uint_as_float(q[i] & 0xffff0000u), acc[u][2 * i + 1]);
+            } else {
+              acc[u][i] = fmaf(gj, __uint_as_float(q[i]), acc[u][i]);
+            }
           }
-        } else {
-          const u32x4 q = ldg16(static_cast<const float *>(y_perm) + (size_t)row * d + c * VEC);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(gj, __uint_as_float(q[i]), acc[v][i]);
         }
       }
     }
-  }
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const int c = tid + 256 * v;
-    if (c >= nvec) continue;
-    u32x4 q;
-    if constexpr (BF16) {
+    for (int u = 0; u < CB_U; ++u) {
+      const int c = v0 + lane + 64 * u;
+      if (c >= nvec) continue;
+      u32x4 q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(acc[v][2 * i], acc[v][2 * i + 1]);
-      stg16(static_cast<bf16_t *>(out) + (size_t)t * d + c * VEC, q);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = __float_as_uint(acc[v][i]);
-      stg16(static_cast<float *>(out) + (size_t)t * d + c * VEC, q);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+          q[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
+        } else {
+          q[i] = __float_as_uint(acc[u][i]);
+        }
+      }
+      stg16(static_cast<uint8_t *>(out) + ((size_t)t * d + (size_t)c * VEC) * es, q);
     }
   }
 }
@@ -130,13 +135,14 @@ hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *g
                           const int32_t *offsets, const void *shared, void *out, int T, int d, int k, bool bf16,
                           hipStream_t s) {
   const int vec = bf16 ? 8 : 4;
-  if (d % vec == 0 && d <= 256 * 8 * vec) {
+  if (d % vec == 0) {
+    const int grid = (T + CB_TOK - 1) / CB_TOK;
     if (bf16)
-      hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, d, k);
+      hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
+                         out, T, d, k);
     else
-      hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, d, k);
+      hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
+                         out, T, d, k);
   } else {
     if (bf16) return hipErrorInvalidValue;  // bf16 rows are validated to be multiples of 64
     hipLaunchKernelGGL(combine_f32_scalar_kernel, dim3(T), dim3(256), 0, s, static_cast<const float *>(y_perm), ids,

@@ -36,6 +36,17 @@ __device__ __forceinline__ void stg16(void *p, u32x4 v) { *reinterpret_cast<u32x
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Raw buffer resources: loads whose byte offset is at or beyond `num_bytes` return
+// zeros without touching memory (hardware range check).  kOob is such an offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }

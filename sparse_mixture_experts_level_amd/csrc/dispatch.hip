@@ -13,7 +13,8 @@
 //   2. dispatch_assign: each block sums the histograms of the blocks before it (its
 //      base per expert), the totals give the per-expert kept counts and their
 //      exclusive prefix (offsets); inside the block, elements are ranked in order in
-//      chunks of 256 by comparing against earlier elements of the chunk;
+//      chunks of 256 (wavefront ballots match equal experts within a wave, per-wave
+//      counts in LDS carry the rank across waves);
 //   3. gather_rows:     copies x[row_token[r]] into row r of x_perm with 16-byte
 //      coalesced vector moves.
 // Only order-independent counter increments use atomics, so every output is
@@ -76,26 +77,46 @@ __device__ int block_exclusive_scan(int32_t *s, int n, int32_t *s_part) {
   return total;
 }
 
+// Lanes of the calling wavefront whose value equals this lane's (only lanes with
+// `active` set take part); nbits = bits needed for the largest value.
+__device__ __forceinline__ uint64_t match_any(int v, bool active, int nbits) {
+  uint64_t m = __ballot(active);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const uint64_t b = __ballot(active && ((v >> bit) & 1));
+    m &= ((v >> bit) & 1) ? b : ~b;
+  }
+  return active ? m : 0ull;
+}
+
 __global__ __launch_bounds__(DP_THREADS) void dispatch_assign_kernel(
     const int32_t *__restrict__ ids, int T, int k, int E, int cap, int tokens_per_block, int num_blocks,
     const int32_t *__restrict__ hist, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ slot, int32_t *__restrict__ row_token) {
+  constexpr int NW = DP_THREADS / 64;
   __shared__ int32_t s_base[MOE_MAX_EXPERTS_DEV];  // running slot per expert for this block
   __shared__ int32_t s_off[MOE_MAX_EXPERTS_DEV];   // kept counts, then their exclusive prefix
   __shared__ int32_t s_part[DP_THREADS];
-  __shared__ int32_t s_chunk[DP_THREADS];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int32_t s_wcnt[NW][MOE_MAX_EXPERTS_DEV];  // per-wave count of an expert in the chunk
+  __shared__ int32_t s_wtag[NW][MOE_MAX_EXPERTS_DEV];  // chunk index the count belongs to
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   for (int e = tid; e < E; e += DP_THREADS) {
     int before = 0, total = 0;
-    for (int bb = 0; bb < num_blocks; ++bb) {
-      const int h = hist[(size_t)bb * E + e];
-      before += bb < b ? h : 0;
-      total += h;
+    for (int bb0 = 0; bb0 < num_blocks; bb0 += 16) {  // 16 independent loads in flight
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) h[i] = bb0 + i < num_blocks ? hist[(size_t)(bb0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        before += bb0 + i < b ? h[i] : 0;
+        total += h[i];
+      }
     }
     s_base[e] = before;
     s_off[e] = cap < 0 ? total : min(total, cap);
     if (b == 0) counts[e] = total;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s_wtag[w][e] = -1;
   }
   __syncthreads();
   const int kept_total = block_exclusive_scan(s_off, E, s_part);
@@ -103,18 +124,30 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_assign_kernel(
     for (int e = tid; e < E; e += DP_THREADS) offsets[e] = s_off[e];
     if (tid == 0) offsets[E] = kept_total;
   }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
 
+  // Elements of the block in token-major order, 256 per chunk: the rank of an element
+  // among earlier elements of the chunk with the same expert is the count in earlier
+  // waves plus the count of lower lanes of its own wave.
   const int64_t q0 = (int64_t)b * tokens_per_block * k;
   const int64_t q1 = min((int64_t)(b + 1) * tokens_per_block, (int64_t)T) * k;
-  for (int64_t c0 = q0; c0 < q1; c0 += DP_THREADS) {
+  int chunk = 0;
+  for (int64_t c0 = q0; c0 < q1; c0 += DP_THREADS, ++chunk) {
     const int64_t q = c0 + tid;
     const bool valid = q < q1;
-    const int e = valid ? ids[q] : -1;
-    s_chunk[tid] = e;
+    const int e = valid ? ids[q] : 0;
+    const uint64_t m = match_any(e, valid, nbits);
+    const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+    const bool leader = valid && in_wave == 0;
+    if (leader) {
+      s_wcnt[wave][e] = __popcll(m);
+      s_wtag[wave][e] = chunk;
+    }
     __syncthreads();
-    int rank = 0;
-    for (int i = 0; i < tid; ++i) rank += (s_chunk[i] == e) ? 1 : 0;
     if (valid) {
+      int rank = in_wave;
+      for (int w = 0; w < wave; ++w) rank += s_wtag[w][e] == chunk ? s_wcnt[w][e] : 0;
       const int sl = s_base[e] + rank;
       if (cap < 0 || sl < cap) {
         slot[q] = sl;
@@ -124,7 +157,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_assign_kernel(
       }
     }
     __syncthreads();
-    if (valid) atomicAdd(&s_base[e], 1);  // order-independent: adds this chunk's count
+    if (leader) atomicAdd(&s_base[e], __popcll(m));  // order-independent: adds this chunk's count
     __syncthreads();
   }
 }

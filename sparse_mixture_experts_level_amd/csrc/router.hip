@@ -12,7 +12,8 @@ namespace moe {
 // A workgroup owns 64 tokens (16 per wave) and every expert, in chunks of up to 256
 // experts.  The router weight chunk for 64 values of d is staged in LDS (double
 // buffered) and shared by the four waves; each wave streams its own 16 token rows
-// straight from HBM into MFMA operand registers.
+// straight from HBM into MFMA operand registers.  Loads run four chunks ahead
+// through range-checked buffer loads (rows past T or E read as zeros).
 namespace {
 
 constexpr int RT_TOK = 64;   // tokens per workgroup
@@ -26,32 +27,44 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *_
                                                                  float *__restrict__ logits, int T, int d, int E,
                                                                  int e_base) {
   constexpr int EC = NSUB * 16;
+  constexpr int P = 4;  // chunks in flight
+  constexpr int PER_T = (EC * 8 + 255) / 256;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][EC * RT_KC * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT_TOK + wave * 16;
-  const int trow = min(t0 + (lane & 15), T - 1);
-  const bf16_t *xrow = x + (size_t)trow * d + (lane >> 4) * 8;
-
-  // staging: EC rows x 8 chunks; each thread moves EC*8/256 chunks per stage
-  constexpr int PER_T = (EC * 8 + 255) / 256;
-  u32x4 stage[PER_T];
-  auto load_stage = [&](int kc) {
+  const int tb = blockIdx.x * RT_TOK;
+  const int t0 = tb + wave * 16;
+  const uint32_t dbytes = (uint32_t)d * 2u;
+  // token rows past T and expert rows past E read as zeros (range-checked buffer loads)
+  const rsrc_t xres = make_rsrc(x + (size_t)tb * d, (uint32_t)min(RT_TOK, T - tb) * dbytes);
+  const rsrc_t wres = make_rsrc(w + (size_t)e_base * d, (uint32_t)min(EC, E - e_base) * dbytes);
+  const uint32_t xoff = (uint32_t)(wave * 16 + (lane & 15)) * dbytes + (uint32_t)(lane >> 4) * 16u;
+  uint32_t woff[PER_T];
 #pragma unroll
-    for (int r = 0; r < PER_T; ++r) {
-      const int q = tid + 256 * r;
-      const int row = q >> 3, c = q & 7;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < EC * 8 && e_base + row < E) v = ldg16(w + (size_t)(e_base + row) * d + kc + c * 8);
-      stage[r] = v;
-    }
+  for (int r = 0; r < PER_T; ++r) {
+    const int q = tid + 256 * r;
+    woff[r] = q < EC * 8 ? (uint32_t)(q >> 3) * dbytes + (uint32_t)(q & 7) * 16u : kOob;
+  }
+  struct Slot {
+    u32x4 a[2];
+    u32x4 w[PER_T];
   };
-  auto store_stage = [&](int buf) {
+  Slot slot[P];
+  const int nk = d / RT_KC;
+  auto issue = [&](Slot &sl, int it) {
+    const bool ok = it < nk;
+    const uint32_t kc = (uint32_t)it * (RT_KC * 2);
+    sl.a[0] = buf_ld16(xres, ok ? xoff + kc : kOob);
+    sl.a[1] = buf_ld16(xres, ok ? xoff + 64u + kc : kOob);
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) sl.w[r] = buf_ld16(wres, ok ? woff[r] + kc : kOob);
+  };
+  auto stage = [&](const Slot &sl, int buf) {
 #pragma unroll
     for (int r = 0; r < PER_T; ++r) {
       const int q = tid + 256 * r;
-      if (q < EC * 8) {
+      if ((EC * 8) % 256 == 0 || q < EC * 8) {
         const int row = q >> 3, c = q & 7;
-        *reinterpret_cast<u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]) = stage[r];
+        *reinterpret_cast<u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]) = sl.w[r];
       }
     }
   };
@@ -60,27 +73,30 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *_
 #pragma unroll
   for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = d / RT_KC;
-  load_stage(0);
-  store_stage(0);
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) issue(slot[s], s);
+  stage(slot[0], 0);
   __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    const int kc = it * RT_KC;
-    const u32x4 a0 = ldg16(xrow + kc), a1 = ldg16(xrow + kc + 32);
-    if (it + 1 < nk) load_stage(kc + RT_KC);
+  for (int c0 = 0; c0 < nk; c0 += P) {
 #pragma unroll
-    for (int n = 0; n < NSUB; ++n) {
-      const int row = n * 16 + (lane & 15);
+    for (int s = 0; s < P; ++s) {
+      const int it = c0 + s;
+      if (it >= nk) break;
+      issue(slot[(s + P - 1) % P], it + P - 1);
+      const int buf = it & 1;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c = s * 4 + (lane >> 4);
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]);
-        acc[n] = mfma16(s == 0 ? a0 : a1, b, acc[n]);
+      for (int n = 0; n < NSUB; ++n) {
+        const int row = n * 16 + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = ks * 4 + (lane >> 4);
+          const u32x4 b = *reinterpret_cast<const u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]);
+          acc[n] = mfma16(slot[s].a[ks], b, acc[n]);
+        }
       }
+      if (it + 1 < nk) stage(slot[(s + 1) % P], (it + 1) & 1);
+      __syncthreads();
     }
-    if (it + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
   }
 
   // C layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4) + i.
