@@ -141,13 +141,14 @@ P *at(void *ws, size_t off) {
   return reinterpret_cast<P *>(static_cast<uint8_t *>(ws) + off);
 }
 
-moe::GroupedGemmArgs projection_args(int32_t G, int32_t group_rows_max, int32_t d, int32_t f, const void *in,
-                                     const int32_t *offsets, const void *w, void *out, bool gate_up) {
+moe::GroupedGemmArgs projection_args(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f,
+                                     const void *in, const int32_t *offsets, const void *w, void *out, bool gate_up) {
   moe::GroupedGemmArgs a{};
   a.A = in;
   a.offsets = offsets;
   a.num_groups = G;
   a.group_rows_max = group_rows_max;
+  a.rows_max = rows_max;
   a.W = w;
   a.w_group_stride = gate_up ? (int64_t)2 * f * d : (int64_t)d * f;
   a.n_out = gate_up ? f : d;
@@ -173,11 +174,10 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s) {
-  (void)rows_max;
-  MOE_TRY(run_projection(projection_args(G, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true), dtype, s,
-                         "gate_up grouped GEMM"));
-  MOE_TRY(run_projection(projection_args(G, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false), dtype, s,
-                         "down grouped GEMM"));
+  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true),
+                         dtype, s, "gate_up grouped GEMM"));
+  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false),
+                         dtype, s, "down grouped GEMM"));
   return MOE_OK;
 }
 
@@ -310,8 +310,8 @@ moe_status moe_grouped_gate_up_swiglu(int32_t num_groups, int64_t rows_max, int3
   MOE_TRY(check_ptr(group_offsets, "group_offsets"));
   MOE_TRY(check_ptr(w_gate_up, "w_gate_up"));
   MOE_TRY(check_ptr(h_rows, "h_rows"));
-  MOE_TRY(run_projection(projection_args(num_groups, (int32_t)std::min<int64_t>(group_rows_max, rows_max), d_model,
-                                         d_ff, x_rows, group_offsets, w_gate_up, h_rows, true),
+  MOE_TRY(run_projection(projection_args(num_groups, rows_max, (int32_t)std::min<int64_t>(group_rows_max, rows_max),
+                                         d_model, d_ff, x_rows, group_offsets, w_gate_up, h_rows, true),
                          dtype, stream, "gate_up grouped GEMM"));
   return ok();
 }
@@ -325,8 +325,8 @@ moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_
   MOE_TRY(check_ptr(group_offsets, "group_offsets"));
   MOE_TRY(check_ptr(w_down, "w_down"));
   MOE_TRY(check_ptr(y_rows, "y_rows"));
-  MOE_TRY(run_projection(projection_args(num_groups, (int32_t)std::min<int64_t>(group_rows_max, rows_max), d_model,
-                                         d_ff, h_rows, group_offsets, w_down, y_rows, false),
+  MOE_TRY(run_projection(projection_args(num_groups, rows_max, (int32_t)std::min<int64_t>(group_rows_max, rows_max),
+                                         d_model, d_ff, h_rows, group_offsets, w_down, y_rows, false),
                          dtype, stream, "down grouped GEMM"));
   return ok();
 }

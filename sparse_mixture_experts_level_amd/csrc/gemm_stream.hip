@@ -215,7 +215,13 @@ hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t
   return a.swiglu ? launch_stream_bm<true>(a, s) : launch_stream_bm<false>(a, s);
 }
 
+// Regime choice: the streaming kernel when groups hold few rows on average (each
+// weight byte feeds few MFMAs, HBM bound), the 256 x 256 tile kernel when they hold
+// many (MFMA bound).  The row bounds are the caller's; either kernel computes any
+// group size correctly.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s) {
+  const int64_t avg_rows = a.rows_max / a.num_groups;
+  if (avg_rows >= 256 && a.group_rows_max >= 256) return launch_grouped_gemm_big_bf16(a, a.rows_max, s);
   return launch_grouped_gemm_stream_bf16(a, s);
 }
 

@@ -38,6 +38,7 @@ struct GroupedGemmArgs {
   const int32_t *offsets;
   int num_groups;
   int group_rows_max;  // tiling hint
+  int64_t rows_max;    // bound on the total rows over all groups
   const void *W;
   int64_t w_group_stride;
   int n_out;
@@ -47,6 +48,7 @@ struct GroupedGemmArgs {
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);
+hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GroupedGemmArgs &a, hipStream_t s);
 
 // ---- combine (combine.hip)

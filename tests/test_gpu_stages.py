@@ -198,6 +198,16 @@ def test_grouped_gemm_bf16_wide():
     _gemm_case([33, 0, 129], 1024, 320, torch.bfloat16, 129, seed=3)
 
 
+@pytest.mark.parametrize("sizes,d,f", [
+    ([600, 0, 300, 1000], 256, 192),  # ragged row tiles, an empty group, a column tail (192 = 1.5 x 128)
+    ([2000], 512, 384),
+    ([257, 511, 1, 256], 320, 256),   # K = 320 (five 64-wide steps)
+])
+def test_grouped_gemm_bf16_large_groups(sizes, d, f):
+    """Average group of >= 256 rows: the 256 x 256 MFMA tile kernel."""
+    _gemm_case(sizes, d, f, torch.bfloat16, max(sizes), seed=len(sizes))
+
+
 @pytest.mark.parametrize("sizes,d,f", [([0, 1, 17, 70, 5], 100, 72), ([10], 128, 256), ([3, 4], 7, 5)])
 def test_grouped_gemm_f32(sizes, d, f):
     _gemm_case(sizes, d, f, torch.float32, max(sizes))
