@@ -46,6 +46,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes
 __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
+// lds_wave_base + 16 * i (lds_wave_base must be equal across the wavefront).
+__device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t off, void *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, off, 0, 0,
+                                           0);
+}
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);

@@ -7,14 +7,11 @@
 // трансформерах", aglamov.biz, section "Бэкенд для экспертов": one grouped GEMM over
 // tokens sorted by expert).
 //
-// Block tile: 256 rows x 256 weight rows, K in steps of 64.  Four wavefronts in a
-// 2 x 2 arrangement each own 128 x 128 of the tile as 4 x 4 blocks of the 32x32x16
-// bf16 MFMA (256 float accumulators per lane).  Both operand tiles are staged
-// through LDS (two buffers of 64 KB), XOR-swizzled by row so the 32-row column reads
-// of the MFMA operand layout hit distinct banks; global loads for the next K step
-// are issued before the current step's MFMAs.  For SwiGLU the 256 weight rows are
-// 128 gate rows and the 128 matching up rows, and each wave owns 64 output columns
-// of both, so gate and up accumulators of a column sit in the same lane.
+// Block tile: 256 rows x 256 weight rows.  Eight wavefronts (two per SIMD) in a
+// 2 x 4 arrangement each own 128 x 64 of the tile as 4 x 2 blocks of the 32x32x16
+// bf16 MFMA.  For SwiGLU the 256 weight rows are 128 gate rows and the 128 matching
+// up rows, and each wave owns 32 output columns of both, so gate and up
+// accumulators of a column sit in the same lane.
 //
 // Tiles: each group contributes ceil(rows / 256) row tiles times the column tiles.
 // A block finds its group from the offsets (one wavefront scan), and walks the
@@ -27,16 +24,7 @@ namespace moe {
 
 namespace {
 
-constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 64;
-constexpr int BG_THREADS = 256;
-constexpr int BG_CHUNKS = BG_BM * BG_BK * 2 / 16 / BG_THREADS;  // 16-byte pieces per thread per operand = 8
-
-// LDS offset (bytes) of row r, 16-byte chunk c of a [256][64] bf16 tile.
-template <int SW>
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-  const int pc = SW == 0 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 7));
-  return (uint32_t)(r * 8 + pc) * 16u;
-}
+constexpr int BG_BM = 256, BG_BN = 256;
 
 // Exclusive prefix of ceil(rows_g / BM) over groups, evaluated by one wavefront; returns
 // for tile index `m_lin` its group (or -1 past the end), the group's first m tile and
@@ -71,14 +59,40 @@ __device__ __forceinline__ void find_group(const int32_t *offsets, int G, int m_
   }
 }
 
-template <bool SWIGLU, int SW>
-__global__ __launch_bounds__(BG_THREADS, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
+// Pipeline: K advances in steps of 32.  Operand tiles go from HBM straight into LDS
+// (buffer loads with an LDS destination, no registers), into NBUF stages that are
+// separate LDS arrays, NBUF - 1 steps ahead of the MFMAs.  Each step: wait for this
+// wave's loads of the current stage (a fixed count of younger loads may stay in
+// flight), one barrier (all waves' loads landed; all waves are done with the stage
+// about to be refilled), issue the loads of step kt + NBUF - 1, then the MFMAs.
+//
+// LDS tile layout: 256 rows of 64 bytes (4 chunks of 16 bytes); chunk c of row r is
+// stored at chunk c ^ ((r >> 2) & 3).  An MFMA operand load reads one chunk of 32
+// consecutive rows; LDS serves 16 lanes (256 bytes, 64 banks) at a time, and any 16
+// consecutive rows then fall on 16 distinct 16-byte bank groups.  One load instruction fills 1 KB = 16 rows; lane p of it
+// brings row 16 * blk + p / 4, stored chunk p % 4.
+//
+// WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
+// 4: eight waves of 128 x 64, two per SIMD).
+template <bool SWIGLU, int WN_W, int NBUF, bool PING>
+__global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ offsets, int G,
                                                                          const bf16_t *__restrict__ W,
                                                                          int64_t wstride, int n_out, int K,
                                                                          bf16_t *__restrict__ out, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BG_BM * BG_BK * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BG_BN * BG_BK * 2];
+  constexpr int BK = 32;
+  constexpr int NT = 128 * WN_W;                 // threads
+  constexpr int NW = NT / 64;                    // waves
+  constexpr int NI = BG_BN / WN_W / 32;          // 32-wide weight blocks per wave
+  constexpr int TILE = BG_BM * BK * 2;           // 16 KB per operand and stage
+  constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
+  static_assert(NBUF >= 2 && NBUF <= 4, "stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[NBUF > 2 ? TILE : 16],
+      sA3[NBUF > 3 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[NBUF > 2 ? TILE : 16],
+      sB3[NBUF > 3 ? TILE : 16];
+  auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
+  auto bufB = [&](int b) -> uint8_t * { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles (n tile folded below)
@@ -108,21 +122,22 @@ __global__ __launch_bounds__(BG_THREADS, 1) void grouped_gemm_big_kernel(const b
   const int rows = min(BG_BM, row_end - m0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN_W, wn = wave % WN_W;
   const uint32_t kbytes = (uint32_t)K * 2u;
   const int n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
 
   const rsrc_t ares = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
   const rsrc_t wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
 
-  // Per-thread global offsets (k = 0) and LDS offsets of its 8 A and 8 B pieces.
-  uint32_t agoff[BG_CHUNKS], bgoff[BG_CHUNKS], loff[BG_CHUNKS];
+  // This lane's global offsets (k = 0) for its IPW instructions per operand.
+  uint32_t agoff[IPW], bgoff[IPW];
 #pragma unroll
-  for (int i = 0; i < BG_CHUNKS; ++i) {
-    const int q = tid + BG_THREADS * i;
-    const int r = q >> 3, c = q & 7;
+  for (int i = 0; i < IPW; ++i) {
+    const int blk = wave * IPW + i;
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
-    int wr;  // weight row held in tile row r
+    int wr;  // weight row held in tile row r, -1 past n_out
     if (SWIGLU) {
       const int col = n0 + (r & 127);
       wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
@@ -130,73 +145,157 @@ __global__ __launch_bounds__(BG_THREADS, 1) void grouped_gemm_big_kernel(const b
       wr = n0 + r < n_out ? n0 + r : -1;
     }
     bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
-    loff[i] = lds_off<SW>(r, c);
   }
-
-  u32x4 ra[BG_CHUNKS], rb[BG_CHUNKS];
-  auto gload = [&](int kt) {
-    const uint32_t kc = (uint32_t)kt * (BG_BK * 2);
+  const int nk = K / BK;
+  auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
+    const bool ok = kt < nk;
+    const uint32_t kc = (uint32_t)kt * (BK * 2);
+    uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
-    for (int i = 0; i < BG_CHUNKS; ++i) {
-      ra[i] = buf_ld16(ares, agoff[i] + kc);
-      rb[i] = buf_ld16(wres, bgoff[i] == kOob ? kOob : bgoff[i] + kc);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < BG_CHUNKS; ++i) {
-      *reinterpret_cast<u32x4 *>(&sA[buf][loff[i]]) = ra[i];
-      *reinterpret_cast<u32x4 *>(&sB[buf][loff[i]]) = rb[i];
+    for (int i = 0; i < IPW; ++i) {
+      const int blk = wave * IPW + i;
+      buf_ld16_lds(ares, ok ? agoff[i] + kc : kOob, la + blk * 1024);
+      buf_ld16_lds(wres, (ok && bgoff[i] != kOob) ? bgoff[i] + kc : kOob, lb + blk * 1024);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NI];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x16{};
 
-  // rows of the operand tiles this lane reads for its MFMA blocks
-  int arow[4], brow[4];
+  // LDS byte offset of this lane's operand row for MFMA block 0 and chunk c; block i
+  // is 32 rows further (same swizzle), a constant distance.
+  const int ar0 = wm * 128 + (lane & 31);
+  const int br0 = SWIGLU ? wn * (NI / 2) * 32 + (lane & 31) : wn * NI * 32 + (lane & 31);
+  auto roff = [&](int r, int c) -> int { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); };
+  auto compute = [&](int b) {
+    const uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = wm * 128 + i * 32 + (lane & 31);
-    brow[i] = SWIGLU ? (i < 2 ? wn * 64 + i * 32 : 128 + wn * 64 + (i - 2) * 32) + (lane & 31)
-                     : wn * 128 + i * 32 + (lane & 31);
-  }
-
-  const int nk = K / BG_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
       const int c = kk * 2 + (lane >> 5);
-      u32x4 af[4], bfr[4];
+      const uint8_t *pa = la + roff(ar0, c);
+      const uint8_t *pb = lb + roff(br0, c);
+      u32x4 af[4], bfr[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const u32x4 *>(&sA[buf][lds_off<SW>(arow[i], c)]);
-        bfr[i] = *reinterpret_cast<const u32x4 *>(&sB[buf][lds_off<SW>(brow[i], c)]);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * 64);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
+        bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * 64);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  if constexpr (!PING) {
+    // prologue: steps 0 .. NBUF-2 in flight
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) issue(b, b);
+    for (int k0 = 0; k0 < nk; k0 += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        const int kt = k0 + b;
+        if (kt >= nk) break;
+        // this wave's loads of step kt are done once at most (NBUF - 2) younger steps remain
+        if constexpr (NBUF == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (NBUF == 3) {
+          if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          if constexpr (IPW == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
+        if constexpr (NBUF == 4) {
+          if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+          if constexpr (IPW == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        }
+        // Bare barrier: a fenced one would also wait for the younger loads still in
+        // flight.  LDS reads of the stage refilled next are complete (lgkmcnt(0)).
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        issue(kt + NBUF - 1, (b + NBUF - 1) % NBUF);
+        compute(b);
+      }
+    }
+  } else {
+    // Ping-pong: the two waves of each SIMD (group 0 = waves 0..3, group 1 = waves
+    // 4..7) alternate between a memory phase -- issue the loads of step k + 3, wait
+    // for this wave's loads of step k + 1, read step k's operand fragments from LDS --
+    // and a compute phase -- the step's MFMAs, at raised priority.  Group 1 runs one
+    // barrier behind group 0, so while one group computes the other feeds.
+    //   Loads of step k land before any wave reads them: each wave completes its own
+    //   loads of step k + 1 in mem(k), before the barrier that precedes every read of
+    //   step k + 1.  A stage is refilled (step k + 3 in mem(k)) only after the barrier
+    //   that follows both groups' reads of its previous step k - 1.
+    static_assert(NBUF == 4 && IPW == 2, "ping-pong schedule is written for 4 stages and 8 waves");
+    const bool second = wave >= 4;
+    u32x4 af[2][4], bfr[2][NI];
+    auto mem = [&](int kt, int b) {
+      issue(kt + 3, (b + 3) % NBUF);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's loads of step kt + 1 done
+      const uint8_t *la = bufA(b), *lb = bufB(b);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+        const uint8_t *pa = la + roff(ar0, c);
+        const uint8_t *pb = lb + roff(br0, c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[kk][i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * 64);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
+          bfr[kk][j] = *reinterpret_cast<const u32x4 *>(pb + dr * 64);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    auto comp = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(af[kk][i], bfr[kk][j], acc[i][j]);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    auto bar = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // prologue: steps 0..2 issued; step 0 landed for every wave before the first read
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    bar();
+    if (second) bar();
+    for (int k0 = 0; k0 < nk; k0 += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        const int kt = k0 + b;
+        if (kt >= nk) break;
+        mem(kt, b);
+        bar();
+        comp();
+        bar();
+      }
+    }
+    if (!second) bar();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may outlive the block
 
   // Epilogue.  32x32 MFMA layout: lane holds column (lane & 31) and rows
   // 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
+  constexpr int NJ = SWIGLU ? NI / 2 : NI;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < (SWIGLU ? 2 : 4); ++j) {
-      const int col = n0 + (SWIGLU ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * NJ * 32 + j * 32 + (lane & 31);
       if (col >= n_out) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -204,7 +303,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void grouped_gemm_big_kernel(const b
         if (row >= rows) continue;
         float v;
         if constexpr (SWIGLU) {
-          v = silu_f32(acc[i][j][r]) * acc[i][j + 2][r];
+          v = silu_f32(acc[i][j][r]) * acc[i][j + NI / 2][r];
         } else {
           v = acc[i][j][r];
         }
@@ -216,21 +315,23 @@ __global__ __launch_bounds__(BG_THREADS, 1) void grouped_gemm_big_kernel(const b
 
 }  // namespace
 
-// Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
-hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
-  const int cols = a.swiglu ? BG_BN / 2 : BG_BN;
+template <bool SWIGLU, int WN_W, int NBUF, bool PING = false>
+hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
   const int64_t grid = m_tiles * n_tiles;
-  if (a.swiglu)
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<true, 0>), dim3((unsigned)grid), dim3(BG_THREADS), 0, s,
-                       static_cast<const bf16_t *>(a.A), a.offsets, a.num_groups, static_cast<const bf16_t *>(a.W),
-                       a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
-  else
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 0>), dim3((unsigned)grid), dim3(BG_THREADS), 0, s,
-                       static_cast<const bf16_t *>(a.A), a.offsets, a.num_groups, static_cast<const bf16_t *>(a.W),
-                       a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
+                     s,
+                     static_cast<const bf16_t *>(a.A), a.offsets, a.num_groups, static_cast<const bf16_t *>(a.W),
+                     a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
   return hipGetLastError();
+}
+
+// Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
+hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  return a.swiglu ? launch_big<true, 4, 4, true>(a, rows_total_max, s)
+                  : launch_big<false, 4, 4, true>(a, rows_total_max, s);
 }
 
 }  // namespace moe
