@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle's sample (0: pick by workload)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="after the run, copy a buffer of this many MiB three times (a kernel of known traffic for "
+                        "scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -52,8 +55,8 @@ def source_hash(paths) -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this layer runs on a single "
-              f"MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs the layer on a "
+              f"single MI355X and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -212,6 +215,14 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(inp, cap, sample, min_seconds=10.0):
