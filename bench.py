@@ -95,11 +95,11 @@ def main():
 
     # ---------------------------------------------------------------- per-stage HIP-event timing
     # The same kernels as moe_forward, called stage by stage through the C ABI, with events on
-    # the stream the library launches on (torch's current stream).
+    # the stream the library launches on (torch's current stream).  As in moe_forward, the
+    # gate_up projection gathers token rows from x through row_token (no x_perm).
     r = layer.routing
     desc = layer.desc
     Rmax = ops.moe_max_rows(desc)
-    x_perm = torch.empty((max(Rmax, 1), d), dtype=inp.x.dtype, device=dev)
     hid = torch.empty((max(Rmax, 1), f), dtype=inp.x.dtype, device=dev)
     y_perm = torch.empty((max(Rmax, 1), d), dtype=inp.x.dtype, device=dev)
     out = torch.empty_like(inp.x)
@@ -121,11 +121,11 @@ def main():
         mark()
         ops.moe_router_topk(desc, r["logits"], r["topk_ids"], r["topk_gates"])
         mark()
-        ops.moe_dispatch_permute(desc, r["topk_ids"], inp.x, r["expert_counts"], r["expert_offsets"], r["slot"],
-                                 r["row_token"], x_perm, layer.ws)
+        ops.moe_dispatch_permute(desc, r["topk_ids"], None, r["expert_counts"], r["expert_offsets"], r["slot"],
+                                 r["row_token"], None, layer.ws)
         mark()
-        ops.moe_grouped_gate_up_swiglu(E, Rmax, grm, d, f, inp.x.dtype, x_perm, r["expert_offsets"], inp.w_gate_up,
-                                       hid)
+        ops.moe_grouped_gate_up_swiglu(E, Rmax, grm, d, f, inp.x.dtype, inp.x, r["expert_offsets"], inp.w_gate_up,
+                                       hid, row_index=r["row_token"])
         mark()
         ops.moe_grouped_down(E, Rmax, grm, d, f, inp.x.dtype, hid, r["expert_offsets"], inp.w_down, y_perm)
         mark()

@@ -185,14 +185,18 @@ moe_status moe_grouped_swiglu_gemm(int32_t num_groups, int64_t rows_max, int32_t
                                    const void *w_down, void *y_rows, void *ws, size_t ws_bytes,
                                    hipStream_t stream);
 
-/* The two halves of moe_grouped_swiglu_gemm as single launches (same contracts):
- *   moe_grouped_gate_up_swiglu: h_rows[r] = silu(W_g[g] x_rows[r]) * (W_u[g] x_rows[r]),
- *     h_rows [rows_max, f] dtype (rounded to dtype);
- *   moe_grouped_down: y_rows[r] = W_d[g] h_rows[r], y_rows [rows_max, d] dtype.
- * No workspace.  Same sources as moe_grouped_swiglu_gemm. */
+/* The two halves of moe_grouped_swiglu_gemm as single launches (same contracts; same
+ * sources; no workspace):
+ *   moe_grouped_gate_up_swiglu: h_rows[r] = silu(W_g[g] a_r) * (W_u[g] a_r), h_rows
+ *     [rows_max, f] dtype (rounded to dtype), where a_r = x_rows[r], or, when row_index
+ *     is not NULL, a_r = x_rows[row_index[r]] with x_rows holding x_row_count rows (a
+ *     row gather: the dispatch's row_token lets the projection read token rows straight
+ *     from x, so x_perm need not exist; x_rows must then be < 2 GiB);
+ *   moe_grouped_down: y_rows[r] = W_d[g] h_rows[r], y_rows [rows_max, d] dtype. */
 moe_status moe_grouped_gate_up_swiglu(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
-                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *group_offsets,
-                                      const void *w_gate_up, void *h_rows, hipStream_t stream);
+                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *row_index,
+                                      int64_t x_row_count, const int32_t *group_offsets, const void *w_gate_up,
+                                      void *h_rows, hipStream_t stream);
 moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
                             int32_t d_ff, int32_t dtype, const void *h_rows, const int32_t *group_offsets,
                             const void *w_down, void *y_rows, hipStream_t stream);
@@ -212,7 +216,7 @@ moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const
 
 /* The whole layer: router linear, top-k, dispatch, routed grouped SwiGLU FFN, the
  * shared expert if desc->d_ff_shared > 0, and combine.
- *   x [T, d] dtype; logit_offset [E] float or NULL; out [T, d] dtype
+ *   x [T, d] dtype, smaller than 2 GiB; logit_offset [E] float or NULL; out [T, d] dtype
  *   routing: NULL, or a struct whose non-NULL fields receive the routing tables
  *   ws: at least moe_workspace_size(desc) bytes */
 moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,

@@ -84,6 +84,8 @@ moe_status check_desc(const moe_desc *desc) {
   if (D.d_ff_shared < 0) return fail(MOE_ERR_INVALID, "d_ff_shared %d < 0", D.d_ff_shared);
   if ((int64_t)D.num_tokens * D.top_k > INT32_MAX)
     return fail(MOE_ERR_INVALID, "num_tokens * top_k exceeds INT32_MAX");
+  if ((int64_t)D.num_tokens * D.d_model * (int64_t)elem_bytes(D.dtype) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "x must be smaller than 2 GiB (32-bit row gather offsets)");
   return check_dtype_dims(D.dtype, D.d_model, D.d_ff, D.d_ff_shared);
 }
 
@@ -104,7 +106,7 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, ids, gates, counts, offsets, slot, row_token, hist, x_perm, hidden, y_perm, sh_hidden, sh_out,
+  size_t logits, ids, gates, counts, offsets, slot, row_token, hist, hidden, y_perm, sh_hidden, sh_out,
       sh_offsets, total;
 };
 
@@ -126,7 +128,6 @@ Layout layout(const moe_desc &D) {
   L.slot = take(T * k * 4);
   L.row_token = take(R * 4);
   L.hist = take(moe::dispatch_workspace_bytes((int)T, (int)E));
-  L.x_perm = take(R * d * s);
   L.hidden = take(R * f * s);
   L.y_perm = take(R * d * s);
   L.sh_hidden = take(fs ? T * fs * s : 0);
@@ -142,9 +143,12 @@ P *at(void *ws, size_t off) {
 }
 
 moe::GroupedGemmArgs projection_args(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f,
-                                     const void *in, const int32_t *offsets, const void *w, void *out, bool gate_up) {
+                                     const void *in, const int32_t *offsets, const void *w, void *out, bool gate_up,
+                                     const int32_t *row_index = nullptr, int64_t in_rows = 0) {
   moe::GroupedGemmArgs a{};
   a.A = in;
+  a.row_index = row_index;
+  a.a_rows = in_rows;
   a.offsets = offsets;
   a.num_groups = G;
   a.group_rows_max = group_rows_max;
@@ -173,8 +177,10 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
 
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
-                           void *y_rows, void *hidden, hipStream_t s) {
-  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true),
+                           void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
+                           int64_t x_row_count = 0) {
+  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true,
+                                         row_index, x_row_count),
                          dtype, s, "gate_up grouped GEMM"));
   MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false),
                          dtype, s, "down grouped GEMM"));
@@ -302,16 +308,24 @@ moe_status moe_grouped_swiglu_gemm(int32_t num_groups, int64_t rows_max, int32_t
 }
 
 moe_status moe_grouped_gate_up_swiglu(int32_t num_groups, int64_t rows_max, int32_t group_rows_max, int32_t d_model,
-                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *group_offsets,
-                                      const void *w_gate_up, void *h_rows, hipStream_t stream) {
+                                      int32_t d_ff, int32_t dtype, const void *x_rows, const int32_t *row_index,
+                                      int64_t x_row_count, const int32_t *group_offsets, const void *w_gate_up,
+                                      void *h_rows, hipStream_t stream) {
   MOE_TRY(check_projection(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype));
   if (rows_max == 0) return ok();
   MOE_TRY(check_ptr(x_rows, "x_rows"));
+  MOE_TRY(check_opt_ptr(row_index, "row_index"));
+  if (row_index) {
+    if (x_row_count < 1) return fail(MOE_ERR_INVALID, "x_row_count %lld < 1 with a row_index", (long long)x_row_count);
+    if (x_row_count * d_model * (int64_t)elem_bytes(dtype) >= ((int64_t)1 << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "gathered activations must be smaller than 2 GiB");
+  }
   MOE_TRY(check_ptr(group_offsets, "group_offsets"));
   MOE_TRY(check_ptr(w_gate_up, "w_gate_up"));
   MOE_TRY(check_ptr(h_rows, "h_rows"));
   MOE_TRY(run_projection(projection_args(num_groups, rows_max, (int32_t)std::min<int64_t>(group_rows_max, rows_max),
-                                         d_model, d_ff, x_rows, group_offsets, w_gate_up, h_rows, true),
+                                         d_model, d_ff, x_rows, group_offsets, w_gate_up, h_rows, true, row_index,
+                                         x_row_count),
                          dtype, stream, "gate_up grouped GEMM"));
   return ok();
 }
@@ -393,7 +407,6 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
   const int T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
   const bool bf = D.dtype == MOE_DTYPE_BF16;
   const int64_t rmax = max_rows(D);
-  void *x_perm = at<void>(ws, L.x_perm);
   void *y_perm = at<void>(ws, L.y_perm);
 
   if (bf)
@@ -409,10 +422,10 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
                                    stream),
               "dispatch");
   if (rmax > 0) {
-    MOE_TRY_HIP(moe::launch_gather_rows(x, row_token, offsets + E, rmax, d, (int)elem_bytes(D.dtype), x_perm, stream),
-                "gather rows");
-    MOE_TRY(run_grouped_ffn(E, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x_perm, offsets,
-                            weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden), stream));
+    // the gate_up projection gathers each expert's token rows from x through row_token,
+    // so the permuted copy of x is never materialised
+    MOE_TRY(run_grouped_ffn(E, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x, offsets,
+                            weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden), stream, row_token, T));
   }
   const void *shared = nullptr;
   if (fs > 0) {

@@ -74,19 +74,25 @@ __device__ __forceinline__ void find_group(const int32_t *offsets, int G, int m_
 //
 // WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
 // 4: eight waves of 128 x 64, two per SIMD).
-template <bool SWIGLU, int WN_W, int NBUF, bool PING>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32>
 __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
+                                                                         const int32_t *__restrict__ row_index,
+                                                                         int64_t a_rows,
                                                                          const int32_t *__restrict__ offsets, int G,
                                                                          const bf16_t *__restrict__ W,
                                                                          int64_t wstride, int n_out, int K,
                                                                          bf16_t *__restrict__ out, int n_tiles) {
-  constexpr int BK = 32;
+  constexpr int BK = BKP;                        // K per step: 32 or 64
+  constexpr int RB = BK * 2;                     // bytes per tile row
+  constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
+  constexpr int RPI = 1024 / RB;                 // tile rows per 1 KB load instruction (16 or 8)
   constexpr int NT = 128 * WN_W;                 // threads
   constexpr int NW = NT / 64;                    // waves
   constexpr int NI = BG_BN / WN_W / 32;          // 32-wide weight blocks per wave
   constexpr int TILE = BG_BM * BK * 2;           // 16 KB per operand and stage
   constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
   static_assert(NBUF >= 2 && NBUF <= 4, "stages");
+  static_assert(BK == 32 || BK == 64, "K step");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[NBUF > 2 ? TILE : 16],
       sA3[NBUF > 3 ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[NBUF > 2 ? TILE : 16],
@@ -126,17 +132,27 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   const uint32_t kbytes = (uint32_t)K * 2u;
   const int n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
 
-  const rsrc_t ares = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
+  // A rows: contiguous from m0, or gathered from the unpermuted activations by row_index
+  const rsrc_t ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes))
+                                : make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
   const rsrc_t wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
 
+  // Swizzle of a row's 16-byte chunks.  32-wide steps: 64-byte rows, chunk c of row r
+  // at c ^ ((r >> 2) & 3); 64-wide steps: 128-byte rows, at c ^ ((r >> 1) & 7).  Either
+  // way 16 consecutive rows read at one logical chunk land on 16 distinct 16-byte bank
+  // groups of a 256-byte LDS cycle, and rows 32 apart keep the same swizzle.
+  auto swz = [&](int r) -> int { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int blk = wave * IPW + i;
-    const int r = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
+    const int r = blk * RPI + lane / NCH;
+    const int c = (lane % NCH) ^ swz(r);
+    if (row_index)
+      agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
+    else
+      agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
     int wr;  // weight row held in tile row r, -1 past n_out
     if (SWIGLU) {
       const int col = n0 + (r & 127);
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
-      buf_ld16_lds(ares, ok ? agoff[i] + kc : kOob, la + blk * 1024);
+      buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kc : kOob, la + blk * 1024);
       buf_ld16_lds(wres, (ok && bgoff[i] != kOob) ? bgoff[i] + kc : kOob, lb + blk * 1024);
     }
   };
@@ -169,21 +185,21 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   // is 32 rows further (same swizzle), a constant distance.
   const int ar0 = wm * 128 + (lane & 31);
   const int br0 = SWIGLU ? wn * (NI / 2) * 32 + (lane & 31) : wn * NI * 32 + (lane & 31);
-  auto roff = [&](int r, int c) -> int { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); };
+  auto roff = [&](int r, int c) -> int { return r * RB + ((c ^ swz(r)) << 4); };
   auto compute = [&](int b) {
     const uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
       const uint8_t *pa = la + roff(ar0, c);
       const uint8_t *pb = lb + roff(br0, c);
       u32x4 af[4], bfr[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * 64);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * RB);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
-        bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * 64);
+        bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -229,24 +245,34 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     //   loads of step k + 1 in mem(k), before the barrier that precedes every read of
     //   step k + 1.  A stage is refilled (step k + 3 in mem(k)) only after the barrier
     //   that follows both groups' reads of its previous step k - 1.
-    static_assert(NBUF == 4 && IPW == 2, "ping-pong schedule is written for 4 stages and 8 waves");
+    // Prefetch distance D = NBUF - 1 steps; a wave in mem(k) issues step k + D and
+    // completes its own loads of step k + 1 (at most D - 1 younger steps in flight).
+    static_assert(IPW == 2 || IPW == 4, "ping-pong schedule is written for eight waves");
+    constexpr int D = NBUF - 1;
     const bool second = wave >= 4;
-    u32x4 af[2][4], bfr[2][NI];
+    u32x4 af[BK / 16][4], bfr[BK / 16][NI];
+    auto wait_next = [&]() {
+      if constexpr (D == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (D == 2 && IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if constexpr (D == 2 && IPW == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if constexpr (D == 3 && IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if constexpr (D == 3 && IPW == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    };
     auto mem = [&](int kt, int b) {
-      issue(kt + 3, (b + 3) % NBUF);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's loads of step kt + 1 done
+      issue(kt + D, (b + D) % NBUF);
+      wait_next();  // this wave's loads of step kt + 1 done
       const uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < BK / 16; ++kk) {
         const int c = kk * 2 + (lane >> 5);
         const uint8_t *pa = la + roff(ar0, c);
         const uint8_t *pb = lb + roff(br0, c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[kk][i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * 64);
+        for (int i = 0; i < 4; ++i) af[kk][i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * RB);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
-          bfr[kk][j] = *reinterpret_cast<const u32x4 *>(pb + dr * 64);
+          bfr[kk][j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -254,7 +280,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     auto comp = [&]() {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -266,11 +292,11 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    // prologue: steps 0..2 issued; step 0 landed for every wave before the first read
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // prologue: steps 0 .. D-1 issued; step 0 landed for every wave before the first read
+#pragma unroll
+    for (int b = 0; b < D; ++b) issue(b, b);
+    if constexpr (D == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else wait_next();
     bar();
     if (second) bar();
     for (int k0 = 0; k0 < nk; k0 += NBUF) {
@@ -315,16 +341,16 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 
 }  // namespace
 
-template <bool SWIGLU, int WN_W, int NBUF, bool PING = false>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
   const int64_t grid = m_tiles * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
-                     s,
-                     static_cast<const bf16_t *>(a.A), a.offsets, a.num_groups, static_cast<const bf16_t *>(a.W),
-                     a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
+                     s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
+                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out),
+                     n_tiles);
   return hipGetLastError();
 }
 

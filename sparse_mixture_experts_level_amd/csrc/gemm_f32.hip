@@ -14,6 +14,7 @@ constexpr int FK = 16;   // K per LDS stage
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float *__restrict__ A,
+                                                               const int32_t *__restrict__ row_index,
                                                                const int32_t *__restrict__ offsets,
                                                                const float *__restrict__ W, int64_t wstride,
                                                                int n_out, int K, float *__restrict__ out,
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float *__re
       for (int idx = tid; idx < FT * FK; idx += 256) {
         const int r = idx / FK, kk = idx % FK;
         const bool kin = k0 + kk < K;
-        sA[kk][r] = (r < rows && kin) ? A[(size_t)(m0 + r) * K + k0 + kk] : 0.f;
+        const size_t arow = row_index ? (size_t)(r < rows ? row_index[m0 + r] : 0) : (size_t)(m0 + r);
+        sA[kk][r] = (r < rows && kin) ? A[arow * K + k0 + kk] : 0.f;
         const int n = n0 + r;
         sG[kk][r] = (n < n_out && kin) ? Wg[(size_t)n * K + k0 + kk] : 0.f;
         if constexpr (SWIGLU) sU[kk][r] = (n < n_out && kin) ? Wg[(size_t)(n_out + n) * K + k0 + kk] : 0.f;
@@ -83,11 +85,13 @@ hipError_t launch_grouped_gemm_f32(const GroupedGemmArgs &a, hipStream_t s) {
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
   if (a.swiglu)
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s,
-                       static_cast<const float *>(a.A), a.offsets, static_cast<const float *>(a.W), a.w_group_stride,
+                       static_cast<const float *>(a.A), a.row_index, a.offsets, static_cast<const float *>(a.W),
+                       a.w_group_stride,
                        a.n_out, a.K, static_cast<float *>(a.out), n_tiles);
   else
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s,
-                       static_cast<const float *>(a.A), a.offsets, static_cast<const float *>(a.W), a.w_group_stride,
+                       static_cast<const float *>(a.A), a.row_index, a.offsets, static_cast<const float *>(a.W),
+                       a.w_group_stride,
                        a.n_out, a.K, static_cast<float *>(a.out), n_tiles);
   return hipGetLastError();
 }

@@ -135,6 +135,8 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 // including the few heavily loaded ones -- over all XCDs.
 template <int BM, int NSUB, bool SWIGLU, int P>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
+                                                                     const int32_t *__restrict__ row_index,
+                                                                     int64_t a_rows,
                                                                      const int32_t *__restrict__ offsets,
                                                                      const bf16_t *__restrict__ W, int64_t wstride,
                                                                      int n_out, int K, bf16_t *__restrict__ out,
@@ -161,17 +163,30 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_
     const int r = ncol0 + sidx * 16 + (lane & 15) + (b >= NSUB ? n_out : 0);
     boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane >> 4) * 16u : kOob;
   }
-  uint32_t aoff[A_PER_T];  // byte offset of this thread's A pieces at k = 0 (row r, 16-byte column c8)
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int q = tid + 256 * i;
-    aoff[i] = q < BM * 8 ? (uint32_t)(q >> 3) * kbytes + (uint32_t)(q & 7) * 16u : kOob;
-  }
   const int nk = K / SG_KC;
 
   for (int m0 = row_begin; m0 < row_end; m0 += BM) {
     const int rows = min(BM, row_end - m0);
-    const rsrc_t ares = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
+    // byte offset of this thread's A pieces at k = 0 (row r, 16-byte column c8); with a
+    // row gather the rows come straight from the unpermuted activations
+    uint32_t aoff[A_PER_T];
+    rsrc_t ares;
+    if (row_index) {
+      ares = make_rsrc(A, (uint32_t)(a_rows * kbytes));
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q >> 3;
+        aoff[i] = (q < BM * 8 && r < rows) ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)(q & 7) * 16u : kOob;
+      }
+    } else {
+      ares = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const int q = tid + 256 * i;
+        aoff[i] = q < BM * 8 ? (uint32_t)(q >> 3) * kbytes + (uint32_t)(q & 7) * 16u : kOob;
+      }
+    }
     const int na = (rows * 8 + 255) / 256;  // workgroup-uniform
 #define SG_BLOCK(N)                                                                                                 \
   if constexpr (N <= A_PER_T) {                                                                                     \
@@ -195,7 +210,7 @@ hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
   const int n_tiles = (a.n_out + cols_per_tile - 1) / cols_per_tile;
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
   hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, P>), dim3((unsigned)grid), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(a.A), a.offsets, static_cast<const bf16_t *>(a.W), a.w_group_stride,
+                     static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, static_cast<const bf16_t *>(a.W), a.w_group_stride,
                      a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
   return hipGetLastError();
 }

@@ -35,6 +35,10 @@ hipError_t launch_gather_rows(const void *x, const int32_t *row_token, const int
 // out[r, n] = A_r . W_g[n].  `w_group_stride` is in elements.
 struct GroupedGemmArgs {
   const void *A;
+  // Optional row gather: with row_index set, row r of a group is A[row_index[r]] and A
+  // holds a_rows rows; otherwise rows are contiguous in A.
+  const int32_t *row_index;
+  int64_t a_rows;
   const int32_t *offsets;
   int num_groups;
   int group_rows_max;  // tiling hint

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
     L.moe_dispatch_permute.restype = st
     L.moe_grouped_swiglu_gemm.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_grouped_swiglu_gemm.restype = st
-    L.moe_grouped_gate_up_swiglu.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_grouped_gate_up_swiglu.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, i64, vp, vp, vp, vp]
     L.moe_grouped_gate_up_swiglu.restype = st
     L.moe_grouped_down.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.moe_grouped_down.restype = st
@@ -179,11 +179,13 @@ def moe_grouped_swiglu_gemm(num_groups, rows_max, group_rows_max, d_model, d_ff,
 
 
 def moe_grouped_gate_up_swiglu(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, x_rows, group_offsets,
-                               w_gate_up, h_rows, stream=None) -> None:
+                               w_gate_up, h_rows, row_index=None, stream=None) -> None:
     code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    n_x = 0 if row_index is None else x_rows.shape[0]
     _check(lib().moe_grouped_gate_up_swiglu(int(num_groups), int(rows_max), int(group_rows_max), int(d_model),
-                                            int(d_ff), code, _ptr(x_rows), _ptr(group_offsets), _ptr(w_gate_up),
-                                            _ptr(h_rows), _stream(stream)), "moe_grouped_gate_up_swiglu")
+                                            int(d_ff), code, _ptr(x_rows), _ptr(row_index), int(n_x),
+                                            _ptr(group_offsets), _ptr(w_gate_up), _ptr(h_rows), _stream(stream)),
+           "moe_grouped_gate_up_swiglu")
 
 
 def moe_grouped_down(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, h_rows, group_offsets, w_down,

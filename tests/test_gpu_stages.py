@@ -213,6 +213,42 @@ def test_grouped_gemm_f32(sizes, d, f):
     _gemm_case(sizes, d, f, torch.float32, max(sizes))
 
 
+@pytest.mark.parametrize("sizes,d,f,dtype,hint", [
+    ([0, 1, 17, 130, 5, 0, 64, 33], 256, 192, torch.bfloat16, 130),  # streaming kernel
+    ([600, 0, 300, 1000], 256, 192, torch.bfloat16, 1000),           # large-tile kernel
+    ([0, 3, 40, 9], 100, 72, torch.float32, 40),
+])
+def test_gate_up_row_gather(sizes, d, f, dtype, hint):
+    """gate_up with row_index: rows are read from an unpermuted activation matrix."""
+    G = len(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offs[-1])
+    T = max(1, R // 2 + 7)
+    say(f"gate_up gather G={G} sizes={sizes} T={T} {dtype}")
+    rng = np.random.default_rng(G)
+    idx = rng.integers(0, T, size=R).astype(np.int32)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dtype)
+    wgu = (torch.randn((G, 2 * f, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
+    h = torch.full((R + 3, f), 5.0, dtype=dtype, device=DEV)
+    go = torch.from_numpy(offs).to(DEV)
+    ops.moe_grouped_gate_up_swiglu(G, R + 3, hint, d, f, dtype, x, go, wgu, h,
+                                   row_index=torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    xn, hn = to_np(x).astype(np.float64), to_np(h)
+    W1 = HostExperts(wgu)
+    worst = 0.0
+    for e in range(G):
+        lo, hi = offs[e], offs[e + 1]
+        if hi > lo:
+            Wg = W1[e]
+            X = xn[idx[lo:hi]]
+            ref = oracle.silu(X @ Wg[:f].T) * (X @ Wg[f:].T)
+            worst = max(worst, row_rel_err(hn[lo:hi], ref))
+    assert np.all(hn[R:] == 5.0)
+    assert worst <= (1e-2 if dtype == torch.bfloat16 else 1e-5), worst
+
+
 # ------------------------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("T,E,k,cap,d,dtype,shared", [
