@@ -134,17 +134,40 @@ def main():
         mark()
         return marks
 
-    if fs == 0:
-        for _ in range(args.warmup):
-            staged_step(False)
-        all_marks = [staged_step(True) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for marks in all_marks:
-            for i, s in enumerate(stages):
-                ev[s].append(marks[i].elapsed_time(marks[i + 1]) * 1e3)  # us
-        stage_us = {s: float(np.mean(v)) for s, v in ev.items()}
-    else:
-        stage_us = {}
+    if fs:
+        # the shared expert: the same grouped GEMMs with one group of all T tokens
+        stages += ["shared_gate_up", "shared_down"]
+        ev.update({"shared_gate_up": [], "shared_down": []})
+        sh_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        sh_hid = torch.empty((T, fs), dtype=inp.x.dtype, device=dev)
+        sh_out = torch.empty_like(inp.x)
+
+    def staged_shared(marks, record):
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                marks.append(e)
+        ops.moe_grouped_gate_up_swiglu(1, T, T, d, fs, inp.x.dtype, inp.x, sh_off, inp.w_shared_gate_up, sh_hid)
+        mark()
+        ops.moe_grouped_down(1, T, T, d, fs, inp.x.dtype, sh_hid, sh_off, inp.w_shared_down, sh_out)
+        mark()
+
+    for _ in range(args.warmup):
+        m = staged_step(False)
+        if fs:
+            staged_shared(m, False)
+    all_marks = []
+    for _ in range(args.steps):
+        m = staged_step(True)
+        if fs:
+            staged_shared(m, True)
+        all_marks.append(m)
+    torch.cuda.synchronize()
+    for marks in all_marks:
+        for i, s in enumerate(stages):
+            ev[s].append(marks[i].elapsed_time(marks[i + 1]) * 1e3)  # us
+    stage_us = {s: float(np.mean(v)) for s, v in ev.items()}
 
     # ---------------------------------------------------------------- roofline of the dominant kernel
     gate_up_bytes = E_t * 2 * f * d * s_bytes + R * d * s_bytes + R * f * s_bytes

@@ -214,6 +214,19 @@ moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const
                                  const int32_t *expert_offsets, const void *shared_out, void *out,
                                  hipStream_t stream);
 
+/* Switch-style auxiliary load-balancing loss ([SMoE] "Маршрутизация токена и auxiliary
+ * loss"): loss = alpha * E * sum_i f_i * P_i, where f_i = expert_counts[i] / (T * k) is
+ * the share of the batch's assignments routed to expert i (router choice, before
+ * capacity) and P_i the softmax probability of expert i averaged over the T tokens.
+ * For k = 1 this is the page's formula; uniform routing gives alpha.
+ *   logits        [T, E] float (as written by moe_router_logits)
+ *   expert_counts [E] int32 (as written by moe_dispatch_permute)
+ *   loss          [1] float, written (device)
+ *   ws            at least moe_workspace_size(desc) bytes
+ * Float accumulation in fixed orders: bit-reproducible. */
+moe_status moe_router_aux_loss(const moe_desc *desc, const float *logits, const int32_t *expert_counts, float alpha,
+                               float *loss, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* The whole layer: router linear, top-k, dispatch, routed grouped SwiGLU FFN, the
  * shared expert if desc->d_ff_shared > 0, and combine.
  *   x [T, d] dtype, smaller than 2 GiB; logit_offset [E] float or NULL; out [T, d] dtype

@@ -127,7 +127,7 @@ Layout layout(const moe_desc &D) {
   L.offsets = take((E + 1) * 4);
   L.slot = take(T * k * 4);
   L.row_token = take(R * 4);
-  L.hist = take(moe::dispatch_workspace_bytes((int)T, (int)E));
+  L.hist = take(std::max(moe::dispatch_workspace_bytes((int)T, (int)E), moe::aux_loss_workspace_bytes((int)T, (int)E)));
   L.hidden = take(R * f * s);
   L.y_perm = take(R * d * s);
   L.sh_hidden = take(fs ? T * fs * s : 0);
@@ -362,6 +362,24 @@ moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const
   MOE_TRY_HIP(moe::launch_combine(y_perm, topk_ids, topk_gates, slot, expert_offsets, shared_out, out, D.num_tokens,
                                   D.d_model, D.top_k, D.dtype == MOE_DTYPE_BF16, stream),
               "combine");
+  return ok();
+}
+
+moe_status moe_router_aux_loss(const moe_desc *desc, const float *logits, const int32_t *expert_counts, float alpha,
+                               float *loss, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(expert_counts, "expert_counts"));
+  MOE_TRY(check_ptr(loss, "loss"));
+  const size_t need = moe::aux_loss_workspace_bytes(D.num_tokens, D.num_experts);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "aux loss needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+  MOE_TRY_HIP(moe::launch_aux_loss(logits, expert_counts, D.num_tokens, D.num_experts, D.top_k, alpha, loss,
+                                   static_cast<float *>(ws), stream),
+              "aux loss");
   return ok();
 }
 

@@ -60,6 +60,11 @@ hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *g
                           const int32_t *offsets, const void *shared, void *out, int T, int d, int k, bool bf16,
                           hipStream_t s);
 
+// ---- auxiliary load-balancing loss (aux_loss.hip)
+size_t aux_loss_workspace_bytes(int T, int E);
+hipError_t launch_aux_loss(const float *logits, const int32_t *counts, int T, int E, int k, float alpha, float *loss,
+                           float *partial_ws, hipStream_t s);
+
 // ---- small utilities (combine.hip)
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v0, int32_t step, hipStream_t s);
 

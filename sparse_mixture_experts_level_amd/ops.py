@@ -27,7 +27,7 @@ SYMBOLS = [
     "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_grouped_gemm_workspace_size",
     "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
     "moe_dispatch_permute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
-    "moe_combine_unpermute", "moe_forward",
+    "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward",
 ]
 
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.moe_grouped_down.restype = st
     L.moe_combine_unpermute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine_unpermute.restype = st
+    L.moe_router_aux_loss.argtypes = [dp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+    L.moe_router_aux_loss.restype = st
     L.moe_forward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward.restype = st
     _lib = L
@@ -201,6 +203,12 @@ def moe_combine_unpermute(desc, y_perm, topk_ids, topk_gates, slot, expert_offse
     _check(lib().moe_combine_unpermute(ctypes.byref(desc), _ptr(y_perm), _ptr(topk_ids), _ptr(topk_gates), _ptr(slot),
                                        _ptr(expert_offsets), _ptr(shared_out), _ptr(out), _stream(stream)),
            "moe_combine_unpermute")
+
+
+def moe_router_aux_loss(desc, logits, expert_counts, alpha, loss, ws, stream=None) -> None:
+    _check(lib().moe_router_aux_loss(ctypes.byref(desc), _ptr(logits), _ptr(expert_counts), float(alpha), _ptr(loss),
+                                     _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_router_aux_loss")
 
 
 def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, routing: Optional[dict] = None,

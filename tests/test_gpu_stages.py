@@ -276,3 +276,58 @@ def test_combine(T, E, k, cap, d, dtype, shared):
     ref = oracle.combine(T, d, ids_np, gates_np.astype(np.float64), fill["slot"], rows,
                          shared=to_np(sh).astype(np.float64) if shared else None)
     assert row_rel_err(to_np(out), ref) <= (2 ** -8 if dtype == torch.bfloat16 else 1e-6)
+
+
+# ------------------------------------------------------------------------------------- aux loss
+
+def _aux_gpu(logits_np, k, alpha=0.01, cap=None):
+    T, E = logits_np.shape
+    desc = _desc(T, E, k, cap)
+    lg = torch.from_numpy(logits_np.astype(np.float32)).to(DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    slot = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    row_token = torch.empty(max(ops.moe_max_rows(desc), 1), dtype=torch.int32, device=DEV)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    loss = torch.full((1,), float("nan"), device=DEV)
+    ops.moe_router_topk(desc, lg, ids, gates)
+    ops.moe_dispatch_permute(desc, ids, None, counts, offsets, slot, row_token, None, ws)
+    ops.moe_router_aux_loss(desc, lg, counts, alpha, loss, ws)
+    torch.cuda.synchronize()
+    return float(loss.item()), to_np(ids)
+
+
+def test_aux_loss_reproduces_the_demo():
+    """The page's demo prints 0.010505 (balanced router) and 0.019086 (collapsed)."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "demo2_capacity_dropping.json")))
+    torch.manual_seed(42)
+    x = torch.randn(32, 64)
+    balanced = torch.nn.Linear(64, 8, bias=False)
+    collapsed = torch.nn.Linear(64, 8, bias=False)
+    with torch.no_grad():
+        collapsed.weight[0] += 5.0
+        lb, lc = balanced(x).numpy(), collapsed(x).numpy()
+    for name, lg in (("balanced", lb), ("collapsed", lc)):
+        say(f"aux loss demo {name}")
+        loss, _ = _aux_gpu(lg.astype(np.float64), 1, cap=ops.moe_capacity(32, 8, 1.0))
+        assert round(loss, 6) == g[name]["aux_loss"]
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 64, 2), (300, 8, 1), (777, 256, 8), (50, 1024, 3)])
+def test_aux_loss_matches_oracle(T, E, k):
+    say(f"aux loss T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E)
+    lg = rng.normal(size=(T, E)) * 2 + np.linspace(0, 3, E)[None, :]
+    loss, ids = _aux_gpu(lg, k, alpha=0.01)
+    ref = oracle.aux_load_balancing_loss(ids, oracle.softmax(lg.astype(np.float32).astype(np.float64)), E, 0.01)
+    assert loss == pytest.approx(ref, rel=2e-5)
+
+
+def test_aux_loss_uniform_is_alpha():
+    E, T = 16, 512
+    lg = np.zeros((T, E))
+    lg[np.arange(T), np.arange(T) % E] = 1e-3  # round-robin choice, nearly uniform probabilities
+    loss, _ = _aux_gpu(lg, 1, alpha=0.02)
+    assert loss == pytest.approx(0.02, rel=1e-3)
