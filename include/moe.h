@@ -236,6 +236,24 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
                        const float *logit_offset, void *out, moe_routing *routing, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* One rank's share of expert parallelism ([HF-MoE] "Параллелизм экспертов
+ * (Expert Parallelism)": each device holds a contiguous subset of the experts,
+ * computes them, and partial outputs are summed across devices with an all-reduce;
+ * global expert indices map to local ones and the other experts are masked).
+ * Routing, capacity and dispatch run over all E experts, so slots and drops are those
+ * of the whole layer; only experts [expert_begin, expert_end) run their FFN, with
+ * weights->w_gate_up / w_down holding just those experts ([expert_end - expert_begin,
+ * ...], local index 0 = expert_begin); the router weights are the full [E, d].
+ *   out_partial[t] = (add_shared ? shared(x_t) : 0)
+ *                    + sum over kept j with expert in range of g_tj * FFN_e(x_t)
+ * Summing the partials of a partition of [0, E) (shared expert added by exactly one
+ * range) gives moe_forward's output up to float summation order.  Other arguments as
+ * for moe_forward; 0 <= expert_begin <= expert_end <= E. */
+moe_status moe_forward_expert_shard(const moe_desc *desc, const moe_weights *weights, int32_t expert_begin,
+                                    int32_t expert_end, int32_t add_shared, const void *x, const float *logit_offset,
+                                    void *out_partial, moe_routing *routing, void *ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

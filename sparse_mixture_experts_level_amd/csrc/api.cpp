@@ -383,19 +383,29 @@ moe_status moe_router_aux_loss(const moe_desc *desc, const float *logits, const 
   return ok();
 }
 
-moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, const float *logit_offset,
-                       void *out, moe_routing *routing, void *ws, size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(check_desc(desc));
-  const moe_desc &D = *desc;
+}  // extern "C"
+
+namespace {
+
+// The layer for experts [e_begin, e_end) of the routing: routing, capacity and dispatch
+// over all experts (so slots are those of the whole layer), the FFN of the range's
+// experts with its weights (index 0 = expert e_begin), and the combine of their
+// contributions, plus the shared expert when add_shared.
+moe_status forward_range(const moe_desc &D, const moe_weights *weights, const void *x, const float *logit_offset,
+                         void *out, moe_routing *routing, void *ws, size_t ws_bytes, hipStream_t stream,
+                         int32_t e_begin, int32_t e_end, bool add_shared) {
   if (!weights) return fail(MOE_ERR_INVALID, "weights is NULL");
   if (D.num_tokens == 0) return ok();
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(out, "out"));
   MOE_TRY(check_ptr(weights->w_router, "w_router"));
-  MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
-  MOE_TRY(check_ptr(weights->w_down, "w_down"));
+  const bool any_local = e_end > e_begin;
+  if (any_local) {
+    MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
+    MOE_TRY(check_ptr(weights->w_down, "w_down"));
+  }
   MOE_TRY(check_opt_ptr(logit_offset, "logit_offset"));
-  if (D.d_ff_shared > 0) {
+  if (D.d_ff_shared > 0 && add_shared) {
     MOE_TRY(check_ptr(weights->w_shared_gate_up, "w_shared_gate_up"));
     MOE_TRY(check_ptr(weights->w_shared_down, "w_shared_down"));
   }
@@ -439,22 +449,49 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
   MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, counts, offsets, slot, row_token, at<int32_t>(ws, L.hist),
                                    stream),
               "dispatch");
-  if (rmax > 0) {
+  if (rmax > 0 && any_local) {
     // the gate_up projection gathers each expert's token rows from x through row_token,
-    // so the permuted copy of x is never materialised
-    MOE_TRY(run_grouped_ffn(E, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x, offsets,
-                            weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden), stream, row_token, T));
+    // so the permuted copy of x is never materialised; a range of experts is the slice
+    // [e_begin, e_end] of the offsets (rows stay in the whole layer's row space)
+    MOE_TRY(run_grouped_ffn(e_end - e_begin, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x,
+                            offsets + e_begin, weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden),
+                            stream, row_token, T));
   }
   const void *shared = nullptr;
-  if (fs > 0) {
+  if (fs > 0 && add_shared) {
     int32_t *sh_off = at<int32_t>(ws, L.sh_offsets);
     MOE_TRY_HIP(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "shared offsets");
     MOE_TRY(run_grouped_ffn(1, T, T, d, fs, D.dtype, x, sh_off, weights->w_shared_gate_up, weights->w_shared_down,
                             at<void>(ws, L.sh_out), at<void>(ws, L.sh_hidden), stream));
     shared = at<void>(ws, L.sh_out);
   }
-  MOE_TRY_HIP(moe::launch_combine(y_perm, ids, gates, slot, offsets, shared, out, T, d, k, bf, stream), "combine");
+  MOE_TRY_HIP(moe::launch_combine(y_perm, ids, gates, slot, offsets, shared, out, T, d, k, bf, stream, e_begin,
+                                  any_local ? e_end : e_begin),
+              "combine");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x, const float *logit_offset,
+                       void *out, moe_routing *routing, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  return forward_range(*desc, weights, x, logit_offset, out, routing, ws, ws_bytes, stream, 0, desc->num_experts,
+                       true);
+}
+
+moe_status moe_forward_expert_shard(const moe_desc *desc, const moe_weights *weights, int32_t expert_begin,
+                                    int32_t expert_end, int32_t add_shared, const void *x, const float *logit_offset,
+                                    void *out_partial, moe_routing *routing, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  if (expert_begin < 0 || expert_end < expert_begin || expert_end > desc->num_experts)
+    return fail(MOE_ERR_INVALID, "expert range [%d, %d) outside [0, %d]", expert_begin, expert_end,
+                desc->num_experts);
+  return forward_range(*desc, weights, x, logit_offset, out_partial, routing, ws, ws_bytes, stream, expert_begin,
+                       expert_end, add_shared != 0);
 }
 
 }  // extern "C"

@@ -4,6 +4,8 @@
 // probabilities; section "Expert capacity и capacity factor": a dropped assignment
 // adds nothing).  Each token gathers its kept rows -- no atomics, so the sum order
 // (shared expert first, then j = 0..k-1) is fixed and the result deterministic.
+// Contributions can be restricted to experts [e_begin, e_end) -- one rank's share of
+// expert parallelism.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
                                                       const int32_t *__restrict__ slot,
                                                       const int32_t *__restrict__ offsets,
                                                       const void *__restrict__ shared, void *__restrict__ out, int T,
-                                                      int d, int k) {
+                                                      int d, int k, int e_begin, int e_end) {
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * CB_TOK + (threadIdx.x >> 6);
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
         const int sl = slot[q];
         const int e = ids[q];
         my_gate = gates[q];
-        if (sl >= 0) my_row = (int64_t)offsets[e] + sl;
+        if (sl >= 0 && e >= e_begin && e < e_end) my_row = (int64_t)offsets[e] + sl;
       }
       const int kn = min(64, k - j0);
       for (int j = 0; j < kn; ++j) {
@@ -110,15 +112,17 @@ __global__ __launch_bounds__(256) void combine_f32_scalar_kernel(const float *__
                                                                  const int32_t *__restrict__ slot,
                                                                  const int32_t *__restrict__ offsets,
                                                                  const float *__restrict__ shared,
-                                                                 float *__restrict__ out, int d, int k) {
+                                                                 float *__restrict__ out, int d, int k, int e_begin,
+                                                                 int e_end) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x; c < d; c += 256) {
     float acc = shared ? shared[(size_t)t * d + c] : 0.f;
     for (int j = 0; j < k; ++j) {
       const size_t q = (size_t)t * k + j;
       const int sl = slot[q];
-      if (sl < 0) continue;
-      acc = fmaf(gates[q], y_perm[((size_t)offsets[ids[q]] + sl) * d + c], acc);
+      const int e = ids[q];
+      if (sl < 0 || e < e_begin || e >= e_end) continue;
+      acc = fmaf(gates[q], y_perm[((size_t)offsets[e] + sl) * d + c], acc);
     }
     out[(size_t)t * d + c] = acc;
   }
@@ -133,20 +137,21 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v0, int32_t step) {
 
 hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *gates, const int32_t *slot,
                           const int32_t *offsets, const void *shared, void *out, int T, int d, int k, bool bf16,
-                          hipStream_t s) {
+                          hipStream_t s, int e_begin, int e_end) {
   const int vec = bf16 ? 8 : 4;
   if (d % vec == 0) {
     const int grid = (T + CB_TOK - 1) / CB_TOK;
     if (bf16)
       hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, T, d, k);
+                         out, T, d, k, e_begin, e_end);
     else
       hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, T, d, k);
+                         out, T, d, k, e_begin, e_end);
   } else {
     if (bf16) return hipErrorInvalidValue;  // bf16 rows are validated to be multiples of 64
     hipLaunchKernelGGL(combine_f32_scalar_kernel, dim3(T), dim3(256), 0, s, static_cast<const float *>(y_perm), ids,
-                       gates, slot, offsets, static_cast<const float *>(shared), static_cast<float *>(out), d, k);
+                       gates, slot, offsets, static_cast<const float *>(shared), static_cast<float *>(out), d, k,
+                       e_begin, e_end);
   }
   return hipGetLastError();
 }

@@ -58,7 +58,7 @@ hipError_t launch_grouped_gemm_f32(const GroupedGemmArgs &a, hipStream_t s);
 // ---- combine (combine.hip)
 hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *gates, const int32_t *slot,
                           const int32_t *offsets, const void *shared, void *out, int T, int d, int k, bool bf16,
-                          hipStream_t s);
+                          hipStream_t s, int e_begin = 0, int e_end = 1 << 30);
 
 // ---- auxiliary load-balancing loss (aux_loss.hip)
 size_t aux_loss_workspace_bytes(int T, int E);

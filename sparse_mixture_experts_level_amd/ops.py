@@ -27,7 +27,7 @@ SYMBOLS = [
     "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_grouped_gemm_workspace_size",
     "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
     "moe_dispatch_permute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
-    "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward",
+    "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
 ]
 
 
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.moe_router_aux_loss.restype = st
     L.moe_forward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward.restype = st
+    L.moe_forward_expert_shard.argtypes = [dp, ctypes.POINTER(MoeWeights), i32, i32, i32, vp, vp, vp,
+                                           ctypes.POINTER(MoeRouting), vp, sz, vp]
+    L.moe_forward_expert_shard.restype = st
     _lib = L
     return L
 
@@ -220,6 +223,21 @@ def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, rou
     _check(lib().moe_forward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(logit_offset), _ptr(out),
                              ctypes.byref(R) if R is not None else None, _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_expert_shard(desc, w_router, w_gate_up_local, w_down_local, expert_begin, expert_end, add_shared, x,
+                             logit_offset, out_partial, ws, routing: Optional[dict] = None, w_shared_gate_up=None,
+                             w_shared_down=None, stream=None) -> None:
+    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up_local), _ptr(w_down_local), _ptr(w_shared_gate_up),
+                   _ptr(w_shared_down))
+    R = None
+    if routing is not None:
+        R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
+    _check(lib().moe_forward_expert_shard(ctypes.byref(desc), ctypes.byref(W), int(expert_begin), int(expert_end),
+                                          int(bool(add_shared)), _ptr(x), _ptr(logit_offset), _ptr(out_partial),
+                                          ctypes.byref(R) if R is not None else None, _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward_expert_shard")
 
 
 class MoELayer:

@@ -142,3 +142,48 @@ def test_full_size_workloads(name, nsample):
     say(f"  max row rel err {res['err']:.3e}, near-tie routing differences {res['differ']}, drops {res['drops']}")
     del res
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,d,E,k,f,cf,fs,nshards", [
+    (300, 256, 8, 2, 192, 1.25, 64, 2),
+    (513, 128, 16, 4, 128, None, 0, 4),
+    (256, 128, 8, 1, 64, 1.0, 64, 8),   # one expert per rank
+])
+def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards):
+    """Each rank's partial equals the layer with the other experts masked (the oracle with their
+    weights zeroed); the partials of a partition sum to the whole layer."""
+    w = wl.Workload("ep", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset="boost4")
+    say(f"expert shards T={T} E={E} k={k} shards={nshards} shared={fs}")
+    inp = wl.make_inputs(w, seed=5, device=DEV)
+    cap = ops.moe_capacity(T, E, cf)
+    desc = ops.make_desc(T, d, f, E, k, cap, fs, torch.bfloat16)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    full = torch.empty_like(inp.x)
+    ops.moe_forward(desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, inp.logit_offset, full, ws,
+                    w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down)
+    x = to_np(inp.x).astype(np.float64)
+    wr = to_np(inp.w_router).astype(np.float64)
+    off = to_np(inp.logit_offset)
+    gu = to_np(inp.w_gate_up).astype(np.float64)
+    dn = to_np(inp.w_down).astype(np.float64)
+    sgu = to_np(inp.w_shared_gate_up).astype(np.float64) if fs else None
+    sd = to_np(inp.w_shared_down).astype(np.float64) if fs else None
+    total = torch.zeros((T, d), dtype=torch.float32, device=DEV)
+    per = E // nshards
+    for r in range(nshards):
+        b, e = r * per, (r + 1) * per
+        part = torch.full_like(inp.x, 9.0)
+        ops.moe_forward_expert_shard(desc, inp.w_router, inp.w_gate_up[b:e].contiguous(),
+                                     inp.w_down[b:e].contiguous(), b, e, r == 0, inp.x, inp.logit_offset, part, ws,
+                                     w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down)
+        torch.cuda.synchronize()
+        total += part.float()
+        mgu, mdn = np.zeros_like(gu), np.zeros_like(dn)
+        mgu[b:e], mdn[b:e] = gu[b:e], dn[b:e]
+        ref = oracle.moe_forward(x, wr, mgu, mdn, k, cap, off,
+                                 w_shared_gate_up=sgu if r == 0 else None, w_shared_down=sd if r == 0 else None)
+        assert row_rel_err(to_np(part), ref["out"]) <= 2e-2
+    torch.cuda.synchronize()
+    full_ref = oracle.moe_forward(x, wr, gu, dn, k, cap, off, w_shared_gate_up=sgu, w_shared_down=sd)["out"]
+    assert row_rel_err(to_np(total), full_ref) <= 2e-2
+    assert row_rel_err(to_np(total), to_np(full).astype(np.float64)) <= 2e-2
