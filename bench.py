@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after the run, copy a buffer of this many MiB three times (a kernel of known traffic for "
                         "scaling hardware byte counters)")
+    p.add_argument("--ep-shards", type=int, default=1, metavar="N",
+                   help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
+                        "contiguous ranges, every range timed on this GPU, the slowest one reported")
     return p.parse_args()
 
 
@@ -72,6 +75,8 @@ def main():
     layer = ops.MoELayer(inp, cap, device=dev)
     T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
     s_bytes = 2 if w.dtype == "bf16" else 4
+    if args.ep_shards > 1:
+        return ep_share_bench(args, w, inp, cap, layer, s_bytes)
 
     # ---------------------------------------------------------------- whole-path timing
     for _ in range(args.warmup):
@@ -246,6 +251,77 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def ep_share_bench(args, w, inp, cap, layer, s_bytes):
+    """One rank's share of expert parallelism at the layer's real shapes: every rank runs the
+    router, top-k and dispatch for all T tokens and the FFN of its E/N experts (rank 0 also the
+    shared expert), writing a partial output that an all-reduce would sum.  Each rank's share is
+    timed here in turn on the one GPU; a step of N ranks takes as long as the slowest share plus
+    the all-reduce, which is not part of this measurement."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_level_amd.ops as ops
+
+    T, d, E, f, fs = w.num_tokens, w.d_model, w.num_experts, w.d_ff, w.d_ff_shared
+    N = args.ep_shards
+    if E % N:
+        print(f"--ep-shards {N} does not divide the {E} experts", file=sys.stderr)
+        sys.exit(2)
+    per = E // N
+    part = torch.empty_like(inp.x)
+    layer.forward(with_routing=True)
+    torch.cuda.synchronize()
+    kept = np.diff(layer.routing["expert_offsets"].cpu().numpy().astype(np.int64))
+
+    def share(r):
+        b, e = r * per, (r + 1) * per
+        ops.moe_forward_expert_shard(layer.desc, inp.w_router, inp.w_gate_up[b:e], inp.w_down[b:e], b, e, r == 0,
+                                     inp.x, inp.logit_offset, part, layer.ws, w_shared_gate_up=inp.w_shared_gate_up,
+                                     w_shared_down=inp.w_shared_down)
+
+    ranks = []
+    for r in range(N):
+        for _ in range(args.warmup):
+            share(r)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            share(r)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        loc = kept[r * per:(r + 1) * per]
+        R_r, Et_r = int(loc.sum()), int((loc > 0).sum())
+        fs_r = fs if r == 0 else 0
+        flop = 2.0 * T * d * E + 6.0 * R_r * d * f + 6.0 * T * d * fs_r
+        nbytes = s_bytes * (T * d + E * d + Et_r * 3 * d * f + 3 * d * fs_r + T * d)
+        rt = max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
+        ranks.append({"rank": r, "experts": [r * per, (r + 1) * per], "ms": round(ms, 4), "kept_rows": R_r,
+                      "experts_touched": Et_r, "shared": bool(fs_r), "roofline_ms": round(rt * 1e3, 4),
+                      "frac_of_roofline": round(rt * 1e3 / ms, 4)})
+    slow = max(ranks, key=lambda x: x["ms"])
+    line = {
+        "metric": METRIC,
+        "value": round(T / (slow["ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": slow["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}, one rank's share of {N}-way expert parallelism (slowest rank)",
+                   "num_tokens": T, "d_model": d, "num_experts": E, "top_k": w.top_k, "d_ff": f, "d_ff_shared": fs,
+                   "capacity": cap, "ep_shards": N, "experts_per_rank": per},
+        "ranks": ranks,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(inp, cap, sample, min_seconds=10.0):

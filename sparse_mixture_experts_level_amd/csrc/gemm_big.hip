@@ -59,6 +59,16 @@ __device__ __forceinline__ void find_group(const int32_t *offsets, int G, int m_
   }
 }
 
+// Total row tiles over all groups, sum_g ceil(rows_g / BM), by one wavefront.
+__device__ __forceinline__ int total_m_tiles(const int32_t *offsets, int G) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int g = lane; g < G; g += 64) sum += (offsets[g + 1] - offsets[g] + BG_BM - 1) / BG_BM;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  return sum;
+}
+
 // Pipeline: K advances in steps of 32.  Operand tiles go from HBM straight into LDS
 // (buffer loads with an LDS destination, no registers), into NBUF stages that are
 // separate LDS arrays, NBUF - 1 steps ahead of the MFMAs.  Each step: wait for this
@@ -100,7 +110,12 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t * { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  // The grid is sized from a bound on the rows; blocks past the real tile count leave, and
+  // the real tiles are spread over the XCDs by the remap over their own count (a remap over
+  // the whole grid would crowd them onto the first XCDs when the bound is loose).
+  const int real_blocks = __builtin_amdgcn_readfirstlane(total_m_tiles(offsets, G)) * n_tiles;
+  if ((int)blockIdx.x >= real_blocks) return;
+  const int lin = xcd_remap(blockIdx.x, real_blocks);
   const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles (n tile folded below)
   int g, mt_first, mt_count;
   // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
