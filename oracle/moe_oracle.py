@@ -50,11 +50,13 @@ import numpy as np
 
 __all__ = [
     "capacity",
+    "capacity_topk",
     "router_logits",
     "softmax",
     "topk_select",
     "topk_gates",
     "capacity_fill",
+    "capacity_fill_reroute",
     "silu",
     "swiglu_ffn",
     "combine",
@@ -75,6 +77,18 @@ def capacity(num_tokens: int, num_experts: int, capacity_factor: Optional[float]
     if capacity_factor is None or capacity_factor <= 0:
         return None
     return int(math.ceil(capacity_factor * num_tokens / num_experts))
+
+
+def capacity_topk(num_tokens: int, num_experts: int, top_k: int, capacity_factor: Optional[float]) -> Optional[int]:
+    """Capacity variant with a top-k factor: the same rounded-up quotient with the
+    batch counted in assignments (k per token) instead of tokens,
+    ``ceil(cf * (k * T) / E)`` in double precision ([SMoE], "Expert capacity и
+    capacity factor" gives the formula for a batch of tokens; with k > 1 each token
+    brings k assignments).  ``None`` (or a factor <= 0) means no capacity limit.
+    """
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return int(math.ceil(capacity_factor * (top_k * num_tokens) / num_experts))
 
 
 def router_logits(x, w_router, logit_offset=None) -> np.ndarray:
@@ -131,23 +145,53 @@ def topk_gates(logits, ids) -> np.ndarray:
     return sel / np.sum(sel, axis=1, keepdims=True)
 
 
-def capacity_fill(ids, num_experts: int, cap: Optional[int]) -> dict:
-    """Sequential first-come capacity fill in token order ([SMoE], "Expert
-    capacity и capacity factor": tokens reaching a full expert are not processed;
-    "Подводные камни collapse экспертов и token dropping": tokens late in the
-    batch are dropped more often; the demo walks tokens in batch order and gives
-    each one the next free slot of its expert while slots remain).
+def fill_sequence(num_tokens: int, top_k: int, order: str = "token"):
+    """The assignments (t, j) in the order the capacity fill visits them.
 
-    Readings: for k > 1 the walk is token-major over the [T, k] assignment
-    table (token t before token t+1; within a token, its k distinct experts in
-    rank order); dropping is per (token, expert) assignment.
+    ``"token"``: token-major, token t before token t+1 and, within a token, its
+    experts in rank order ([SMoE], "Подводные камни collapse экспертов и token
+    dropping": buffers fill in batch order, so late tokens are dropped).
+    ``"slot"``: rank-major, every token's first choice before any second choice
+    (a priority variant in which a token's top choice never loses its place to
+    another token's lower-ranked choice).
+    """
+    if order == "token":
+        return [(t, j) for t in range(num_tokens) for j in range(top_k)]
+    if order == "slot":
+        return [(t, j) for j in range(top_k) for t in range(num_tokens)]
+    raise ValueError("order must be 'token' or 'slot'")
+
+
+def _rows_by_expert(ids, slot, num_experts: int, kept) -> tuple:
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_token = np.full(int(offsets[-1]), -1, dtype=np.int32)
+    T, k = slot.shape
+    for t in range(T):
+        for j in range(k):
+            if slot[t, j] >= 0:
+                row_token[offsets[int(ids[t, j])] + slot[t, j]] = t
+    return offsets, row_token
+
+
+def capacity_fill(ids, num_experts: int, cap: Optional[int], order: str = "token") -> dict:
+    """Sequential first-come capacity fill ([SMoE], "Expert capacity и capacity
+    factor": tokens reaching a full expert are not processed; "Подводные камни
+    collapse экспертов и token dropping": tokens late in the batch are dropped more
+    often; the demo walks tokens in batch order and gives each one the next free
+    slot of its expert while slots remain).
+
+    Readings: for k > 1 the walk is token-major over the [T, k] assignment table
+    (``order="token"``, the default; ``"slot"`` is the rank-major variant, see
+    ``fill_sequence``); dropping is per (token, expert) assignment.
 
     Returns a dict with
       counts   [E] int64  demand per expert (all assignments, kept or not)
       kept     [E] int64  kept assignments per expert = min(counts, cap)
       offsets  [E+1] int64 exclusive prefix sum of ``kept``
       slot     [T, k] int32 position inside the expert's buffer, -1 if dropped
-      row_token [R] int32  token of each kept row, rows ordered by (expert, token)
+      row_token [R] int32  token of each kept row, rows ordered by (expert, slot),
+                          i.e. by expert and then in fill order
       drops    int        number of dropped assignments
     """
     ids = np.asarray(ids)
@@ -156,23 +200,16 @@ def capacity_fill(ids, num_experts: int, cap: Optional[int]) -> dict:
     counts = [0] * num_experts
     slot = np.full((T, k), -1, dtype=np.int32)
     drops = 0
-    for t in range(T):
-        for j in range(k):
-            e = int(ids[t, j])
-            counts[e] += 1
-            if cap is None or fill[e] < cap:
-                slot[t, j] = fill[e]
-                fill[e] += 1
-            else:
-                drops += 1
+    for t, j in fill_sequence(T, k, order):
+        e = int(ids[t, j])
+        counts[e] += 1
+        if cap is None or fill[e] < cap:
+            slot[t, j] = fill[e]
+            fill[e] += 1
+        else:
+            drops += 1
     kept = np.array(fill, dtype=np.int64)
-    offsets = np.zeros(num_experts + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(kept)
-    row_token = np.full(int(offsets[-1]), -1, dtype=np.int32)
-    for t in range(T):
-        for j in range(k):
-            if slot[t, j] >= 0:
-                row_token[offsets[int(ids[t, j])] + slot[t, j]] = t
+    offsets, row_token = _rows_by_expert(ids, slot, num_experts, kept)
     return {
         "counts": np.array(counts, dtype=np.int64),
         "kept": kept,
@@ -180,6 +217,69 @@ def capacity_fill(ids, num_experts: int, cap: Optional[int]) -> dict:
         "slot": slot,
         "row_token": row_token,
         "drops": drops,
+    }
+
+
+def capacity_fill_reroute(ids, logits, num_experts: int, cap: Optional[int], order: str = "token") -> dict:
+    """Capacity fill in which an overflowing assignment is redirected to the token's
+    next most suitable expert instead of being dropped outright ([GW], "Как работает
+    MoE: принцип маршрутизации", load-balancing item 4: exceeding an expert's capacity
+    leads to dropping the token or sending it on to the next best expert).
+
+    Readings (the page names the option and nothing more):
+      * Two passes.  The first is the plain fill of ``capacity_fill``; no token's
+        own top-k choice is ever displaced by a redirected one, so the assignments
+        kept by the first pass are exactly those of the drop policy.
+      * The token's i-th overflowing assignment (i = 0, 1, ... in rank order j) is
+        offered to the expert ranked k + i in the token's router order (descending
+        logit, equal logits to the lower index), which the token does not use yet;
+        if k + i >= E there is none and the assignment is dropped.
+      * The second pass visits the offered assignments in the same fill order and
+        gives each the next free slot of its new expert while the expert has room
+        left after the first pass; otherwise it is dropped.  Rows of an expert: its
+        first-pass rows, then its redirected rows.
+      * An assignment keeps its gate (gates are fixed before capacity applies).
+    Returns the ``capacity_fill`` keys (``counts`` stays the router's demand) plus
+      assigned [T, k] int32  expert that serves each assignment (the router's
+                             choice unless redirected)
+      rerouted int           number of assignments kept by the second pass
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    first = capacity_fill(ids, num_experts, cap, order)
+    assigned = ids.astype(np.int32).copy()
+    slot = first["slot"].copy()
+    if cap is None:
+        return {**first, "assigned": assigned, "rerouted": 0}
+    ranking = np.argsort(-np.asarray(logits, dtype=np.float64), axis=1, kind="stable")
+    offered = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        i = 0
+        for j in range(k):
+            if slot[t, j] < 0:
+                if k + i < num_experts:
+                    offered[t, j] = ranking[t, k + i]
+                i += 1
+    fill = [int(v) for v in first["kept"]]
+    rerouted = 0
+    for t, j in fill_sequence(T, k, order):
+        e = int(offered[t, j])
+        if e >= 0 and fill[e] < cap:
+            slot[t, j] = fill[e]
+            fill[e] += 1
+            assigned[t, j] = e
+            rerouted += 1
+    kept = np.array(fill, dtype=np.int64)
+    offsets, row_token = _rows_by_expert(assigned, slot, num_experts, kept)
+    return {
+        "counts": first["counts"],
+        "kept": kept,
+        "offsets": offsets,
+        "slot": slot,
+        "row_token": row_token,
+        "drops": int((slot < 0).sum()),
+        "assigned": assigned,
+        "rerouted": rerouted,
     }
 
 
@@ -242,7 +342,7 @@ def _expert(w, e) -> np.ndarray:
 
 def moe_forward(x, w_router, w_gate_up, w_down, top_k: int, cap: Optional[int], logit_offset=None,
                 w_shared_gate_up=None, w_shared_down=None, tokens: Optional[Sequence[int]] = None,
-                ids=None) -> dict:
+                ids=None, fill_order: str = "token", overflow: str = "drop") -> dict:
     """The whole layer: route, fill, expert FFNs, combine.
 
     ``w_gate_up`` / ``w_down`` may be any object whose ``[e]`` item converts to
@@ -251,7 +351,9 @@ def moe_forward(x, w_router, w_gate_up, w_down, top_k: int, cap: Optional[int], 
     fill always run over the whole batch, since a token's slot depends on every
     earlier token.  ``ids`` overrides the top-k choice (the gates are still the
     renormalised probabilities of the given experts); it lets a comparison
-    absorb near-tie routing differences.
+    absorb near-tie routing differences.  ``fill_order`` ("token" or "slot") and
+    ``overflow`` ("drop" or "reroute") select the capacity-fill variant
+    (``capacity_fill`` / ``capacity_fill_reroute``).
     """
     x64 = np.asarray(x, dtype=np.float64)
     T, d = x64.shape
@@ -261,7 +363,14 @@ def moe_forward(x, w_router, w_gate_up, w_down, top_k: int, cap: Optional[int], 
         ids = topk_select(logits, top_k)
     ids = np.asarray(ids, dtype=np.int32)
     gates = topk_gates(logits, ids)
-    fill = capacity_fill(ids, E, cap)
+    if overflow == "drop":
+        fill = capacity_fill(ids, E, cap, fill_order)
+        serving = ids
+    elif overflow == "reroute":
+        fill = capacity_fill_reroute(ids, logits, E, cap, fill_order)
+        serving = fill["assigned"]
+    else:
+        raise ValueError("overflow must be 'drop' or 'reroute'")
     slot = fill["slot"]
     toks = list(range(T)) if tokens is None else [int(t) for t in tokens]
 
@@ -270,7 +379,7 @@ def moe_forward(x, w_router, w_gate_up, w_down, top_k: int, cap: Optional[int], 
     for t in toks:
         for j in range(top_k):
             if slot[t, j] >= 0:
-                need.setdefault(int(ids[t, j]), []).append((t, j))
+                need.setdefault(int(serving[t, j]), []).append((t, j))
     rows = {}
     for e in sorted(need):
         X = x64[[t for t, _ in need[e]]]
