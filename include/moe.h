@@ -16,6 +16,9 @@
  *   g_tj     = p_t[S_tj] / sum_j' p_t[S_tj']   renormalised gates
  *   capacity C = ceil(capacity_factor * T / E); assignments are filled first come,
  *   first served in token order; overflow assignments are dropped
+ *   (variants, chosen in moe_desc: a rank-major fill order, and redirection of
+ *   overflow to the token's next ranked expert, [GW] "Как работает MoE: принцип
+ *   маршрутизации", load-balancing item 4)
  *   y_t      = [shared expert(x_t)] + sum_{kept j} g_tj * FFN_{S_tj}(x_t)
  *   FFN_e(x) = W_d[e] (silu(W_g[e] x) * (W_u[e] x))   bias-free SwiGLU
  *
@@ -64,6 +67,19 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 
+/* Order in which the capacity fill visits the assignments (t, j). */
+typedef enum moe_fill_order {
+  MOE_FILL_TOKEN_MAJOR = 0, /* token t before token t+1, then rank j ([SMoE] "Подводные камни ...") */
+  MOE_FILL_RANK_MAJOR = 1   /* every token's rank-0 choice before any rank-1 choice, ... */
+} moe_fill_order;
+
+/* What happens to an assignment that finds its expert full. */
+typedef enum moe_overflow {
+  MOE_OVERFLOW_DROP = 0,   /* dropped ([SMoE] "Expert capacity и capacity factor") */
+  MOE_OVERFLOW_REROUTE = 1 /* offered to the token's next ranked expert ([GW] "Как работает MoE:
+                              принцип маршрутизации", item 4); see moe_dispatch_reroute */
+} moe_overflow;
+
 /* Shape of one MoE layer call. */
 typedef struct moe_desc {
   int32_t num_tokens;  /* T >= 0; T == 0 makes every call a no-op returning MOE_OK */
@@ -74,6 +90,8 @@ typedef struct moe_desc {
   int32_t capacity;    /* C >= 0 rows per expert, or MOE_NO_CAPACITY */
   int32_t d_ff_shared; /* 0: no shared expert; else hidden width of the always-on expert */
   int32_t dtype;       /* moe_dtype */
+  int32_t fill_order;  /* moe_fill_order (0 = token-major) */
+  int32_t overflow;    /* moe_overflow (0 = drop) */
 } moe_desc;
 
 /* Expert weights of one layer (device pointers).  Packed layouts follow the
@@ -97,7 +115,8 @@ typedef struct moe_routing {
   int32_t *expert_counts;  /* [E]   demand per expert, before capacity */
   int32_t *expert_offsets; /* [E+1] exclusive prefix sum of kept rows per expert */
   int32_t *slot;           /* [T, k] slot inside the expert's buffer, -1 = dropped */
-  int32_t *row_token;      /* [R_max] token of each kept row (rows sorted by expert, then token) */
+  int32_t *row_token;      /* [R_max] token of each kept row (rows sorted by expert, then slot) */
+  int32_t *assigned_ids;   /* [T, k] expert serving each assignment: topk_ids unless redirected */
 } moe_routing;
 
 /* ---------------------------------------------------------------- host helpers */
@@ -107,6 +126,11 @@ typedef struct moe_routing {
  * when capacity_factor <= 0 or is not finite; returns 0 for T < 0 or E < 1; values
  * above INT32_MAX are clamped to INT32_MAX.  Host only, no device access. */
 int32_t moe_capacity(int32_t num_tokens, int32_t num_experts, double capacity_factor);
+
+/* Capacity variant with a top-k factor, ceil(capacity_factor * (k * T) / E) in IEEE
+ * double: the batch counted in assignments rather than tokens.  Same special cases
+ * as moe_capacity; k < 1 returns 0.  Host only. */
+int32_t moe_capacity_topk(int32_t num_tokens, int32_t num_experts, int32_t top_k, double capacity_factor);
 
 /* Upper bound R_max on kept rows: min(T*k, E*C), or T*k without capacity.
  * Returns -1 for an invalid descriptor. */
@@ -147,21 +171,53 @@ moe_status moe_router_topk(const moe_desc *desc, const float *logits, int32_t *t
 /* Capacity-limited dispatch ([SMoE] "Expert capacity и capacity factor",
  * "Подводные камни collapse экспертов и token dropping"; [HF-MoE] "Бэкенд для
  * экспертов": tokens sorted by expert id before one grouped GEMM).
- * Walking assignments (t, j) in token order (t outer, j inner), each takes the next
- * free slot of its expert while fewer than C are taken; later ones are dropped.
+ * Walking assignments (t, j) in desc->fill_order (token-major: t outer, j inner;
+ * rank-major: j outer, t inner), each takes the next free slot of its expert while
+ * fewer than C are taken; later ones are dropped.  desc->overflow must be
+ * MOE_OVERFLOW_DROP (MOE_ERR_INVALID otherwise; redirection is moe_dispatch_reroute).
  *   topk_ids       [T, k] int32, each in [0, E) (precondition, not checked on device)
  *   x              [T, d] dtype, or NULL when x_perm is NULL
  *   expert_counts  [E]   int32, written: demand per expert
  *   expert_offsets [E+1] int32, written: offsets[0] = 0, offsets[e+1] - offsets[e] =
  *                  min(counts[e], C)
  *   slot           [T, k] int32, written: slot in the expert's buffer or -1 if dropped
- *   row_token      [R_max] int32, written for rows < offsets[E]: the row's token
+ *   row_token      [R_max] int32, written for rows < offsets[E]: the row's token; the rows
+ *                  of an expert are in slot order (its assignments in fill order)
  *   x_perm         [R_max, d] dtype or NULL: row offsets[e] + slot(t, j) = x[t];
  *                  rows >= offsets[E] are left unspecified
  *   ws             at least moe_workspace_size(desc) bytes */
 moe_status moe_dispatch_permute(const moe_desc *desc, const int32_t *topk_ids, const void *x,
                                 int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot,
                                 int32_t *row_token, void *x_perm, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Capacity-limited dispatch with redirection of overflow ([GW] "Как работает MoE:
+ * принцип маршрутизации", load-balancing item 4: an assignment beyond an expert's
+ * capacity may be sent on to the next most suitable expert instead of dropped).
+ * Two passes, both in desc->fill_order:
+ *   1. the plain fill of moe_dispatch_permute: kept assignments are exactly those
+ *      of the drop policy;
+ *   2. the i-th overflowing assignment of token t (i counted in rank order j) is
+ *      offered to the expert ranked k + i in t's router order (descending logit,
+ *      equal logits to the lower index); offers take the next free slot of that
+ *      expert while it has room left after pass 1, otherwise (or if k + i >= E)
+ *      they are dropped.  Each expert's rows: its pass-1 rows, then its offers.
+ * Gates are not changed: a redirected assignment keeps its gate.  Without capacity
+ * nothing overflows and the result is that of moe_dispatch_permute.
+ *   logits         [T, E] float (the router's, as given to moe_router_topk)
+ *   topk_ids       [T, k] int32 as written by moe_router_topk from those logits
+ *   expert_counts  [E]   int32, written: the router's demand per expert (pass 1)
+ *   expert_offsets [E+1] int32, written: exclusive prefix of the final kept rows
+ *   slot           [T, k] int32, written: slot in the serving expert's buffer, or -1
+ *   assigned_ids   [T, k] int32, written: serving expert (topk_ids[t][j] unless
+ *                  redirected; for a dropped assignment, topk_ids[t][j])
+ *   row_token      [R_max] int32, written for rows < offsets[E]
+ *   ws             at least moe_workspace_size(desc) bytes
+ * Pass assigned_ids as the ids of moe_combine_unpermute.  desc->overflow is not
+ * consulted. */
+moe_status moe_dispatch_reroute(const moe_desc *desc, const float *logits, const int32_t *topk_ids,
+                                int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot,
+                                int32_t *assigned_ids, int32_t *row_token, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
 
 /* Grouped SwiGLU expert FFN over rows sorted by group ([HF-MoE] "Бэкенд для
@@ -208,6 +264,8 @@ moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_
  *   out[t] = shared_out[t] (or 0) + sum_{j: slot[t,j] >= 0} topk_gates[t,j] *
  *            y_perm[expert_offsets[topk_ids[t,j]] + slot[t,j]], summed in float in
  *            order j = 0..k-1, then rounded to dtype.
+ *   topk_ids: the expert serving each assignment -- the router's ids, or the
+ *   assigned_ids of moe_dispatch_reroute when overflow is redirected.
  *   y_perm [R_max, d] dtype; shared_out [T, d] dtype or NULL; out [T, d] dtype */
 moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const int32_t *topk_ids,
                                  const float *topk_gates, const int32_t *slot,
@@ -228,7 +286,8 @@ moe_status moe_router_aux_loss(const moe_desc *desc, const float *logits, const 
                                float *loss, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The whole layer: router linear, top-k, dispatch, routed grouped SwiGLU FFN, the
- * shared expert if desc->d_ff_shared > 0, and combine.
+ * shared expert if desc->d_ff_shared > 0, and combine.  The dispatch follows
+ * desc->fill_order and desc->overflow (moe_dispatch_permute or moe_dispatch_reroute).
  *   x [T, d] dtype, smaller than 2 GiB; logit_offset [E] float or NULL; out [T, d] dtype
  *   routing: NULL, or a struct whose non-NULL fields receive the routing tables
  *   ws: at least moe_workspace_size(desc) bytes */

@@ -82,6 +82,10 @@ moe_status check_desc(const moe_desc *desc) {
   if (D.capacity < 0 && D.capacity != MOE_NO_CAPACITY)
     return fail(MOE_ERR_INVALID, "capacity %d: must be >= 0 or MOE_NO_CAPACITY", D.capacity);
   if (D.d_ff_shared < 0) return fail(MOE_ERR_INVALID, "d_ff_shared %d < 0", D.d_ff_shared);
+  if (D.fill_order != MOE_FILL_TOKEN_MAJOR && D.fill_order != MOE_FILL_RANK_MAJOR)
+    return fail(MOE_ERR_INVALID, "fill_order %d is not a moe_fill_order", D.fill_order);
+  if (D.overflow != MOE_OVERFLOW_DROP && D.overflow != MOE_OVERFLOW_REROUTE)
+    return fail(MOE_ERR_INVALID, "overflow %d is not a moe_overflow", D.overflow);
   if ((int64_t)D.num_tokens * D.top_k > INT32_MAX)
     return fail(MOE_ERR_INVALID, "num_tokens * top_k exceeds INT32_MAX");
   if ((int64_t)D.num_tokens * D.d_model * (int64_t)elem_bytes(D.dtype) >= ((int64_t)1 << 31))
@@ -106,9 +110,11 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, ids, gates, counts, offsets, slot, row_token, hist, hidden, y_perm, sh_hidden, sh_out,
-      sh_offsets, total;
+  size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, hidden, y_perm, sh_hidden,
+      sh_out, sh_offsets, total;
 };
+
+bool rerouting(const moe_desc &D) { return D.overflow == MOE_OVERFLOW_REROUTE && D.capacity != MOE_NO_CAPACITY; }
 
 Layout layout(const moe_desc &D) {
   Layout L{};
@@ -127,7 +133,11 @@ Layout layout(const moe_desc &D) {
   L.offsets = take((E + 1) * 4);
   L.slot = take(T * k * 4);
   L.row_token = take(R * 4);
-  L.hist = take(std::max(moe::dispatch_workspace_bytes((int)T, (int)E), moe::aux_loss_workspace_bytes((int)T, (int)E)));
+  // redirection of overflow: the experts ranked k .. 2k-1 per token, the serving experts
+  L.spare = take(D.overflow == MOE_OVERFLOW_REROUTE ? T * k * 4 : 0);
+  L.assigned = take(D.overflow == MOE_OVERFLOW_REROUTE ? T * k * 4 : 0);
+  L.hist = take(std::max(moe::dispatch_workspace_bytes((int)T, (int)k, (int)E, D.overflow == MOE_OVERFLOW_REROUTE),
+                         moe::aux_loss_workspace_bytes((int)T, (int)E)));
   L.hidden = take(R * f * s);
   L.y_perm = take(R * d * s);
   L.sh_hidden = take(fs ? T * fs * s : 0);
@@ -195,6 +205,14 @@ int32_t moe_capacity(int32_t num_tokens, int32_t num_experts, double capacity_fa
   if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return MOE_NO_CAPACITY;
   if (num_tokens < 0 || num_experts < 1) return 0;
   const double c = std::ceil(capacity_factor * (double)num_tokens / (double)num_experts);
+  if (c >= (double)INT32_MAX) return INT32_MAX;
+  return (int32_t)c;
+}
+
+int32_t moe_capacity_topk(int32_t num_tokens, int32_t num_experts, int32_t top_k, double capacity_factor) {
+  if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return MOE_NO_CAPACITY;
+  if (num_tokens < 0 || num_experts < 1 || top_k < 1) return 0;
+  const double c = std::ceil(capacity_factor * ((double)top_k * (double)num_tokens) / (double)num_experts);
   if (c >= (double)INT32_MAX) return INT32_MAX;
   return (int32_t)c;
 }
@@ -273,17 +291,58 @@ moe_status moe_dispatch_permute(const moe_desc *desc, const int32_t *topk_ids, c
   MOE_TRY(check_ptr(row_token, "row_token"));
   MOE_TRY(check_opt_ptr(x_perm, "x_perm"));
   if (x_perm) MOE_TRY(check_ptr(x, "x"));
-  const size_t need = moe::dispatch_workspace_bytes(D.num_tokens, D.num_experts);
+  if (D.overflow != MOE_OVERFLOW_DROP)
+    return fail(MOE_ERR_INVALID, "moe_dispatch_permute drops overflow; redirection is moe_dispatch_reroute");
+  const size_t need = moe::dispatch_workspace_bytes(D.num_tokens, D.top_k, D.num_experts, false);
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
   MOE_TRY(check_ptr(ws, "ws"));
-  MOE_TRY_HIP(moe::launch_dispatch(topk_ids, D.num_tokens, D.top_k, D.num_experts, D.capacity, expert_counts,
-                                   expert_offsets, slot, row_token, static_cast<int32_t *>(ws), stream),
+  MOE_TRY_HIP(moe::launch_dispatch(topk_ids, D.num_tokens, D.top_k, D.num_experts, D.capacity,
+                                   D.fill_order == MOE_FILL_RANK_MAJOR, expert_counts, expert_offsets, slot, row_token,
+                                   static_cast<int32_t *>(ws), stream),
               "dispatch");
   if (x_perm)
     MOE_TRY_HIP(moe::launch_gather_rows(x, row_token, expert_offsets + D.num_experts, max_rows(D), D.d_model,
                                         (int)elem_bytes(D.dtype), x_perm, stream),
                 "gather rows");
+  return ok();
+}
+
+moe_status moe_dispatch_reroute(const moe_desc *desc, const float *logits, const int32_t *topk_ids,
+                                int32_t *expert_counts, int32_t *expert_offsets, int32_t *slot, int32_t *assigned_ids,
+                                int32_t *row_token, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+  MOE_TRY(check_ptr(expert_counts, "expert_counts"));
+  if (D.num_tokens == 0) return ok();
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(assigned_ids, "assigned_ids"));
+  MOE_TRY(check_ptr(row_token, "row_token"));
+  const int T = D.num_tokens, k = D.top_k, E = D.num_experts;
+  const size_t spare_bytes = align_up((size_t)T * k * 4);
+  const size_t need = spare_bytes + moe::dispatch_workspace_bytes(T, k, E, true);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "dispatch with redirection needs %zu workspace bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+  const bool rank_major = D.fill_order == MOE_FILL_RANK_MAJOR;
+  if (D.capacity == MOE_NO_CAPACITY) {  // nothing overflows
+    MOE_TRY_HIP(moe::launch_dispatch(topk_ids, T, k, E, D.capacity, rank_major, expert_counts, expert_offsets, slot,
+                                     row_token, static_cast<int32_t *>(ws), stream),
+                "dispatch");
+    MOE_TRY_HIP(hipMemcpyAsync(assigned_ids, topk_ids, (size_t)T * k * 4, hipMemcpyDeviceToDevice, stream),
+                "assigned ids");
+    return ok();
+  }
+  int32_t *spare = static_cast<int32_t *>(ws);
+  MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, nullptr, nullptr, stream, spare), "next-ranked experts");
+  MOE_TRY_HIP(moe::launch_dispatch_reroute(topk_ids, spare, T, k, E, D.capacity, rank_major, expert_counts,
+                                           expert_offsets, slot, assigned_ids, row_token,
+                                           at<int32_t>(ws, spare_bytes), stream),
+              "dispatch with redirection");
   return ok();
 }
 
@@ -419,6 +478,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
     MOE_TRY(check_opt_ptr(R.expert_offsets, "routing.expert_offsets"));
     MOE_TRY(check_opt_ptr(R.slot, "routing.slot"));
     MOE_TRY(check_opt_ptr(R.row_token, "routing.row_token"));
+    MOE_TRY(check_opt_ptr(R.assigned_ids, "routing.assigned_ids"));
   }
   const Layout L = layout(D);
   if (!ws || ws_bytes < L.total)
@@ -445,10 +505,25 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
                                               static_cast<const float *>(weights->w_router), logit_offset, logits, T,
                                               d, E, stream),
                 "router logits");
-  MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream), "router top-k");
-  MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, counts, offsets, slot, row_token, at<int32_t>(ws, L.hist),
-                                   stream),
-              "dispatch");
+  const bool rank_major = D.fill_order == MOE_FILL_RANK_MAJOR;
+  const int32_t *serving = ids;  // expert of each assignment, as the combine reads it
+  if (rerouting(D)) {
+    int32_t *spare = at<int32_t>(ws, L.spare);
+    int32_t *assigned = R.assigned_ids ? R.assigned_ids : at<int32_t>(ws, L.assigned);
+    MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream, spare), "router top-k");
+    MOE_TRY_HIP(moe::launch_dispatch_reroute(ids, spare, T, k, E, D.capacity, rank_major, counts, offsets, slot,
+                                             assigned, row_token, at<int32_t>(ws, L.hist), stream),
+                "dispatch with redirection");
+    serving = assigned;
+  } else {
+    MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream), "router top-k");
+    MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, rank_major, counts, offsets, slot, row_token,
+                                     at<int32_t>(ws, L.hist), stream),
+                "dispatch");
+    if (R.assigned_ids)
+      MOE_TRY_HIP(hipMemcpyAsync(R.assigned_ids, ids, (size_t)T * k * 4, hipMemcpyDeviceToDevice, stream),
+                  "assigned ids");
+  }
   if (rmax > 0 && any_local) {
     // the gate_up projection gathers each expert's token rows from x through row_token,
     // so the permuted copy of x is never materialised; a range of experts is the slice
@@ -465,7 +540,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
                             at<void>(ws, L.sh_out), at<void>(ws, L.sh_hidden), stream));
     shared = at<void>(ws, L.sh_out);
   }
-  MOE_TRY_HIP(moe::launch_combine(y_perm, ids, gates, slot, offsets, shared, out, T, d, k, bf, stream, e_begin,
+  MOE_TRY_HIP(moe::launch_combine(y_perm, serving, gates, slot, offsets, shared, out, T, d, k, bf, stream, e_begin,
                                   any_local ? e_end : e_begin),
               "combine");
   return ok();

@@ -14,17 +14,31 @@ hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const 
                                      int T, int d, int E, hipStream_t s);
 hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits,
                                     int T, int d, int E, hipStream_t s);
-hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s);
+// ids / gates may be NULL (not written).  With `spare`, also writes the experts ranked
+// k .. 2k-1 per token into spare [T, k] (-1 where the rank is >= E).
+hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s,
+                              int32_t *spare = nullptr);
 
 // ---- dispatch (dispatch.hip)
+// Assignments are walked in fill order: token-major (position p = t * k + j) or, with
+// rank_major, rank-major (p = j * T + t).  Blocks own contiguous position ranges.
 struct DispatchPlan {
-  int tokens_per_block;
+  int64_t per_block;  // positions per block, a multiple of 256
   int num_blocks;
 };
-DispatchPlan dispatch_plan(int T);
-size_t dispatch_workspace_bytes(int T, int E);
-hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int cap /* <0: none */, int32_t *counts,
-                           int32_t *offsets, int32_t *slot, int32_t *row_token, int32_t *hist_ws, hipStream_t s);
+DispatchPlan dispatch_plan(int T, int k);
+// Workspace of launch_dispatch, or of launch_dispatch_reroute when reroute is set.
+size_t dispatch_workspace_bytes(int T, int k, int E, bool reroute);
+hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int cap /* <0: none */, bool rank_major,
+                           int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *row_token, int32_t *ws,
+                           hipStream_t s);
+// Two-pass fill: the plain fill, then every overflowing assignment is offered to the
+// token's next ranked expert (spare [T, k] from launch_router_topk: the i-th overflow of
+// a token takes spare[t][i]) and kept if that expert has room left; assigned [T, k]
+// receives the serving expert of each assignment.  cap >= 0.
+hipError_t launch_dispatch_reroute(const int32_t *ids, const int32_t *spare, int T, int k, int E, int cap,
+                                   bool rank_major, int32_t *counts, int32_t *offsets, int32_t *slot,
+                                   int32_t *assigned, int32_t *row_token, int32_t *ws, hipStream_t s);
 hipError_t launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *offsets_end, int64_t rows_max,
                               int d, int elem_bytes, void *x_perm, hipStream_t s);
 

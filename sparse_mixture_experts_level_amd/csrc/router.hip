@@ -161,10 +161,13 @@ constexpr int TK_WAVES = 4;
 
 // Every lane follows the k rounds identically (same winner, same running sum of
 // exp(l_j - l_max) in the same order); lane (j mod 64) keeps winner j in register
-// slot j / 64 and writes it at the end.  No LDS and no barriers.
+// slot j / 64 and writes it at the end.  No LDS and no barriers.  With `spare`, the
+// selection goes on for k more rounds (the experts ranked k .. 2k-1, used to redirect
+// overflowing assignments) without gates.
 template <int VPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
-                                                          int32_t *__restrict__ ids, float *__restrict__ gates) {
+                                                          int32_t *__restrict__ ids, float *__restrict__ gates,
+                                                          int32_t *__restrict__ spare) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * TK_WAVES + wave;
   if (t >= T) return;
@@ -175,42 +178,54 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
     const int e = lane + 64 * v;
     key[v] = e < E ? topk_key(row[e], e) : 0ull;  // 0 ranks below every real key
   }
-  int my_id[VPL];
+  int my_id[VPL], my_sp[VPL];
   float my_z[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     my_id[v] = 0;
+    my_sp[v] = -1;
     my_z[v] = 0.f;
   }
   float m = 0.f, sum = 0.f;
-  for (int j = 0; j < k; ++j) {
+  const int rounds = spare ? min(2 * k, E) : k;
+  for (int j = 0; j < rounds; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
     best = wave_max_u64(best);
     const int e = 0xffff - int(best & 0xffffu);
-    const float val = key_value(best);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if (key[v] == best) key[v] = 0ull;
-    if (j == 0) m = val;
-    const float z = expf(val - m);
-    sum += z;
-    if ((j & 63) == lane) {
+    if (j < k) {
+      const float val = key_value(best);
+      if (j == 0) m = val;
+      const float z = expf(val - m);
+      sum += z;
+      if ((j & 63) == lane) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (v == (j >> 6)) {
-          my_id[v] = e;
-          my_z[v] = z;
-        }
+        for (int v = 0; v < VPL; ++v)
+          if (v == (j >> 6)) {
+            my_id[v] = e;
+            my_z[v] = z;
+          }
+      }
+    } else {
+      const int i = j - k;
+      if ((i & 63) == lane) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (v == (i >> 6)) my_sp[v] = e;
+      }
     }
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int j = v * 64 + lane;
     if (j < k) {
-      ids[(size_t)t * k + j] = my_id[v];
-      gates[(size_t)t * k + j] = my_z[v] / sum;
+      if (ids) ids[(size_t)t * k + j] = my_id[v];
+      if (gates) gates[(size_t)t * k + j] = my_z[v] / sum;
+      if (spare) spare[(size_t)t * k + j] = my_sp[v];
     }
   }
 }
@@ -252,12 +267,13 @@ hipError_t launch_router_logits_f32(const float *x, const float *w_router, const
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s) {
+hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s,
+                              int32_t *spare) {
   const int grid = (T + TK_WAVES - 1) / TK_WAVES;
   const int vpl = (E + 63) / 64;
 #define TK_CASE(V)                                                                                          \
   case V:                                                                                                   \
-    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates); \
+    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates, spare); \
     break;
   switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
     TK_CASE(1)

@@ -22,11 +22,13 @@ MOE_NO_CAPACITY = -1
 MOE_MAX_EXPERTS = 1024
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_FILL_TOKEN_MAJOR, MOE_FILL_RANK_MAJOR = 0, 1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_REROUTE = 0, 1
 
 SYMBOLS = [
-    "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_grouped_gemm_workspace_size",
+    "moe_capacity", "moe_capacity_topk", "moe_max_rows", "moe_workspace_size", "moe_grouped_gemm_workspace_size",
     "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
-    "moe_dispatch_permute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
+    "moe_dispatch_permute", "moe_dispatch_reroute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
     "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
 ]
 
@@ -40,7 +42,8 @@ class MoEError(RuntimeError):
 class MoeDesc(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("d_ff_shared", ctypes.c_int32), ("dtype", ctypes.c_int32), ("fill_order", ctypes.c_int32),
+                ("overflow", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -51,7 +54,7 @@ class MoeWeights(ctypes.Structure):
 class MoeRouting(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_gates", ctypes.c_void_p),
                 ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p), ("slot", ctypes.c_void_p),
-                ("row_token", ctypes.c_void_p)]
+                ("row_token", ctypes.c_void_p), ("assigned_ids", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +71,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     dp = ctypes.POINTER(MoeDesc)
     L.moe_capacity.argtypes, L.moe_capacity.restype = [i32, i32, ctypes.c_double], i32
+    L.moe_capacity_topk.argtypes, L.moe_capacity_topk.restype = [i32, i32, i32, ctypes.c_double], i32
     L.moe_max_rows.argtypes, L.moe_max_rows.restype = [dp], i64
     L.moe_workspace_size.argtypes, L.moe_workspace_size.restype = [dp], sz
     L.moe_grouped_gemm_workspace_size.argtypes, L.moe_grouped_gemm_workspace_size.restype = [i32, i64, i32, i32], sz
@@ -77,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.moe_router_topk.argtypes, L.moe_router_topk.restype = [dp, vp, vp, vp, vp], st
     L.moe_dispatch_permute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch_permute.restype = st
+    L.moe_dispatch_reroute.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_reroute.restype = st
     L.moe_grouped_swiglu_gemm.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_grouped_swiglu_gemm.restype = st
     L.moe_grouped_gate_up_swiglu.argtypes = [i32, i64, i32, i32, i32, i32, vp, vp, i64, vp, vp, vp, vp]
@@ -124,16 +130,30 @@ def dtype_code(dt: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {dt}")
 
 
-def make_desc(num_tokens, d_model, d_ff, num_experts, top_k, capacity, d_ff_shared=0, dtype=torch.bfloat16) -> MoeDesc:
+_FILL = {"token": MOE_FILL_TOKEN_MAJOR, "rank": MOE_FILL_RANK_MAJOR, "slot": MOE_FILL_RANK_MAJOR}
+_OVERFLOW = {"drop": MOE_OVERFLOW_DROP, "reroute": MOE_OVERFLOW_REROUTE}
+
+
+def make_desc(num_tokens, d_model, d_ff, num_experts, top_k, capacity, d_ff_shared=0, dtype=torch.bfloat16,
+              fill_order="token", overflow="drop") -> MoeDesc:
+    fo = _FILL[fill_order] if isinstance(fill_order, str) else int(fill_order)
+    ov = _OVERFLOW[overflow] if isinstance(overflow, str) else int(overflow)
     return MoeDesc(int(num_tokens), int(d_model), int(d_ff), int(num_experts), int(top_k),
                    MOE_NO_CAPACITY if capacity is None else int(capacity), int(d_ff_shared),
-                   dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype))
+                   dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), fo, ov)
 
 
 # ------------------------------------------------------------------------ host helpers
 
 def moe_capacity(num_tokens: int, num_experts: int, capacity_factor: Optional[float]) -> Optional[int]:
     c = lib().moe_capacity(int(num_tokens), int(num_experts), 0.0 if capacity_factor is None else float(capacity_factor))
+    return None if c == MOE_NO_CAPACITY else int(c)
+
+
+def moe_capacity_topk(num_tokens: int, num_experts: int, top_k: int,
+                      capacity_factor: Optional[float]) -> Optional[int]:
+    c = lib().moe_capacity_topk(int(num_tokens), int(num_experts), int(top_k),
+                                0.0 if capacity_factor is None else float(capacity_factor))
     return None if c == MOE_NO_CAPACITY else int(c)
 
 
@@ -172,6 +192,15 @@ def moe_dispatch_permute(desc, topk_ids, x, expert_counts, expert_offsets, slot,
                                       _ptr(expert_offsets), _ptr(slot), _ptr(row_token), _ptr(x_perm), _ptr(ws),
                                       0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "moe_dispatch_permute")
+
+
+def moe_dispatch_reroute(desc, logits, topk_ids, expert_counts, expert_offsets, slot, assigned_ids, row_token, ws,
+                         stream=None) -> None:
+    _check(lib().moe_dispatch_reroute(ctypes.byref(desc), _ptr(logits), _ptr(topk_ids), _ptr(expert_counts),
+                                      _ptr(expert_offsets), _ptr(slot), _ptr(assigned_ids), _ptr(row_token),
+                                      _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                      _stream(stream)),
+           "moe_dispatch_reroute")
 
 
 def moe_grouped_swiglu_gemm(num_groups, rows_max, group_rows_max, d_model, d_ff, dtype, x_rows, group_offsets,
@@ -245,11 +274,11 @@ class MoELayer:
 
     Convenience only: allocation happens here, once, never inside a forward call."""
 
-    def __init__(self, inputs, capacity, device="cuda"):
+    def __init__(self, inputs, capacity, device="cuda", fill_order="token", overflow="drop"):
         w = inputs.workload
         self.inputs = inputs
         self.desc = make_desc(w.num_tokens, w.d_model, w.d_ff, w.num_experts, w.top_k, capacity,
-                              w.d_ff_shared, w.torch_dtype)
+                              w.d_ff_shared, w.torch_dtype, fill_order=fill_order, overflow=overflow)
         self.ws = workspace(moe_workspace_size(self.desc), device)
         self.out = torch.empty_like(inputs.x)
         T, E, k = w.num_tokens, w.num_experts, w.top_k
@@ -263,6 +292,7 @@ class MoELayer:
             "expert_offsets": torch.empty((E + 1,), **i32),
             "slot": torch.empty((T, k), **i32),
             "row_token": torch.empty((max(R, 1),), **i32),
+            "assigned_ids": torch.empty((T, k), **i32),
         }
 
     def forward(self, with_routing=True, stream=None):

@@ -96,8 +96,15 @@ def check_ids_against_oracle(gpu_ids: np.ndarray, ref_logits: np.ndarray, k: int
     return differ
 
 
-def check_dispatch_exact(ids: np.ndarray, E: int, cap, counts, offsets, slot, row_token) -> dict:
-    ref = oracle.capacity_fill(ids, E, cap)
+def check_dispatch_exact(ids: np.ndarray, E: int, cap, counts, offsets, slot, row_token, order="token",
+                         logits=None, assigned=None) -> dict:
+    """Bit-exact comparison with the oracle's fill; with `logits`, the two-pass fill that
+    redirects overflow (and `assigned`, the serving experts, is compared too)."""
+    if logits is None:
+        ref = oracle.capacity_fill(ids, E, cap, order)
+    else:
+        ref = oracle.capacity_fill_reroute(ids, logits, E, cap, order)
+        assert np.array_equal(np.asarray(assigned), ref["assigned"]), "assigned_ids"
     assert np.array_equal(np.asarray(counts), ref["counts"]), "expert_counts"
     assert np.array_equal(np.asarray(offsets), ref["offsets"]), "expert_offsets"
     assert np.array_equal(np.asarray(slot), ref["slot"]), "slot"

@@ -78,6 +78,8 @@ def test_max_rows_and_workspace():
     (dict(dtype=7), ops.MOE_ERR_UNSUPPORTED),
     (dict(dtype=ops.MOE_DTYPE_BF16, d_model=96), ops.MOE_ERR_UNSUPPORTED),
     (dict(dtype=ops.MOE_DTYPE_BF16, d_ff_shared=32), ops.MOE_ERR_UNSUPPORTED),
+    (dict(fill_order=2), ops.MOE_ERR_INVALID),
+    (dict(overflow=-1), ops.MOE_ERR_INVALID),
 ])
 def test_bad_descriptor_is_rejected(bad, status):
     d = _desc(**bad)
@@ -134,3 +136,23 @@ def test_status_strings():
     for s in range(5):
         assert L.moe_status_string(s).startswith(b"MOE_")
     assert math.isfinite(1.0)
+
+
+def test_capacity_topk_matches_the_oracle():
+    for T, E, k, cf in [(8, 4, 2, 1.0), (32, 8, 2, 1.25), (16384, 256, 8, 1.25), (5, 3, 2, 1.0), (8192, 64, 1, 1.25),
+                        (4096, 8, 2, 0.3), (16, 32, 4, 1.0)]:
+        assert ops.moe_capacity_topk(T, E, k, cf) == oracle.capacity_topk(T, E, k, cf)
+    assert ops.moe_capacity_topk(100, 8, 2, None) is None
+    assert L.moe_capacity_topk(100, 8, 0, 1.0) == 0
+
+
+def test_dispatch_variants_are_checked():
+    d = _desc(overflow=ops.MOE_OVERFLOW_REROUTE)
+    st = L.moe_dispatch_permute(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == ops.MOE_ERR_INVALID and b"moe_dispatch_reroute" in L.moe_last_error()
+    st = L.moe_dispatch_reroute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert st == ops.MOE_ERR_INVALID and b"assigned_ids" in L.moe_last_error()
+    st = L.moe_dispatch_reroute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None)
+    assert st == ops.MOE_ERR_WORKSPACE
+    # the redirection tables enlarge the layer's workspace
+    assert ops.moe_workspace_size(d) > ops.moe_workspace_size(_desc())

@@ -187,3 +187,42 @@ def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards)
     full_ref = oracle.moe_forward(x, wr, gu, dn, k, cap, off, w_shared_gate_up=sgu, w_shared_down=sd)["out"]
     assert row_rel_err(to_np(total), full_ref) <= 2e-2
     assert row_rel_err(to_np(total), to_np(full).astype(np.float64)) <= 2e-2
+
+
+@pytest.mark.parametrize("T,d,E,k,f,cf,order,overflow", [
+    (300, 256, 8, 2, 192, 1.0, "rank", "drop"),
+    (300, 256, 8, 2, 192, 1.0, "token", "reroute"),
+    (513, 128, 16, 4, 128, 2.0, "rank", "reroute"),
+    (513, 128, 16, 4, 128, 0.5, "token", "reroute"),   # every expert full after pass 1
+    (257, 64, 4, 1, 64, 0.75, "token", "reroute"),
+])
+def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
+    """moe_forward with the rank-major fill and/or redirection of overflow vs the oracle."""
+    w = wl.Workload("variant", T, d, E, k, f, cf, "bf16", offset="boost4")
+    say(f"forward variant T={T} E={E} k={k} cf={cf} order={order} overflow={overflow}")
+    inp = wl.make_inputs(w, seed=3, device=DEV)
+    cap = ops.moe_capacity(T, E, cf)
+    layer = ops.MoELayer(inp, cap, fill_order=order, overflow=overflow)
+    layer.forward()
+    torch.cuda.synchronize()
+    r = {key: to_np(v) for key, v in layer.routing.items()}
+    x = to_np(inp.x).astype(np.float64)
+    wr = to_np(inp.w_router).astype(np.float64)
+    off = to_np(inp.logit_offset)
+    ref_logits = oracle.router_logits(x, wr, off)
+    gpu_ids = r["topk_ids"].astype(np.int64)
+    check_ids_against_oracle(gpu_ids, ref_logits, k)
+    o = "slot" if order == "rank" else "token"
+    own = r["logits"].astype(np.float64)
+    check_dispatch_exact(gpu_ids, E, cap, r["expert_counts"], r["expert_offsets"], r["slot"], r["row_token"],
+                         order=o, logits=own if overflow == "reroute" else None, assigned=r["assigned_ids"])
+    if overflow == "drop":
+        assert np.array_equal(r["assigned_ids"], gpu_ids)
+    ref = oracle.moe_forward(x, wr, HostExperts(inp.w_gate_up), HostExperts(inp.w_down), k, cap, off, ids=gpu_ids,
+                             fill_order=o, overflow=overflow)
+    if overflow == "reroute":
+        assert np.array_equal(ref["assigned"], r["assigned_ids"])
+        room_after_pass1 = cap - np.minimum(np.bincount(gpu_ids.reshape(-1), minlength=E), cap)
+        if room_after_pass1.sum() > 0 and ref["drops"] > 0:
+            assert ref["rerouted"] > 0
+    assert row_rel_err(to_np(layer.out), ref["out"]) <= 2e-2

@@ -18,8 +18,8 @@ ops = pytest.importorskip("sparse_mixture_experts_level_amd.ops")
 DEV = "cuda"
 
 
-def _desc(T, E, k, cap=None, d=64, f=64, fs=0, dtype=torch.float32):
-    return ops.make_desc(T, d, f, E, k, cap, fs, dtype)
+def _desc(T, E, k, cap=None, d=64, f=64, fs=0, dtype=torch.float32, fill_order="token", overflow="drop"):
+    return ops.make_desc(T, d, f, E, k, cap, fs, dtype, fill_order=fill_order, overflow=overflow)
 
 
 # ------------------------------------------------------------------------------------- top-k
@@ -94,6 +94,57 @@ def _ids(rng, T, E, k, skew=0.0):
 def test_dispatch_bitexact(T, E, k, cap, skew):
     rng = np.random.default_rng(T + E + k)
     _dispatch_case(_ids(rng, T, E, k, skew), E, cap)
+
+
+def _variant_case(logits_np, k, cap, order, reroute, tag=""):
+    """Rank-major fill and/or redirection of overflow on the GPU vs the oracle, bit-exact.  The
+    ids come from the GPU's top-k of float32 logits, and the oracle takes the same float32
+    logits, so the routing is identical and every integer output must match."""
+    T, E = logits_np.shape
+    say(f"dispatch variant {tag} T={T} E={E} k={k} cap={cap} order={order} reroute={reroute}")
+    desc = _desc(T, E, k, cap, fill_order=order, overflow="reroute" if reroute else "drop")
+    R = ops.moe_max_rows(desc)
+    lg32 = logits_np.astype(np.float32)
+    lg = torch.from_numpy(lg32).to(DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    ops.moe_router_topk(desc, lg, ids, gates)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    assigned = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    row_token = torch.full((max(R, 1),), -7, dtype=torch.int32, device=DEV)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    if reroute:
+        ops.moe_dispatch_reroute(desc, lg, ids, counts, offsets, slot, assigned, row_token, ws)
+    else:
+        ops.moe_dispatch_permute(desc, ids, None, counts, offsets, slot, row_token, None, ws)
+    torch.cuda.synchronize()
+    ids_np = to_np(ids)
+    assert np.array_equal(ids_np, oracle.topk_select(lg32.astype(np.float64), k))
+    order_o = "slot" if order == "rank" else "token"
+    return check_dispatch_exact(ids_np, E, cap, to_np(counts), to_np(offsets), to_np(slot), to_np(row_token),
+                                order=order_o, logits=lg32.astype(np.float64) if reroute else None,
+                                assigned=to_np(assigned) if reroute else None)
+
+
+@pytest.mark.parametrize("T,E,k,cap,skew,reroutes", [
+    (300, 8, 2, 10, 0.0, False), (5000, 64, 1, 78, 2.0, True), (3000, 256, 8, 40, 1.5, True),
+    (777, 1024, 3, 2, 0.5, True), (64, 8, 2, 0, 0.0, False), (1, 4, 4, 1, 0.0, False), (4100, 32, 4, 600, 1.0, True),
+    (1000, 6, 3, 700, 0.0, False),
+])
+@pytest.mark.parametrize("order,reroute", [("rank", False), ("token", True), ("rank", True)])
+def test_dispatch_variants_bitexact(T, E, k, cap, skew, reroutes, order, reroute):
+    rng = np.random.default_rng(T + 3 * E + k)
+    logits = rng.normal(size=(T, E)) - skew * np.log(np.arange(1, E + 1))[None, :]
+    ref = _variant_case(logits, k, cap, order, reroute)
+    if reroute and reroutes:  # cases chosen so that hot experts overflow while cold ones keep room
+        assert ref["rerouted"] > 0
+
+
+def test_dispatch_reroute_without_capacity_is_the_plain_dispatch():
+    rng = np.random.default_rng(9)
+    _variant_case(rng.normal(size=(400, 16)), 4, None, "token", True)
 
 
 def test_dispatch_float_rows_and_everyone_on_one_expert():
