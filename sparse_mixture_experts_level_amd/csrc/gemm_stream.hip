@@ -47,6 +47,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
     u32x4 a[NA];
   };
   Chunk slot[P];
+  // loads of chunk c into a slot; chunks past the end of K get out-of-range offsets
   auto issue = [&](Chunk &ch, int c) {
     // an invalid base is kOob, and kOob + kc stays out of range (kc < 2^31)
     const bool ok = c < nk;
@@ -57,6 +58,16 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int b = 0; b < NB; ++b) ch.b[s][b] = buf_ld16(wres, ok ? boff[b] + kc + s * 64u : kOob);
+  };
+  // the same for a chunk known to be inside K: straight-line code, no selects
+  auto issue_in = [&](Chunk &ch, int c) {
+    const uint32_t kc = (uint32_t)c * (SG_KC * 2);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ch.a[i] = buf_ld16(ares, aoff[i] + kc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ch.b[s][b] = buf_ld16(wres, boff[b] + kc + s * 64u);
   };
   auto stage_a = [&](const Chunk &ch, int buf) {
 #pragma unroll
@@ -95,16 +106,30 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
   for (int s = 0; s < P - 1; ++s) issue(slot[s], s);
   stage_a(slot[0], 0);
   __syncthreads();
-  for (int c0 = 0; c0 < nk; c0 += P) {
+  // Main loop, P chunks per trip, while every chunk it issues lies inside K: no
+  // conditions, so slots, LDS buffers (chunk parity = s & 1, P even) and wait counts are
+  // all static.  Step c issues chunk c + P - 1 into the slot chunk c - 1 has finished
+  // with, computes chunk c, and stages the A rows of chunk c + 1.
+  static_assert(P % 2 == 0, "the LDS buffer of a chunk is its parity");
+  int c0 = 0;
+  for (; c0 + 2 * P - 2 < nk; c0 += P) {
 #pragma unroll
     for (int s = 0; s < P; ++s) {
-      const int c = c0 + s;
-      if (c >= nk) break;
-      issue(slot[(s + P - 1) % P], c + P - 1);  // reuses the slot chunk c-1 has finished with
-      compute(slot[s], c & 1);
-      if (c + 1 < nk) stage_a(slot[(s + 1) % P], (c + 1) & 1);
+      issue_in(slot[(s + P - 1) % P], c0 + s + P - 1);
+      compute(slot[s], s & 1);
+      stage_a(slot[(s + 1) % P], (s + 1) & 1);
       __syncthreads();
     }
+  }
+  // the last (fewer than 2P - 1) chunks
+#pragma unroll
+  for (int s = 0; s < 2 * P - 1; ++s) {
+    const int c = c0 + s;
+    if (c >= nk) break;
+    if (c + P - 1 < nk) issue_in(slot[(s + P - 1) % P], c + P - 1);
+    compute(slot[s % P], s & 1);
+    if (c + 1 < nk) stage_a(slot[(s + 1) % P], (s + 1) & 1);
+    __syncthreads();
   }
 
   // epilogue: C layout of the 16x16 MFMA -- column (lane & 15), rows 4*(lane>>4)+j
