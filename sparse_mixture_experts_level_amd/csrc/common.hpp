@@ -70,6 +70,52 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Groups cut into blocks of BM rows: group g holds ceil(rows_g / BM) blocks, rows_g =
+// offsets[g+1] - offsets[g], numbered group after group.  One wavefront scans the
+// offsets; the results are equal in every lane.
+// Block index m_lin -> its group (-1 past the last block), the group's first block and
+// its block count.
+template <int BM>
+__device__ __forceinline__ void find_row_block(const int32_t *offsets, int G, int m_lin, int &g_out, int &first,
+                                               int &count) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  g_out = -1;
+  first = 0;
+  count = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int mt = 0;
+    if (g < G) mt = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+    int incl = mt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const uint64_t hit = __ballot(g < G && base + incl > m_lin);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      g_out = g0 + l;
+      first = base + __shfl(incl - mt, l, 64);
+      count = __shfl(mt, l, 64);
+      return;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+}
+
+// Total row blocks over all groups, sum_g ceil(rows_g / BM).
+template <int BM>
+__device__ __forceinline__ int total_row_blocks(const int32_t *offsets, int G) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int g = lane; g < G; g += 64) sum += (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  return sum;
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace moe

@@ -26,49 +26,6 @@ namespace {
 
 constexpr int BG_BM = 256, BG_BN = 256;
 
-// Exclusive prefix of ceil(rows_g / BM) over groups, evaluated by one wavefront; returns
-// for tile index `m_lin` its group (or -1 past the end), the group's first m tile and
-// the number of its m tiles.
-__device__ __forceinline__ void find_group(const int32_t *offsets, int G, int m_lin, int &g_out, int &mt_first,
-                                           int &mt_count) {
-  const int lane = threadIdx.x & 63;
-  int base = 0;
-  g_out = -1;
-  mt_first = 0;
-  mt_count = 0;
-  for (int g0 = 0; g0 < G; g0 += 64) {
-    const int g = g0 + lane;
-    int mt = 0;
-    if (g < G) mt = (offsets[g + 1] - offsets[g] + BG_BM - 1) / BG_BM;
-    int incl = mt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    const uint64_t hit = __ballot(g < G && base + incl > m_lin);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      g_out = g0 + l;
-      const int excl = __shfl(incl - mt, l, 64);
-      mt_first = base + excl;
-      mt_count = __shfl(mt, l, 64);
-      return;
-    }
-    base += __shfl(incl, 63, 64);
-  }
-}
-
-// Total row tiles over all groups, sum_g ceil(rows_g / BM), by one wavefront.
-__device__ __forceinline__ int total_m_tiles(const int32_t *offsets, int G) {
-  const int lane = threadIdx.x & 63;
-  int sum = 0;
-  for (int g = lane; g < G; g += 64) sum += (offsets[g + 1] - offsets[g] + BG_BM - 1) / BG_BM;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-  return sum;
-}
-
 // Pipeline: K advances in steps of 32.  Operand tiles go from HBM straight into LDS
 // (buffer loads with an LDS destination, no registers), into NBUF stages that are
 // separate LDS arrays, NBUF - 1 steps ahead of the MFMAs.  Each step: wait for this
@@ -113,14 +70,14 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   // The grid is sized from a bound on the rows; blocks past the real tile count leave, and
   // the real tiles are spread over the XCDs by the remap over their own count (a remap over
   // the whole grid would crowd them onto the first XCDs when the bound is loose).
-  const int real_blocks = __builtin_amdgcn_readfirstlane(total_m_tiles(offsets, G)) * n_tiles;
+  const int real_blocks = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
   if ((int)blockIdx.x >= real_blocks) return;
   const int lin = xcd_remap(blockIdx.x, real_blocks);
   const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles (n tile folded below)
   int g, mt_first, mt_count;
   // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
   // (mt_first + mt_count) * n_tiles).  Within a group the order is chosen below.
-  find_group(offsets, G, m_lin, g, mt_first, mt_count);
+  find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count);
   // the scan's results are equal in every lane: keep them (and all that derives from
   // them, like the buffer resources) in scalar registers
   g = __builtin_amdgcn_readfirstlane(g);

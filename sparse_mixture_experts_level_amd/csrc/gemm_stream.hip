@@ -11,12 +11,13 @@
 // 16-column output subtiles; with SwiGLU it loads the matching gate rows and up
 // rows (W rows n and n + n_out) so both accumulators of a column sit in the same
 // lane.  Weight rows go straight from HBM into MFMA B-operand registers (16 bytes
-// per lane per subtile and 32-wide k step), prefetched two LDS stages ahead.  The
-// expert's token rows (A operand, reused by every column tile of the expert) are
-// staged through LDS in 64-wide K chunks, XOR-swizzled by row so the 16-lane column
-// reads of the MFMA layout spread over distinct banks.  Row blocks of BM rows are
-// walked in order, so any group size is computed correctly; 16-row subtiles beyond
-// the group's rows skip their MFMAs.
+// per lane per subtile and 32-wide k step).  The expert's token rows (A operand,
+// reused by every column tile of the expert) go straight from memory into LDS with
+// buffer loads that target LDS (no registers), in 64-wide K chunks, XOR-swizzled by
+// row so the 16-lane column reads of the MFMA layout spread over distinct banks.
+// Both operands run two chunks ahead through three register slots / LDS stages.
+// Row blocks of BM rows are walked in order, so any group size is computed
+// correctly; 16-row subtiles beyond the group's rows skip their MFMAs.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,65 +27,56 @@ namespace {
 
 constexpr int SG_KC = 64;  // K per pipeline chunk = two 32-wide MFMA k steps
 
+// LDS bytes of one A stage: BM rows of one chunk, and at least the 64 * NW pieces of 16
+// bytes that one round of the workgroup's NW waves writes.
+template <int BM, int NW>
+constexpr int sg_stage_bytes() {
+  return (BM * 8 < 64 * NW ? 64 * NW : BM * 8) * 16;
+}
+
 // Loop over K for one block of `rows` <= BM rows starting at m0, specialised on NA,
-// the number of 256-thread A load rounds the block needs (ceil(rows * 8 / 256)):
-// blocks of few rows issue few A loads and run only the MFMA subtiles they fill.
+// the number of workgroup-wide rounds of 16-byte A pieces the block needs
+// (ceil(rows * 8 / (64 * NW))): blocks of few rows issue few A loads and run only the
+// MFMA subtiles they fill.
 //
-// P chunks are in flight per wave.  Every load is issued unconditionally through a
-// buffer resource; chunks past the end of K, token rows past the block's end and
-// weight subtiles past n_out get an out-of-range offset and read as zeros without a
-// memory access, which keeps the order of outstanding loads static: waiting for
-// chunk c never waits for chunks issued after it.
-template <int BM, int NSUB, bool SWIGLU, int P, int NA>
+// S register slots / LDS stages; operands run S - 1 chunks ahead.  Step c: wait until
+// this thread's loads of chunk c are complete (a fixed number of younger loads may stay
+// in flight), barrier (every thread's A pieces of chunk c are in LDS, and every wave is
+// done reading the stage about to be refilled), issue chunk c + S - 1 (weights into a
+// register slot, A pieces into an LDS stage), compute chunk c.
+// Loads are issued unconditionally through buffer resources: token rows past the
+// block's end and weight subtiles past n_out get an out-of-range offset and read as
+// zeros without a memory access, which keeps the count of loads per step static.
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA>
 __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t ares, const uint32_t *boff,
-                                             const uint32_t *aoff, uint8_t (*ldsA)[BM * SG_KC * 2], int nk, int rows,
-                                             int m0, int ncol0, int nvalid, int n_out, bf16_t *__restrict__ out) {
+                                             const uint32_t *aoff, uint8_t *sA0, uint8_t *sA1, uint8_t *sA2,
+                                             uint8_t *sA3, int nk, int rows, int m0, int ncol0, int nvalid,
+                                             int n_out, bf16_t *__restrict__ out) {
+  static_assert(S == 3 || S == 4, "three or four stages");
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;
-  constexpr int MS = (NA * 256 / 8 + 15) / 16 < BM / 16 ? (NA * 256 / 8 + 15) / 16 : BM / 16;
-  const int tid = threadIdx.x, lane = tid & 63;
-  struct Chunk {
-    u32x4 b[2][NB];
-    u32x4 a[NA];
-  };
-  Chunk slot[P];
-  // loads of chunk c into a slot; chunks past the end of K get out-of-range offsets
-  auto issue = [&](Chunk &ch, int c) {
-    // an invalid base is kOob, and kOob + kc stays out of range (kc < 2^31)
-    const bool ok = c < nk;
+  constexpr int MS = NA * NW / 2 < BM / 16 ? NA * NW / 2 : BM / 16;  // 16-row subtiles the block can fill
+  constexpr int LOADS = NA + 2 * NB;                       // loads per thread and chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto stage = [&](int i) -> uint8_t * { return i == 0 ? sA0 : i == 1 ? sA1 : i == 2 ? sA2 : sA3; };
+  u32x4 slot[S][2][NB];
+
+  auto issue = [&](int sl, int c) {
     const uint32_t kc = (uint32_t)c * (SG_KC * 2);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ch.a[i] = buf_ld16(ares, ok ? aoff[i] + kc : kOob);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) ch.b[s][b] = buf_ld16(wres, ok ? boff[b] + kc + s * 64u : kOob);
-  };
-  // the same for a chunk known to be inside K: straight-line code, no selects
-  auto issue_in = [&](Chunk &ch, int c) {
-    const uint32_t kc = (uint32_t)c * (SG_KC * 2);
+      for (int b = 0; b < NB; ++b) slot[sl][s][b] = buf_ld16(wres, boff[b] + kc + s * 64u);
+    uint8_t *st = stage(sl);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ch.a[i] = buf_ld16(ares, aoff[i] + kc);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) ch.b[s][b] = buf_ld16(wres, boff[b] + kc + s * 64u);
-  };
-  auto stage_a = [&](const Chunk &ch, int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = tid + 256 * i;
-      if ((BM * 8) % 256 == 0 || q < BM * 8) {
-        const int r = q >> 3, c = q & 7;
-        *reinterpret_cast<u32x4 *>(&ldsA[buf][(r * 8 + (c ^ (r & 7))) * 16]) = ch.a[i];
-      }
-    }
+    for (int i = 0; i < NA; ++i) buf_ld16_lds(ares, aoff[i] + kc, st + (i * 64 * NW + wave * 64) * 16);
   };
   f32x4 acc[MS][NB];
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Chunk &ch, int buf) {
+  auto compute = [&](int sl) {
+    const uint8_t *st = stage(sl);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 a[MS];  // all row fragments of this k step first: one LDS wait per step
@@ -92,45 +84,49 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
       for (int i = 0; i < MS; ++i) {
         const int r = i * 16 + (lane & 15);
         const int c = s * 4 + (lane >> 4);
-        a[i] = *reinterpret_cast<const u32x4 *>(&ldsA[buf][(r * 8 + (c ^ (r & 7))) * 16]);
+        a[i] = *reinterpret_cast<const u32x4 *>(st + (r * 8 + (c ^ (r & 7))) * 16);
       }
 #pragma unroll
       for (int i = 0; i < MS; ++i)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], ch.b[s][b], acc[i][b]);
+        for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], slot[sl][s][b], acc[i][b]);
     }
   };
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // prologue: chunks 0 .. P-2 in flight, A of chunk 0 in LDS buffer 0
+  // prologue: chunks 0 .. S-2 in flight (a chunk past K repeats chunk 0: harmless)
 #pragma unroll
-  for (int s = 0; s < P - 1; ++s) issue(slot[s], s);
-  stage_a(slot[0], 0);
-  __syncthreads();
-  // Main loop, P chunks per trip, while every chunk it issues lies inside K: no
-  // conditions, so slots, LDS buffers (chunk parity = s & 1, P even) and wait counts are
-  // all static.  Step c issues chunk c + P - 1 into the slot chunk c - 1 has finished
-  // with, computes chunk c, and stages the A rows of chunk c + 1.
-  static_assert(P % 2 == 0, "the LDS buffer of a chunk is its parity");
+  for (int s = 0; s < S - 1; ++s) issue(s, s < nk ? s : 0);
+  // Main loop, S chunks per trip, while every chunk it issues lies inside K: the loads
+  // of chunk c are complete once at most (S - 2) * LOADS younger ones remain.  Bare
+  // barrier: a fenced one would also wait for those younger loads.
   int c0 = 0;
-  for (; c0 + 2 * P - 2 < nk; c0 += P) {
+  for (; c0 + 2 * S - 2 < nk; c0 += S) {
 #pragma unroll
-    for (int s = 0; s < P; ++s) {
-      issue_in(slot[(s + P - 1) % P], c0 + s + P - 1);
-      compute(slot[s], s & 1);
-      stage_a(slot[(s + 1) % P], (s + 1) & 1);
-      __syncthreads();
+    for (int s = 0; s < S; ++s) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * LOADS) : "memory");
+      bar();
+      issue((s + S - 1) % S, c0 + s + S - 1);
+      compute(s);
     }
   }
-  // the last (fewer than 2P - 1) chunks
+  // the last chunks (fewer than 2S - 1): all own loads complete before each barrier
 #pragma unroll
-  for (int s = 0; s < 2 * P - 1; ++s) {
+  for (int s = 0; s < 2 * S - 1; ++s) {
     const int c = c0 + s;
     if (c >= nk) break;
-    if (c + P - 1 < nk) issue_in(slot[(s + P - 1) % P], c + P - 1);
-    compute(slot[s % P], s & 1);
-    if (c + 1 < nk) stage_a(slot[(s + 1) % P], (s + 1) & 1);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    bar();
+    if (c + S - 1 < nk) issue((s + S - 1) % S, c + S - 1);
+    compute(s % S);
   }
+  // no LDS write may outlive the block, and the next row block refills the stages
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // epilogue: C layout of the 16x16 MFMA -- column (lane & 15), rows 4*(lane>>4)+j
 #pragma unroll
@@ -157,9 +153,10 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 
 // Tiles are taken in block-id order (expert-major, column tile minor); the hardware
 // deals consecutive blocks to the 8 XCDs round-robin, which spreads every expert --
-// including the few heavily loaded ones -- over all XCDs.
-template <int BM, int NSUB, bool SWIGLU, int P>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
+// including the few heavily loaded ones -- over all XCDs.  NW waves per workgroup
+// share the staged A rows: wider workgroups load each token row fewer times.
+template <int BM, int NSUB, bool SWIGLU, int S, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
                                                                      const int32_t *__restrict__ row_index,
                                                                      int64_t a_rows,
                                                                      const int32_t *__restrict__ offsets,
@@ -167,8 +164,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_
                                                                      int n_out, int K, bf16_t *__restrict__ out,
                                                                      int n_tiles) {
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;  // 16-row weight subtiles per wave
-  constexpr int A_PER_T = (BM * 8 + 255) / 256;  // 16-byte A pieces staged per thread per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t ldsA[2][BM * SG_KC * 2];
+  constexpr int NT = 64 * NW;                     // threads
+  constexpr int A_PER_T = (BM * 8 + NT - 1) / NT;  // 16-byte A pieces per thread and chunk
+  constexpr int STAGE = sg_stage_bytes<BM, NW>();
+  // one LDS array per stage, so that waiting for the loads into one stage never waits
+  // for the loads into another
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[S > 3 ? STAGE : 16];
 
   const int tile = blockIdx.x;
   const int g = tile / n_tiles, nt = tile - g * n_tiles;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_
   if (row_begin >= row_end) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ncol0 = (nt * 4 + wave) * 16 * NSUB;
+  const int ncol0 = (nt * NW + wave) * 16 * NSUB;
   const int nvalid = max(0, min(NSUB, (n_out - ncol0) / 16));  // wave-uniform
   const uint32_t kbytes = (uint32_t)K * 2u;
   const rsrc_t wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
@@ -192,33 +193,31 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_
 
   for (int m0 = row_begin; m0 < row_end; m0 += BM) {
     const int rows = min(BM, row_end - m0);
-    // byte offset of this thread's A pieces at k = 0 (row r, 16-byte column c8); with a
-    // row gather the rows come straight from the unpermuted activations
+    // A piece q = i * NT + tid lands in LDS at q * 16: row q / 8, stored 16-byte column
+    // q % 8, which holds logical column (q % 8) ^ (row % 8).  Its source: that row of the
+    // block (gathered from the unpermuted activations through row_index when given).
     uint32_t aoff[A_PER_T];
-    rsrc_t ares;
-    if (row_index) {
-      ares = make_rsrc(A, (uint32_t)(a_rows * kbytes));
+    rsrc_t ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes)) : make_rsrc(A + (size_t)m0 * K,
+                                                                                     (uint32_t)rows * kbytes);
 #pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) {
-        const int q = tid + 256 * i;
-        const int r = q >> 3;
-        aoff[i] = (q < BM * 8 && r < rows) ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)(q & 7) * 16u : kOob;
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int q = tid + NT * i;
+      const int r = q >> 3, c = (q & 7) ^ (r & 7);
+      uint32_t o = kOob;
+      if (r < rows) {
+        const uint32_t row = row_index ? (uint32_t)row_index[m0 + r] : (uint32_t)r;
+        o = row * kbytes + (uint32_t)c * 16u;
       }
-    } else {
-      ares = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) {
-        const int q = tid + 256 * i;
-        aoff[i] = q < BM * 8 ? (uint32_t)(q >> 3) * kbytes + (uint32_t)(q & 7) * 16u : kOob;
-      }
+      aoff[i] = o;
     }
-    const int na = (rows * 8 + 255) / 256;  // workgroup-uniform
-#define SG_BLOCK(N)                                                                                                 \
-  if constexpr (N <= A_PER_T) {                                                                                     \
-    if (na == N) {                                                                                                  \
-      stream_block<BM, NSUB, SWIGLU, P, N>(wres, ares, boff, aoff, ldsA, nk, rows, m0, ncol0, nvalid, n_out, out); \
-      continue;                                                                                                     \
-    }                                                                                                               \
+    const int na = (rows * 8 + NT - 1) / NT;  // workgroup-uniform
+#define SG_BLOCK(N)                                                                                              \
+  if constexpr (N <= A_PER_T) {                                                                                  \
+    if (na == N) {                                                                                               \
+      stream_block<BM, NSUB, SWIGLU, S, NW, N>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, nk, rows, m0, ncol0, nvalid, \
+                                           n_out, out);                                                          \
+      continue;                                                                                                  \
+    }                                                                                                            \
   }
     SG_BLOCK(1)
     SG_BLOCK(2)
@@ -228,25 +227,28 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(const bf16_
   }
 }
 
-template <int BM, int NSUB, bool SWIGLU>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4>
 hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
-  constexpr int P = 4;
-  const int cols_per_tile = 64 * NSUB;
+  const int cols_per_tile = 16 * NW * NSUB;
   const int n_tiles = (a.n_out + cols_per_tile - 1) / cols_per_tile;
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, P>), dim3((unsigned)grid), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, static_cast<const bf16_t *>(a.W), a.w_group_stride,
-                     a.n_out, a.K, static_cast<bf16_t *>(a.out), n_tiles);
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                     static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets,
+                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out),
+                     n_tiles);
   return hipGetLastError();
 }
 
 template <bool SWIGLU>
 hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
+  // three stages for gate_up (two weight subtiles per wave keep enough bytes in flight),
+  // four for down (one subtile per wave: a deeper pipeline instead)
+  constexpr int S = SWIGLU ? 3 : 4;
   const int r = a.group_rows_max;
-  if (r <= 16) return launch_stream<16, 1, SWIGLU>(a, s);
-  if (r <= 32) return launch_stream<32, 1, SWIGLU>(a, s);
-  if (r <= 64) return launch_stream<64, 1, SWIGLU>(a, s);
-  return launch_stream<128, 1, SWIGLU>(a, s);
+  if (r <= 16) return launch_stream<16, 1, SWIGLU, S>(a, s);
+  if (r <= 32) return launch_stream<32, 1, SWIGLU, S>(a, s);
+  if (r <= 64) return launch_stream<64, 1, SWIGLU, S>(a, s);
+  return launch_stream<128, 1, SWIGLU, S>(a, s);
 }
 
 }  // namespace
