@@ -19,6 +19,9 @@ Sources (web pages; cited by title and section):
           gerwin.io (sections "Как работает MoE: принцип маршрутизации",
           "Обратная сторона медали: недостатки и сложности MoE").
 
+The backward pass (``moe_backward``) is the plain chain-rule derivative of these
+steps with the routing held fixed.
+
 The steps, in order:
   1. router logits  l_t = W_r x_t (+ optional per-expert offset)   [SMoE, router]
   2. softmax over experts, in float64                               [SMoE, router]
@@ -63,6 +66,10 @@ __all__ = [
     "moe_forward",
     "aux_load_balancing_loss",
     "active_params",
+    "silu_grad",
+    "swiglu_ffn_backward",
+    "topk_gates_backward",
+    "moe_backward",
 ]
 
 
@@ -419,6 +426,137 @@ def aux_load_balancing_loss(ids, probs, num_experts: int, alpha: float = 1e-2) -
     f = np.bincount(ids.reshape(-1), minlength=num_experts).astype(np.float64) / ids.size
     P = p.mean(axis=0)
     return float(alpha * num_experts * np.sum(f * P)) if T else 0.0
+
+
+def silu_grad(z) -> np.ndarray:
+    """d/dz silu(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z))), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def swiglu_ffn_backward(x_rows, w_gate_up, w_down, dy_rows, scale=None) -> dict:
+    """Gradient of one expert's SwiGLU FFN (``swiglu_ffn``) summed over its rows,
+    each row's output weighted by ``scale`` (its gate; 1 when omitted):
+        out_r = scale_r * y_r,  y = (silu(X W_g^T) * (X W_u^T)) W_d^T.
+    Returns dx [n, d], dw_gate_up [2f, d], dw_down [d, f] and dscale [n] (= dy_r . y_r),
+    by the chain rule, float64.  The training setting is the pages' ([HF-MoE],
+    "Обучение MoE с помощью Transformers": the expert projections run as grouped
+    GEMMs in training as well); the gradient itself is the plain derivative.
+    """
+    X = np.asarray(x_rows, dtype=np.float64)
+    Wgu = np.asarray(w_gate_up, dtype=np.float64)
+    Wd = np.asarray(w_down, dtype=np.float64)
+    dY = np.asarray(dy_rows, dtype=np.float64)
+    n, f = X.shape[0], Wd.shape[1]
+    c = np.ones(n) if scale is None else np.asarray(scale, dtype=np.float64)
+    G = X @ Wgu[:f].T
+    U = X @ Wgu[f:].T
+    H = silu(G) * U
+    Y = H @ Wd.T
+    dscale = np.sum(dY * Y, axis=1)
+    dYs = dY * c[:, None]                 # gradient reaching y_r
+    dH = dYs @ Wd                         # [n, f]
+    dG = dH * U * silu_grad(G)
+    dU = dH * silu(G)
+    dx = dG @ Wgu[:f] + dU @ Wgu[f:]
+    dw_gate_up = np.concatenate([dG.T @ X, dU.T @ X], axis=0)
+    dw_down = dYs.T @ H
+    return {"dx": dx, "dw_gate_up": dw_gate_up, "dw_down": dw_down, "dscale": dscale}
+
+
+def topk_gates_backward(logits, ids, dgates) -> np.ndarray:
+    """Gradient of the renormalised top-k gates with respect to the router logits.
+    The gates are a softmax over the selected logits (``topk_gates``), so for the
+    selected experts dl_j = g_j * (dg_j - sum_j' g_j' dg_j') and dl = 0 for the
+    others (the selection itself is piecewise constant).  Returns dlogits [T, E]."""
+    l = np.asarray(logits, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    g = topk_gates(l, ids)
+    dg = np.asarray(dgates, dtype=np.float64)
+    dsel = g * (dg - np.sum(g * dg, axis=1, keepdims=True))
+    dl = np.zeros_like(l)
+    np.put_along_axis(dl, ids, dsel, axis=1)
+    return dl
+
+
+def moe_backward(x, w_router, w_gate_up, w_down, top_k: int, cap: Optional[int], dy, logit_offset=None,
+                 w_shared_gate_up=None, w_shared_down=None, ids=None, fill_order: str = "token",
+                 overflow: str = "drop") -> dict:
+    """Gradient of ``moe_forward``'s output, contracted with ``dy`` [T, d], with respect
+    to x, the router weight and every expert weight, float64.
+
+    Routing (top-k choice, capacity slots, drops, redirection) is piecewise constant
+    and taken as fixed; gradients flow through the gates, the expert FFNs and the shared
+    expert.  A dropped assignment contributes nothing, so its gate receives no
+    gradient from it (its gate still enters the renormalisation of the others); an
+    expert with no kept rows gets zero weight gradients.  ``ids`` overrides the top-k
+    choice as in ``moe_forward``.  Returns dx, dw_router, dw_gate_up, dw_down (and
+    dw_shared_gate_up / dw_shared_down when a shared expert is given), plus dlogits and
+    dgates.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    T, d = x64.shape
+    wr = np.asarray(w_router, dtype=np.float64)
+    E = wr.shape[0]
+    logits = router_logits(x64, wr, logit_offset)
+    if ids is None:
+        ids = topk_select(logits, top_k)
+    ids = np.asarray(ids, dtype=np.int32)
+    gates = topk_gates(logits, ids)
+    if overflow == "drop":
+        fill = capacity_fill(ids, E, cap, fill_order)
+        serving = ids
+    elif overflow == "reroute":
+        fill = capacity_fill_reroute(ids, logits, E, cap, fill_order)
+        serving = fill["assigned"]
+    else:
+        raise ValueError("overflow must be 'drop' or 'reroute'")
+    slot = fill["slot"]
+    dx = np.zeros((T, d))
+    dgates = np.zeros((T, top_k))
+    dw_gate_up, dw_down = {}, {}
+    rows = {}
+    for t in range(T):
+        for j in range(top_k):
+            if slot[t, j] >= 0:
+                rows.setdefault(int(serving[t, j]), []).append((t, j))
+    for e in range(E):
+        Wgu = _expert(w_gate_up, e)
+        Wd = _expert(w_down, e)
+        if e not in rows:
+            dw_gate_up[e] = np.zeros_like(Wgu)
+            dw_down[e] = np.zeros_like(Wd)
+            continue
+        tj = rows[e]
+        toks = [t for t, _ in tj]
+        g = np.array([gates[t, j] for t, j in tj])
+        b = swiglu_ffn_backward(x64[toks], Wgu, Wd, dy64[toks], scale=g)
+        for r, (t, j) in enumerate(tj):
+            dx[t] += b["dx"][r]
+            dgates[t, j] = b["dscale"][r]
+        dw_gate_up[e] = b["dw_gate_up"]
+        dw_down[e] = b["dw_down"]
+    dlogits = topk_gates_backward(logits, ids, dgates)
+    dx += dlogits @ wr
+    out = {
+        "dx": dx,
+        "dw_router": dlogits.T @ x64,
+        "dw_gate_up": np.stack([dw_gate_up[e] for e in range(E)]),
+        "dw_down": np.stack([dw_down[e] for e in range(E)]),
+        "dlogits": dlogits,
+        "dgates": dgates,
+        "ids": ids,
+        "slot": slot,
+    }
+    if w_shared_gate_up is not None:
+        b = swiglu_ffn_backward(x64, w_shared_gate_up, w_shared_down, dy64)
+        out["dx"] = out["dx"] + b["dx"]
+        out["dw_shared_gate_up"] = b["dw_gate_up"]
+        out["dw_shared_down"] = b["dw_down"]
+    return out
 
 
 def active_params(d_model: int, hidden: int, num_experts: int, top_k: int, ffn: str = "swiglu") -> dict:
