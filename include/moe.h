@@ -295,6 +295,37 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
                        const float *logit_offset, void *out, moe_routing *routing, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Weight gradients of moe_backward (device pointers). */
+typedef struct moe_grads {
+  void *dw_router;         /* [E, d] float */
+  void *dw_gate_up;        /* [E, 2f, d] dtype: gate rows then up rows, as w_gate_up */
+  void *dw_down;           /* [E, d, f] dtype */
+  void *dw_shared_gate_up; /* [2 f_s, d] dtype, or NULL when d_ff_shared == 0 */
+  void *dw_shared_down;    /* [d, f_s]   dtype, or NULL when d_ff_shared == 0 */
+} moe_grads;
+
+/* Workspace bytes needed by moe_backward; 0 for an invalid or unsupported descriptor. */
+size_t moe_backward_workspace_size(const moe_desc *desc);
+
+/* Backward pass of the layer: gradients of L = sum(dy * out) for the out of moe_forward,
+ * with the routing held fixed (top-k choice, slots and drops are piecewise constant;
+ * [HF-MoE] "Обучение MoE с помощью Transformers": in training the expert projections
+ * run as grouped GEMMs too).  Per kept row of expert e with gate g:
+ *   dH' = dy W_d[e];  dg = dH' . H;  [dG dU] from g dH' through SwiGLU;
+ *   dx += [dG dU] W_gu[e];  dW_d[e] += (g dy) (x) H;  dW_gu[e] += [dG dU] (x) x;
+ * gates (softmax over the selected logits): dl_j = g_j (dg_j - sum g dg), dW_r = dl^T x,
+ * dx += dl W_r; the shared expert likewise with g = 1 for every token.  Experts without
+ * kept rows get zero gradients.  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise).
+ *   x, dy      [T, d] dtype (the forward's input; the loss gradient w.r.t. out)
+ *   routing    the tables moe_forward wrote for x: topk_ids, topk_gates, expert_offsets,
+ *              slot, row_token (and assigned_ids when desc->overflow redirects) are read
+ *   dx         [T, d] dtype, written
+ *   grads      written in full (see moe_grads)
+ *   ws         at least moe_backward_workspace_size(desc) bytes
+ * Accumulation in float; every sum in a fixed order (bit-reproducible). */
+moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const void *x, const moe_routing *routing,
+                        const void *dy, void *dx, moe_grads *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* One rank's share of expert parallelism ([HF-MoE] "Параллелизм экспертов
  * (Expert Parallelism)": each device holds a contiguous subset of the experts,
  * computes them, and partial outputs are summed across devices with an all-reduce;

@@ -570,3 +570,283 @@ moe_status moe_forward_expert_shard(const moe_desc *desc, const moe_weights *wei
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------- backward
+
+namespace {
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct BwdLayout {
+  size_t gu, dhp, dgu, hg, dxr, wdT, wguT, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wrT, dxrt, tpoff,
+      sh_off, gus, dhs, dgus, hs, dxs, wsdT, wsguT, dyTT, hsT, dgusT, total;
+  int64_t Rpad, Tpad, Epad;
+};
+
+BwdLayout bwd_layout(const moe_desc &D) {
+  BwdLayout L{};
+  const int64_t T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
+  const int64_t R = max_rows(D);
+  L.Rpad = round_up(R + 32 * E, 8);  // each group padded to a multiple of 32 rows
+  L.Tpad = round_up(T, 32);
+  L.Epad = round_up(E, 64);
+  size_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t at = o;
+    o += align_up((size_t)std::max<int64_t>(bytes, 0));
+    return at;
+  };
+  const int64_t s = 2;
+  L.gu = take(R * 2 * f * 4);  // float
+  L.dhp = take(R * f * s);
+  L.dgu = take(R * 2 * f * s);
+  L.hg = take(R * f * s);
+  L.dxr = take(R * d * s);
+  L.wdT = take(E * f * d * s);
+  L.wguT = take(E * d * 2 * f * s);
+  L.poff = take((E + 1) * 4);
+  L.dyT = take(d * L.Rpad * s);
+  L.hgT = take(f * L.Rpad * s);
+  L.dguT = take(2 * f * L.Rpad * s);
+  L.xT = take(d * L.Rpad * s);
+  L.dgate = take(T * k * 4);
+  L.dl = take(T * E * 4);
+  L.dl16 = take(T * L.Epad * s);
+  L.dlT = take(L.Epad * L.Tpad * s);
+  L.xTT = take(d * L.Tpad * s);
+  L.wrT = take(d * L.Epad * s);
+  L.dxrt = take(T * d * s);
+  L.tpoff = take(2 * 4);
+  L.sh_off = take(2 * 4);
+  L.gus = take(fs ? T * 2 * fs * 4 : 0);  // float
+  L.dhs = take(fs ? T * fs * s : 0);
+  L.dgus = take(fs ? T * 2 * fs * s : 0);
+  L.hs = take(fs ? T * fs * s : 0);
+  L.dxs = take(fs ? T * d * s : 0);
+  L.wsdT = take(fs ? fs * d * s : 0);
+  L.wsguT = take(fs ? d * 2 * fs * s : 0);
+  L.dyTT = take(fs ? d * L.Tpad * s : 0);
+  L.hsT = take(fs ? fs * L.Tpad * s : 0);
+  L.dgusT = take(fs ? 2 * fs * L.Tpad * s : 0);
+  L.total = o;
+  return L;
+}
+
+moe_status check_bwd_desc(const moe_desc *desc) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 layers");
+  const BwdLayout L = bwd_layout(D);
+  const int64_t f2 = 2 * (int64_t)std::max(D.d_ff, D.d_ff_shared);
+  // operands of the weight-gradient GEMM are addressed through 32-bit buffer offsets
+  if (f2 * std::max<int64_t>(L.Rpad, L.Tpad) * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)D.d_model * std::max<int64_t>(L.Rpad, L.Tpad) * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "the backward pass needs its transposed activations to stay below 2 GiB");
+  return MOE_OK;
+}
+
+// w_stride: elements from one group's weight matrix to the next, and at least the size of
+// one matrix (the kernels bound their weight reads by it).
+moe::GroupedGemmArgs gemm_args(int32_t G, int64_t rows_max, int32_t group_rows_max, const void *A,
+                               const int32_t *row_index, int64_t a_rows, const int32_t *offsets, const void *W,
+                               int64_t w_stride, int32_t n_out, int32_t K, void *out, bool out_f32 = false) {
+  moe::GroupedGemmArgs a{};
+  a.A = A;
+  a.row_index = row_index;
+  a.a_rows = a_rows;
+  a.offsets = offsets;
+  a.num_groups = G;
+  a.group_rows_max = std::max(1, group_rows_max);
+  a.rows_max = rows_max;
+  a.W = W;
+  a.w_group_stride = w_stride;
+  a.n_out = n_out;
+  a.K = K;
+  a.out = out;
+  a.swiglu = false;
+  a.out_f32 = out_f32;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_backward_workspace_size(const moe_desc *desc) {
+  if (check_bwd_desc(desc) != MOE_OK) return 0;
+  return bwd_layout(*desc).total;
+}
+
+moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const void *x, const moe_routing *routing,
+                        const void *dy, void *dx, moe_grads *grads, void *ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_bwd_desc(desc));
+  const moe_desc &D = *desc;
+  if (!weights) return fail(MOE_ERR_INVALID, "weights is NULL");
+  if (!routing) return fail(MOE_ERR_INVALID, "routing is NULL: pass the tables moe_forward wrote");
+  if (!grads) return fail(MOE_ERR_INVALID, "grads is NULL");
+  if (D.num_tokens == 0) return ok();
+  const int T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(dy, "dy"));
+  MOE_TRY(check_ptr(dx, "dx"));
+  MOE_TRY(check_ptr(weights->w_router, "w_router"));
+  MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
+  MOE_TRY(check_ptr(weights->w_down, "w_down"));
+  MOE_TRY(check_ptr(routing->topk_ids, "routing.topk_ids"));
+  MOE_TRY(check_ptr(routing->topk_gates, "routing.topk_gates"));
+  MOE_TRY(check_ptr(routing->expert_offsets, "routing.expert_offsets"));
+  MOE_TRY(check_ptr(routing->slot, "routing.slot"));
+  MOE_TRY(check_ptr(routing->row_token, "routing.row_token"));
+  if (rerouting(D)) MOE_TRY(check_ptr(routing->assigned_ids, "routing.assigned_ids"));
+  MOE_TRY(check_ptr(grads->dw_router, "grads.dw_router"));
+  MOE_TRY(check_ptr(grads->dw_gate_up, "grads.dw_gate_up"));
+  MOE_TRY(check_ptr(grads->dw_down, "grads.dw_down"));
+  if (fs > 0) {
+    MOE_TRY(check_ptr(weights->w_shared_gate_up, "w_shared_gate_up"));
+    MOE_TRY(check_ptr(weights->w_shared_down, "w_shared_down"));
+    MOE_TRY(check_ptr(grads->dw_shared_gate_up, "grads.dw_shared_gate_up"));
+    MOE_TRY(check_ptr(grads->dw_shared_down, "grads.dw_shared_down"));
+  }
+  const BwdLayout L = bwd_layout(D);
+  if (!ws || ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_backward needs %zu workspace bytes, got %zu", L.total,
+                ws ? ws_bytes : (size_t)0);
+  MOE_TRY(check_ptr(ws, "ws"));
+
+  const int32_t *ids = routing->topk_ids, *offsets = routing->expert_offsets, *slot = routing->slot,
+                *row_token = routing->row_token;
+  const int32_t *serving = rerouting(D) ? routing->assigned_ids : ids;
+  const float *gates = routing->topk_gates;
+  const int64_t R = max_rows(D);
+  const int32_t grb = std::max(1, group_rows_bound(D));
+  const int32_t *rows_dev = offsets + E;  // kept rows, on the device
+  auto W = [&](size_t off) { return at<void>(ws, off); };
+  const int64_t s = 2;
+  auto hcall = [&](hipError_t e, const char *what) { return hip_status(e, what); };
+  auto gemm = [&](const moe::GroupedGemmArgs &a, const char *what) {
+    return hcall(moe::launch_grouped_gemm_bf16(a, stream), what);
+  };
+  int32_t *poff = at<int32_t>(ws, L.poff), *tpoff = at<int32_t>(ws, L.tpoff), *sh_off = at<int32_t>(ws, L.sh_off);
+  MOE_TRY(hcall(moe::launch_fill_i32(tpoff, 2, 0, (int32_t)L.Tpad, stream), "offsets"));
+  MOE_TRY(hcall(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "offsets"));
+
+  // ---- routed experts
+  if (R > 0) {
+    MOE_TRY(hcall(moe::launch_pad_offsets(offsets, E, poff, stream), "padded offsets"));
+    // G | U of every kept row, recomputed from x
+    MOE_TRY(gemm(gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d,
+                           W(L.gu), true),
+                 "gate_up recompute"));
+    // dH' = dy W_d (weights transposed to [f, d] per expert)
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0,
+                                           nullptr, W(L.wdT), d, (int64_t)f * d, stream),
+                "w_down transpose"));
+    MOE_TRY(gemm(gemm_args(E, R, grb, dy, row_token, T, offsets, W(L.wdT), (int64_t)f * d, f, d, W(L.dhp)),
+                 "dH' grouped GEMM"));
+  }
+  float *dgate = at<float>(ws, L.dgate);
+  MOE_TRY(hcall(moe::launch_fill_u32(dgate, (int64_t)T * k, 0u, stream), "zero gate gradients"));
+  if (R > 0) {
+    MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gu), W(L.dhp), R, rows_dev, f, row_token, serving, slot, offsets, gates,
+                                       k, W(L.dgu), W(L.hg), dgate, stream),
+                "SwiGLU backward"));
+    // dx rows = [dG dU] W_gu (weights transposed to [d, 2f] per expert)
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d, E, nullptr, nullptr,
+                                           nullptr, 0, nullptr, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
+                "w_gate_up transpose"));
+    MOE_TRY(gemm(gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, W(L.wguT), (int64_t)d * 2 * f, d, 2 * f,
+                           W(L.dxr)),
+                 "dx grouped GEMM"));
+    // weight gradients, grouped over each expert's rows (padded to 32, zeros in the pad)
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dyT), d * L.Rpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.hgT), f * L.Rpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dguT), 2 * f * L.Rpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.xT), d * L.Rpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, rows_dev, W(L.dyT), L.Rpad, 0,
+                                           stream),
+                "dy transpose"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, rows_dev, W(L.xT), L.Rpad, 0,
+                                           stream),
+                "x transpose"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, rows_dev, W(L.hgT),
+                                           L.Rpad, 0, stream),
+                "H transpose"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, rows_dev, W(L.dguT),
+                                           L.Rpad, 0, stream),
+                "dGU transpose"));
+    MOE_TRY(hcall(moe::launch_wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, stream),
+                "dW_down"));
+    MOE_TRY(hcall(moe::launch_wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up,
+                                  stream),
+                "dW_gate_up"));
+  } else {
+    MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_down, (int64_t)E * d * f * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_gate_up, (int64_t)E * 2 * f * d * s / 4, 0u, stream), "zero"));
+  }
+
+  // ---- router: dl from the gate gradients; dW_r = dl^T x, dx += dl W_r
+  MOE_TRY(hcall(moe::launch_gates_bwd(ids, gates, dgate, T, E, k, (int)L.Epad, at<float>(ws, L.dl), W(L.dl16), stream),
+              "gate backward"));
+  MOE_TRY(hcall(moe::launch_fill_u32(W(L.dlT), L.Epad * L.Tpad * s / 4, 0u, stream), "zero"));
+  MOE_TRY(hcall(moe::launch_fill_u32(W(L.xTT), d * L.Tpad * s / 4, 0u, stream), "zero"));
+  MOE_TRY(hcall(moe::launch_fill_u32(W(L.wrT), d * L.Epad * s / 4, 0u, stream), "zero"));
+  MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dl16), 0, T, (int)L.Epad, 1, nullptr, nullptr, nullptr, 0, nullptr,
+                                         W(L.dlT), L.Tpad, 0, stream),
+              "dl transpose"));
+  MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, T, d, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.xTT), L.Tpad, 0,
+                                         stream),
+              "x transpose"));
+  MOE_TRY(hcall(moe::launch_wgrad(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, E, d, true, grads->dw_router, stream),
+              "dW_router"));
+  MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_router, 0, E, d, 1, nullptr, nullptr, nullptr, 0, nullptr,
+                                         W(L.wrT), L.Epad, 0, stream),
+              "w_router transpose"));
+  MOE_TRY(gemm(gemm_args(1, T, T, W(L.dl16), nullptr, 0, sh_off, W(L.wrT), (int64_t)d * L.Epad, d, (int32_t)L.Epad,
+                         W(L.dxrt)),
+               "router dx"));
+
+  // ---- shared expert (weight 1, every token)
+  const void *dxs = nullptr;
+  if (fs > 0) {
+    MOE_TRY(gemm(gemm_args(1, T, T, x, nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, 2 * fs, d,
+                           W(L.gus), true),
+                 "shared gate_up recompute"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_down, 0, d, fs, 1, nullptr, nullptr, nullptr, 0, nullptr,
+                                           W(L.wsdT), d, 0, stream),
+                "shared w_down transpose"));
+    MOE_TRY(gemm(gemm_args(1, T, T, dy, nullptr, 0, sh_off, W(L.wsdT), (int64_t)fs * d, fs, d, W(L.dhs)), "shared dH'"));
+    MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gus), W(L.dhs), T, nullptr, fs, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       1, W(L.dgus), W(L.hs), nullptr, stream),
+                "shared SwiGLU backward"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_gate_up, 0, 2 * fs, d, 1, nullptr, nullptr, nullptr, 0,
+                                           nullptr, W(L.wsguT), 2 * fs, 0, stream),
+                "shared w_gate_up transpose"));
+    MOE_TRY(gemm(gemm_args(1, T, T, W(L.dgus), nullptr, 0, sh_off, W(L.wsguT), (int64_t)d * 2 * fs, d, 2 * fs,
+                           W(L.dxs)), "shared dx"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dyTT), d * L.Tpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.hsT), fs * L.Tpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dgusT), 2 * fs * L.Tpad * s / 4, 0u, stream), "zero"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.dyTT), L.Tpad,
+                                           0, stream),
+                "dy transpose"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.hsT),
+                                           L.Tpad, 0, stream),
+                "shared H transpose"));
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, nullptr,
+                                           W(L.dgusT), L.Tpad, 0, stream),
+                "shared dGU transpose"));
+    MOE_TRY(hcall(moe::launch_wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false,
+                                  grads->dw_shared_down, stream),
+                "dW_shared_down"));
+    MOE_TRY(hcall(moe::launch_wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false,
+                                  grads->dw_shared_gate_up, stream),
+                "dW_shared_gate_up"));
+    dxs = W(L.dxs);
+  }
+
+  // ---- dx: the expert rows of each token, the router term and the shared expert's
+  MOE_TRY(hcall(moe::launch_dx_gather(W(L.dxr), serving, slot, offsets, T, d, k, W(L.dxrt), dxs, dx, stream), "dx"));
+  return ok();
+}
+
+}  // extern "C"

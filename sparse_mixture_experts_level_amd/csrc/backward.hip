@@ -1,0 +1,369 @@
+// Backward pass of the sparse MoE layer on gfx950: the kernels besides the grouped
+// GEMMs.  The training setting is the one of "Что такое Mixture of Experts (MoE) в
+// трансформерах", aglamov.biz, section "Обучение MoE с помощью Transformers" (the
+// expert projections run as grouped GEMMs in training too); the gradient itself is
+// the chain rule through the forward with the routing held fixed:
+//   per kept row r = (t, j) of expert e, with G = x W_g^T, U = x W_u^T, H = silu(G) U:
+//     dH'_r = dy_t W_d[e]                 (unweighted; a grouped GEMM)
+//     dg_tj = dH'_r . H_r                 (= dy_t . y_r)
+//     dH = g_tj dH';  dG = dH U silu'(G);  dU = dH silu(G)
+//     dx_t += [dG dU] W_gu[e]             (a grouped GEMM)
+//     dW_d[e] += (g dy_t) (x) H_r,  dW_gu[e] += [dG dU] (x) x_t   (grouped over rows)
+//   gates g = softmax over the selected logits:
+//     dl_tj = g_tj (dg_tj - sum_j' g_tj' dg_tj'),   dW_r = dl^T x,   dx += dl W_r
+// Every kernel here is deterministic: no atomics, fixed summation orders.
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int TR = 64;  // transpose tile
+
+// out[b][c][pos(r)] = in[b][src(r)][c] for r < rows, c < cols (bf16), where src(r) =
+// row_index[r] (or r) and pos(r) = r, or, with group offsets, the row's place in a
+// layout whose groups start on padded offsets: pos(r) = r - off[g] + poff[g].
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t *__restrict__ in, int64_t in_stride_b,
+                                                             int64_t rows, int cols, const int32_t *__restrict__ row_index,
+                                                             const int32_t *__restrict__ off,
+                                                             const int32_t *__restrict__ poff, int G,
+                                                             const int32_t *__restrict__ rows_dev,
+                                                             bf16_t *__restrict__ out, int64_t out_ld,
+                                                             int64_t out_stride_b) {
+  __shared__ bf16_t tile[TR][TR + 2];
+  const int b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.x * TR;
+  const int c0 = blockIdx.y * TR;
+  const int64_t nrows = rows_dev ? min<int64_t>(rows, (int64_t)*rows_dev) : rows;
+  if (r0 >= nrows) return;
+  const bf16_t *src = in + (size_t)b * in_stride_b;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < TR; i += 4) {
+    const int64_t r = r0 + i;
+    bf16_t v = 0;
+    if (r < nrows && c0 + tx < cols) {
+      const int64_t sr = row_index ? (int64_t)row_index[r] : r;
+      v = src[(size_t)sr * cols + c0 + tx];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  // destination position of this thread's row (column of out)
+  const int64_t r = r0 + tx;
+  int64_t pos = r;
+  if (off && r < nrows) {
+    int lo = 0, hi = G;  // largest g with off[g] <= r
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= r) lo = mid; else hi = mid;
+    }
+    pos = r - off[lo] + poff[lo];
+  }
+  bf16_t *dst = out + (size_t)b * out_stride_b;
+  for (int i = ty; i < TR; i += 4) {
+    const int c = c0 + i;
+    if (r < nrows && c < cols) dst[(size_t)c * out_ld + pos] = tile[tx][i];
+  }
+}
+
+// poff[g] = sum over g' < g of the group's rows rounded up to 32 (the K chunk of the
+// weight-gradient GEMM), poff[G] = total.  One block.
+__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t *__restrict__ off, int G,
+                                                          int32_t *__restrict__ poff) {
+  __shared__ int32_t s[MOE_MAX_EXPERTS_DEV + 1];
+  for (int g = threadIdx.x; g < G; g += 256) s[g] = (off[g + 1] - off[g] + 31) / 32 * 32;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int g = 0; g < G; ++g) {
+      const int v = s[g];
+      poff[g] = run;
+      run += v;
+    }
+    poff[G] = run;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+__device__ __forceinline__ float silu_grad_f32(float z) {
+  const float s = 1.0f / (1.0f + __expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// One wavefront per row r of the expert-sorted layout.  Finds the row's assignment
+// (t, j), takes its gate g (1 without gates), and from gu = [G | U] (float: silu' is
+// steep enough that a bf16 G would cost percent-level gradient error) and dh' computes
+// dgu = [dG | dU], hg = g * H and dgate[t][j] = dh' . H (float, fixed lane order).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict__ gu, const bf16_t *__restrict__ dhp,
+                                                         int64_t rows, const int32_t *__restrict__ rows_dev, int f,
+                                                         const int32_t *__restrict__ row_token,
+                                                         const int32_t *__restrict__ serving,
+                                                         const int32_t *__restrict__ slot,
+                                                         const int32_t *__restrict__ offsets,
+                                                         const float *__restrict__ gates, int k,
+                                                         bf16_t *__restrict__ dgu, bf16_t *__restrict__ hg,
+                                                         float *__restrict__ dgate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nrows = rows_dev ? min<int64_t>(rows, (int64_t)*rows_dev) : rows;
+  if (r >= nrows) return;
+  float g = 1.0f;
+  int jt = -1;
+  int64_t t = r;
+  if (gates) {
+    t = row_token[r];
+    for (int j = 0; j < k; ++j) {
+      const int sl = slot[t * k + j];
+      if (sl >= 0 && (int64_t)offsets[serving[t * k + j]] + sl == r) jt = j;
+    }
+    g = jt >= 0 ? gates[t * k + jt] : 0.0f;
+  }
+  const float *G = gu + (size_t)r * 2 * f, *U = G + f;
+  const bf16_t *D = dhp + (size_t)r * f;
+  bf16_t *dG = dgu + (size_t)r * 2 * f, *dU = dG + f;
+  bf16_t *HG = hg + (size_t)r * f;
+  float dot = 0.0f;
+  for (int c = lane * 8; c < f; c += 64 * 8) {
+    const u32x4 dv = ldg16(D + c);
+    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(G + c), g1 = *reinterpret_cast<const f32x4 *>(G + c + 4);
+    const f32x4 u0 = *reinterpret_cast<const f32x4 *>(U + c), u1 = *reinterpret_cast<const f32x4 *>(U + c + 4);
+    u32x4 og, ou, oh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float z[2], u[2], d[2], rg[2], ru[2], rh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 2 * q + h;
+        z[h] = e < 4 ? g0[e] : g1[e - 4];
+        u[h] = e < 4 ? u0[e] : u1[e - 4];
+        d[h] = bf16_to_f32(bf16_t(dv[q] >> (16 * h)));
+        const float sz = silu_f32(z[h]);
+        const float H = sz * u[h];
+        dot += d[h] * H;
+        const float dh = g * d[h];
+        rg[h] = dh * u[h] * silu_grad_f32(z[h]);
+        ru[h] = dh * sz;
+        rh[h] = g * H;
+      }
+      og[q] = pack_bf16x2(rg[0], rg[1]);
+      ou[q] = pack_bf16x2(ru[0], ru[1]);
+      oh[q] = pack_bf16x2(rh[0], rh[1]);
+    }
+    stg16(dG + c, og);
+    stg16(dU + c, ou);
+    stg16(HG + c, oh);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+  if (dgate && lane == 0 && jt >= 0) dgate[t * k + jt] = dot;
+}
+
+// Gradient of the renormalised gates with respect to the logits, one wavefront per token:
+// dl[t][ids_j] = g_j (dg_j - sum_j' g_j' dg_j'), zero elsewhere; written as float [T, E]
+// and as bf16 [T, Epad] (zero padded).
+__global__ __launch_bounds__(256) void gates_bwd_kernel(const int32_t *__restrict__ ids,
+                                                        const float *__restrict__ gates,
+                                                        const float *__restrict__ dgate, int T, int E, int k,
+                                                        int Epad, float *__restrict__ dl,
+                                                        bf16_t *__restrict__ dl16) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += gates[(size_t)t * k + j] * dgate[(size_t)t * k + j];  // same order in every lane
+  for (int e = lane; e < Epad; e += 64) {
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j)
+      if (ids[(size_t)t * k + j] == e) {
+        const float g = gates[(size_t)t * k + j];
+        v = g * (dgate[(size_t)t * k + j] - s);
+      }
+    if (e < E) dl[(size_t)t * E + e] = v;
+    dl16[(size_t)t * Epad + e] = f32_to_bf16(v);
+  }
+}
+
+// dx[t] = sum over kept j of dxr[row(t, j)] (+ extra[t]) (+ extra2[t]), float sums in
+// a fixed order, one wavefront per token, 16-byte vectors.
+__global__ __launch_bounds__(256) void dx_gather_kernel(const bf16_t *__restrict__ dxr,
+                                                        const int32_t *__restrict__ serving,
+                                                        const int32_t *__restrict__ slot,
+                                                        const int32_t *__restrict__ offsets, int T, int d, int k,
+                                                        const bf16_t *__restrict__ extra,
+                                                        const bf16_t *__restrict__ extra2, bf16_t *__restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add = [&](const bf16_t *p) {
+      const u32x4 v = ldg16(p);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(bf16_t(v[q]));
+        acc[2 * q + 1] += bf16_to_f32(bf16_t(v[q] >> 16));
+      }
+    };
+    for (int j = 0; j < k; ++j) {
+      const int sl = slot[(size_t)t * k + j];
+      if (sl >= 0) add(dxr + ((size_t)offsets[serving[(size_t)t * k + j]] + sl) * d + c);
+    }
+    if (extra) add(extra + (size_t)t * d + c);
+    if (extra2) add(extra2 + (size_t)t * d + c);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    stg16(dx + (size_t)t * d + c, o);
+  }
+}
+
+// Weight-gradient GEMM grouped over the contraction: for group g,
+//   out[g][m][n] = sum over k in [poff[g], poff[g+1]) of AT[m][k] * BT[n][k]
+// AT [M, lda], BT [N, ldb] bf16, K-contiguous; group ranges are multiples of 32 (padding
+// columns hold zeros).  64 x 64 output tile per workgroup, 4 waves of 32 x 32
+// (2 x 2 16x16x32 MFMA subtiles), operands straight from memory into MFMA registers,
+// P chunks of 32 in flight.  Rows past M / columns past N read zeros and are not stored.
+// An empty group writes zeros.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void wgrad_kernel(const bf16_t *__restrict__ AT, int64_t lda,
+                                                    const bf16_t *__restrict__ BT, int64_t ldb,
+                                                    const int32_t *__restrict__ poff, int M, int N, int m_tiles,
+                                                    int n_tiles, void *__restrict__ out) {
+  constexpr int P = 4;
+  const int tile = blockIdx.x;
+  const int g = tile / (m_tiles * n_tiles);
+  const int rem = tile - g * m_tiles * n_tiles;
+  const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = mt * 64 + (wave >> 1) * 32, n0 = nt * 64 + (wave & 1) * 32;
+  const int kb = poff[g], ke = poff[g + 1];
+  const int nk = (ke - kb) / 32;
+  const rsrc_t ares = make_rsrc(AT, (uint32_t)min<int64_t>((int64_t)M * lda * 2, 0x7fffffffLL));
+  const rsrc_t bres = make_rsrc(BT, (uint32_t)min<int64_t>((int64_t)N * ldb * 2, 0x7fffffffLL));
+  uint32_t ao[2], bo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + i * 16 + (lane & 15), n = n0 + i * 16 + (lane & 15);
+    ao[i] = m < M ? (uint32_t)(((int64_t)m * lda + kb) * 2) + (uint32_t)(lane >> 4) * 16u : kOob;
+    bo[i] = n < N ? (uint32_t)(((int64_t)n * ldb + kb) * 2) + (uint32_t)(lane >> 4) * 16u : kOob;
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 fa[P][2], fb[P][2];
+  auto issue = [&](int s, int c) {
+    const bool ok = c < nk;
+    const uint32_t kc = (uint32_t)c * 64u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa[s][i] = buf_ld16(ares, ok && ao[i] != kOob ? ao[i] + kc : kOob);
+      fb[s][i] = buf_ld16(bres, ok && bo[i] != kOob ? bo[i] + kc : kOob);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) issue(s, s);
+  for (int c0 = 0; c0 < nk; c0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      const int c = c0 + s;
+      if (c >= nk) break;
+      issue((s + P - 1) % P, c + P - 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(fa[s][i], fb[s][j], acc[i][j]);
+    }
+  }
+  // C layout of the 16x16 MFMA: column (lane & 15), rows 4 * (lane >> 4) + q
+  const size_t obase = (size_t)g * M * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + j * 16 + (lane & 15);
+      if (n >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + i * 16 + (lane >> 4) * 4 + q;
+        if (m >= M) continue;
+        if constexpr (OUT_F32)
+          static_cast<float *>(out)[obase + (size_t)m * N + n] = acc[i][j][q];
+        else
+          static_cast<bf16_t *>(out)[obase + (size_t)m * N + n] = f32_to_bf16(acc[i][j][q]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
+                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G,
+                                 const int32_t *rows_dev, void *out, int64_t out_ld, int64_t out_stride_b,
+                                 hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + TR - 1) / TR), (unsigned)((cols + TR - 1) / TR), (unsigned)batch);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t *>(in), in_stride_b, rows,
+                     cols, row_index, off, poff, G, rows_dev, static_cast<bf16_t *>(out), out_ld, out_stride_b);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_offsets(const int32_t *off, int G, int32_t *poff, hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(256), 0, s, off, G, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void *p, int64_t n_words, uint32_t v, hipStream_t s) {
+  if (n_words <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n_words + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint32_t *>(p), n_words, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, const int32_t *rows_dev, int f,
+                             const int32_t *row_token, const int32_t *serving, const int32_t *slot,
+                             const int32_t *offsets, const float *gates, int k, void *dgu, void *hg, float *dgate,
+                             hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const float *>(gu), static_cast<const bf16_t *>(dhp), rows, rows_dev, f, row_token,
+                     serving, slot, offsets, gates, k, static_cast<bf16_t *>(dgu), static_cast<bf16_t *>(hg), dgate);
+  return hipGetLastError();
+}
+
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, int T, int E, int k, int Epad,
+                            float *dl, void *dl16, hipStream_t s) {
+  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, ids, gates, dgate, T, E, k,
+                     Epad, dl, static_cast<bf16_t *>(dl16));
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
+                            int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s) {
+  hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const bf16_t *>(dxr), serving, slot, offsets, T, d, k,
+                     static_cast<const bf16_t *>(extra), static_cast<const bf16_t *>(extra2), static_cast<bf16_t *>(dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
+                        int N, bool out_f32, void *out, hipStream_t s) {
+  const int m_tiles = (M + 63) / 64, n_tiles = (N + 63) / 64;
+  const int64_t grid = (int64_t)G * m_tiles * n_tiles;
+  if (out_f32)
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT), lda,
+                       static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out);
+  else
+    hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT),
+                       lda, static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

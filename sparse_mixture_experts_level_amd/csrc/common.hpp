@@ -26,6 +26,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return bf16_t(u >> 16);
 }
 
+// Store of a float result as the output element type (bf16, rounded to nearest even, or float).
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT *p, float v) {
+  if constexpr (sizeof(OutT) == 4)
+    *p = v;
+  else
+    *p = f32_to_bf16(v);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }

@@ -41,14 +41,14 @@ constexpr int BG_BM = 256, BG_BN = 256;
 //
 // WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
 // 4: eight waves of 128 x 64, two per SIMD).
-template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t>
 __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
                                                                          const int32_t *__restrict__ offsets, int G,
                                                                          const bf16_t *__restrict__ W,
                                                                          int64_t wstride, int n_out, int K,
-                                                                         bf16_t *__restrict__ out, int n_tiles) {
+                                                                         OutT *__restrict__ out, int n_tiles) {
   constexpr int BK = BKP;                        // K per step: 32 or 64
   constexpr int RB = BK * 2;                     // bytes per tile row
   constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
         } else {
           v = acc[i][j][r];
         }
-        out[(size_t)(m0 + row) * n_out + col] = f32_to_bf16(v);
+        store_out(out + (size_t)(m0 + row) * n_out + col, v);
       }
     }
   }
@@ -313,23 +313,24 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 
 }  // namespace
 
-template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32, typename OutT = bf16_t>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
   const int64_t grid = m_tiles * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
-                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out),
+                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles);
   return hipGetLastError();
 }
 
 // Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
-  return a.swiglu ? launch_big<true, 4, 4, true>(a, rows_total_max, s)
-                  : launch_big<false, 4, 4, true>(a, rows_total_max, s);
+  if (a.swiglu) return launch_big<true, 4, 4, true>(a, rows_total_max, s);
+  return a.out_f32 ? launch_big<false, 4, 4, true, 32, float>(a, rows_total_max, s)
+                   : launch_big<false, 4, 4, true>(a, rows_total_max, s);
 }
 
 }  // namespace moe

@@ -47,11 +47,11 @@ constexpr int sg_stage_bytes() {
 // Loads are issued unconditionally through buffer resources: token rows past the
 // block's end and weight subtiles past n_out get an out-of-range offset and read as
 // zeros without a memory access, which keeps the count of loads per step static.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT>
 __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t ares, const uint32_t *boff,
                                              const uint32_t *aoff, uint8_t *sA0, uint8_t *sA1, uint8_t *sA2,
                                              uint8_t *sA3, int nk, int rows, int m0, int ncol0, int nvalid,
-                                             int n_out, bf16_t *__restrict__ out) {
+                                             int n_out, OutT *__restrict__ out) {
   static_assert(S == 3 || S == 4, "three or four stages");
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;
   constexpr int MS = NA * NW / 2 < BM / 16 ? NA * NW / 2 : BM / 16;  // 16-row subtiles the block can fill
@@ -145,7 +145,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
         } else {
           v = acc[i][s][j];
         }
-        out[(size_t)(m0 + r) * n_out + col] = f32_to_bf16(v);
+        store_out(out + (size_t)(m0 + r) * n_out + col, v);
       }
     }
   }
@@ -155,13 +155,13 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 // deals consecutive blocks to the 8 XCDs round-robin, which spreads every expert --
 // including the few heavily loaded ones -- over all XCDs.  NW waves per workgroup
 // share the staged A rows: wider workgroups load each token row fewer times.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, typename OutT>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
                                                                      const int32_t *__restrict__ row_index,
                                                                      int64_t a_rows,
                                                                      const int32_t *__restrict__ offsets,
                                                                      const bf16_t *__restrict__ W, int64_t wstride,
-                                                                     int n_out, int K, bf16_t *__restrict__ out,
+                                                                     int n_out, int K, OutT *__restrict__ out,
                                                                      int n_tiles) {
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;  // 16-row weight subtiles per wave
   constexpr int NT = 64 * NW;                     // threads
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
 #define SG_BLOCK(N)                                                                                              \
   if constexpr (N <= A_PER_T) {                                                                                  \
     if (na == N) {                                                                                               \
-      stream_block<BM, NSUB, SWIGLU, S, NW, N>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, nk, rows, m0, ncol0, nvalid, \
+      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, nk, rows, m0, ncol0, nvalid, \
                                            n_out, out);                                                          \
       continue;                                                                                                  \
     }                                                                                                            \
@@ -227,34 +227,35 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   }
 }
 
-template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4, typename OutT = bf16_t>
 hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
   const int cols_per_tile = 16 * NW * NSUB;
   const int n_tiles = (a.n_out + cols_per_tile - 1) / cols_per_tile;
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                      static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets,
-                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<bf16_t *>(a.out),
+                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles);
   return hipGetLastError();
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, typename OutT = bf16_t>
 hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
   // three stages for gate_up (two weight subtiles per wave keep enough bytes in flight),
   // four for down (one subtile per wave: a deeper pipeline instead)
   constexpr int S = SWIGLU ? 3 : 4;
   const int r = a.group_rows_max;
-  if (r <= 16) return launch_stream<16, 1, SWIGLU, S>(a, s);
-  if (r <= 32) return launch_stream<32, 1, SWIGLU, S>(a, s);
-  if (r <= 64) return launch_stream<64, 1, SWIGLU, S>(a, s);
-  return launch_stream<128, 1, SWIGLU, S>(a, s);
+  if (r <= 16) return launch_stream<16, 1, SWIGLU, S, 4, OutT>(a, s);
+  if (r <= 32) return launch_stream<32, 1, SWIGLU, S, 4, OutT>(a, s);
+  if (r <= 64) return launch_stream<64, 1, SWIGLU, S, 4, OutT>(a, s);
+  return launch_stream<128, 1, SWIGLU, S, 4, OutT>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s) {
-  return a.swiglu ? launch_stream_bm<true>(a, s) : launch_stream_bm<false>(a, s);
+  if (a.swiglu) return launch_stream_bm<true>(a, s);
+  return a.out_f32 ? launch_stream_bm<false, float>(a, s) : launch_stream_bm<false>(a, s);
 }
 
 // Regime choice: the streaming kernel when groups hold few rows on average (each

@@ -63,6 +63,7 @@ struct GroupedGemmArgs {
   int K;
   void *out;
   bool swiglu;
+  bool out_f32 = false;  // float output instead of the element type (bf16 kernels, no SwiGLU)
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);
@@ -81,5 +82,29 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, int T, in
 
 // ---- small utilities (combine.hip)
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v0, int32_t step, hipStream_t s);
+
+// ---- backward (backward.hip); bf16 activations and weights
+// out[b][c][pos(r)] = in[b][src(r)][c]: src(r) = row_index[r] or r; pos(r) = r, or with
+// group offsets off/poff (G groups) the row's place in the padded layout; rows past
+// *rows_dev (when given) are skipped.
+hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
+                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G,
+                                 const int32_t *rows_dev, void *out, int64_t out_ld, int64_t out_stride_b,
+                                 hipStream_t s);
+// poff[g] = sum over g' < g of ceil32(off[g'+1] - off[g']), poff[G] = total
+hipError_t launch_pad_offsets(const int32_t *off, int G, int32_t *poff, hipStream_t s);
+hipError_t launch_fill_u32(void *p, int64_t n_words, uint32_t v, hipStream_t s);
+// per row: dgu = [dG | dU], hg = g * H, dgate[t][j] = dh' . H (gates NULL: g = 1, rows are tokens)
+hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, const int32_t *rows_dev, int f,
+                             const int32_t *row_token, const int32_t *serving, const int32_t *slot,
+                             const int32_t *offsets, const float *gates, int k, void *dgu, void *hg, float *dgate,
+                             hipStream_t s);
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, int T, int E, int k, int Epad,
+                            float *dl, void *dl16, hipStream_t s);
+hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
+                            int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
+// out[g][m][n] = sum_{k in [poff[g], poff[g+1])} AT[m][k] BT[n][k]; ranges multiples of 32
+hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
+                        int N, bool out_f32, void *out, hipStream_t s);
 
 }  // namespace moe

@@ -30,6 +30,7 @@ SYMBOLS = [
     "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
     "moe_dispatch_permute", "moe_dispatch_reroute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
     "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
+    "moe_backward_workspace_size", "moe_backward",
 ]
 
 
@@ -49,6 +50,11 @@ class MoeDesc(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("w_shared_gate_up", ctypes.c_void_p), ("w_shared_down", ctypes.c_void_p)]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [("dw_router", ctypes.c_void_p), ("dw_gate_up", ctypes.c_void_p), ("dw_down", ctypes.c_void_p),
+                ("dw_shared_gate_up", ctypes.c_void_p), ("dw_shared_down", ctypes.c_void_p)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -98,6 +104,10 @@ def lib() -> ctypes.CDLL:
     L.moe_forward_expert_shard.argtypes = [dp, ctypes.POINTER(MoeWeights), i32, i32, i32, vp, vp, vp,
                                            ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward_expert_shard.restype = st
+    L.moe_backward_workspace_size.argtypes, L.moe_backward_workspace_size.restype = [dp], sz
+    L.moe_backward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, ctypes.POINTER(MoeRouting), vp, vp,
+                               ctypes.POINTER(MoeGrads), vp, sz, vp]
+    L.moe_backward.restype = st
     _lib = L
     return L
 
@@ -267,6 +277,21 @@ def moe_forward_expert_shard(desc, w_router, w_gate_up_local, w_down_local, expe
                                           ctypes.byref(R) if R is not None else None, _ptr(ws),
                                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward_expert_shard")
+
+
+def moe_backward_workspace_size(desc: MoeDesc) -> int:
+    return int(lib().moe_backward_workspace_size(ctypes.byref(desc)))
+
+
+def moe_backward(desc, w_router, w_gate_up, w_down, x, routing: dict, dy, dx, grads: dict, ws,
+                 w_shared_gate_up=None, w_shared_down=None, stream=None) -> None:
+    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down))
+    R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
+    G = MoeGrads(*(_ptr(grads.get(n)) for n, _ in MoeGrads._fields_))
+    _check(lib().moe_backward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), ctypes.byref(R), _ptr(dy), _ptr(dx),
+                              ctypes.byref(G), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)),
+           "moe_backward")
 
 
 class MoELayer:
