@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="after the run, copy a buffer of this many MiB three times (a kernel of known traffic for "
                         "scaling hardware byte counters)")
+    p.add_argument("--backward", action="store_true",
+                   help="time the layer's backward pass (moe_backward, routing from one forward) instead of the "
+                        "forward")
     p.add_argument("--ep-shards", type=int, default=1, metavar="N",
                    help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
                         "contiguous ranges, every range timed on this GPU, the slowest one reported")
@@ -77,6 +80,8 @@ def main():
     s_bytes = 2 if w.dtype == "bf16" else 4
     if args.ep_shards > 1:
         return ep_share_bench(args, w, inp, cap, layer, s_bytes)
+    if args.backward:
+        return backward_bench(args, w, inp, cap, layer, s_bytes)
 
     # ---------------------------------------------------------------- whole-path timing
     for _ in range(args.warmup):
@@ -318,6 +323,76 @@ def ep_share_bench(args, w, inp, cap, layer, s_bytes):
                    "num_tokens": T, "d_model": d, "num_experts": E, "top_k": w.top_k, "d_ff": f, "d_ff_shared": fs,
                    "capacity": cap, "ep_shards": N, "experts_per_rank": per},
         "ranks": ranks,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def backward_bench(args, w, inp, cap, layer, s_bytes):
+    """The backward pass alone: gradients of sum(dy * out) with respect to x and every
+    weight, for the routing of one forward pass of the same batch."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_level_amd.ops as ops
+
+    dev = "cuda"
+    T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
+    if w.dtype != "bf16":
+        print("the backward pass is implemented for bf16 layers", file=sys.stderr)
+        sys.exit(2)
+    layer.forward(with_routing=True)
+    torch.cuda.synchronize()
+    kept = np.diff(layer.routing["expert_offsets"].cpu().numpy().astype(np.int64))
+    R, E_t = int(kept.sum()), int((kept > 0).sum())
+    g = torch.Generator(device=dev).manual_seed(args.seed + 1)
+    dy = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+    dx = torch.empty_like(dy)
+    grads = {"dw_router": torch.empty((E, d), dtype=torch.float32, device=dev),
+             "dw_gate_up": torch.empty((E, 2 * f, d), dtype=torch.bfloat16, device=dev),
+             "dw_down": torch.empty((E, d, f), dtype=torch.bfloat16, device=dev)}
+    if fs:
+        grads["dw_shared_gate_up"] = torch.empty((2 * fs, d), dtype=torch.bfloat16, device=dev)
+        grads["dw_shared_down"] = torch.empty((d, fs), dtype=torch.bfloat16, device=dev)
+    ws = ops.workspace(ops.moe_backward_workspace_size(layer.desc), dev)
+
+    def step():
+        ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx, grads, ws,
+                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # algorithmic work: recompute of G|U, dH', dx rows, dW_gate_up, dW_down (16 R d f), the
+    # router (4 T E d) and the shared expert (16 T d f_s); bytes: touched experts' weights read
+    # once, every weight gradient written once, x, dy read and dx written
+    flop = 16.0 * R * d * f + 4.0 * T * E * d + 16.0 * T * d * fs
+    nbytes = s_bytes * (E_t * 3 * d * f + E * 3 * d * f + 6 * d * fs + 3 * T * d) + E * d * (s_bytes + 4)
+    rt = max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
+    line = {
+        "metric": "MoE-layer backward tokens/sec on 1 MI355X",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}, backward pass", "num_tokens": T, "d_model": d, "num_experts": E,
+                   "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap, "kept_rows": R,
+                   "experts_touched": E_t},
+        "layer_roofline": {"algorithmic_flop": flop, "algorithmic_bytes": nbytes, "roofline_ms": round(rt * 1e3, 4),
+                           "frac_of_roofline": round(rt * 1e3 / ms, 4)},
         "roofline": None,
         "cpu_baseline": None,
     }

@@ -726,6 +726,13 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   auto gemm = [&](const moe::GroupedGemmArgs &a, const char *what) {
     return hcall(moe::launch_grouped_gemm_bf16(a, stream), what);
   };
+  // weight-gradient GEMM: 256 x 256 tiles when the groups' contraction ranges are long,
+  // 64 x 64 tiles for short ones (few rows per expert)
+  auto wgrad = [&](const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M, int N,
+                   bool f32, void *out, int64_t avg_k) {
+    return avg_k >= 128 ? moe::launch_wgrad_big(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream)
+                        : moe::launch_wgrad(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream);
+  };
   int32_t *poff = at<int32_t>(ws, L.poff), *tpoff = at<int32_t>(ws, L.tpoff), *sh_off = at<int32_t>(ws, L.sh_off);
   MOE_TRY(hcall(moe::launch_fill_i32(tpoff, 2, 0, (int32_t)L.Tpad, stream), "offsets"));
   MOE_TRY(hcall(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "offsets"));
@@ -738,8 +745,8 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                            W(L.gu), true),
                  "gate_up recompute"));
     // dH' = dy W_d (weights transposed to [f, d] per expert)
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0,
-                                           nullptr, W(L.wdT), d, (int64_t)f * d, stream),
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0, d,
+                                           W(L.wdT), d, (int64_t)f * d, stream),
                 "w_down transpose"));
     MOE_TRY(gemm(gemm_args(E, R, grb, dy, row_token, T, offsets, W(L.wdT), (int64_t)f * d, f, d, W(L.dhp)),
                  "dH' grouped GEMM"));
@@ -752,32 +759,27 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                 "SwiGLU backward"));
     // dx rows = [dG dU] W_gu (weights transposed to [d, 2f] per expert)
     MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d, E, nullptr, nullptr,
-                                           nullptr, 0, nullptr, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
+                                           nullptr, 0, 2 * f, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
                 "w_gate_up transpose"));
     MOE_TRY(gemm(gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, W(L.wguT), (int64_t)d * 2 * f, d, 2 * f,
                            W(L.dxr)),
                  "dx grouped GEMM"));
     // weight gradients, grouped over each expert's rows (padded to 32, zeros in the pad)
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dyT), d * L.Rpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.hgT), f * L.Rpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dguT), 2 * f * L.Rpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.xT), d * L.Rpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, rows_dev, W(L.dyT), L.Rpad, 0,
+    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad, 0,
                                            stream),
                 "dy transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, rows_dev, W(L.xT), L.Rpad, 0,
+    MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.xT), L.Rpad, 0,
                                            stream),
                 "x transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, rows_dev, W(L.hgT),
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.hgT),
                                            L.Rpad, 0, stream),
                 "H transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, rows_dev, W(L.dguT),
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.dguT),
                                            L.Rpad, 0, stream),
                 "dGU transpose"));
-    MOE_TRY(hcall(moe::launch_wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, stream),
+    MOE_TRY(hcall(wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, R / E),
                 "dW_down"));
-    MOE_TRY(hcall(moe::launch_wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up,
-                                  stream),
+    MOE_TRY(hcall(wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up, R / E),
                 "dW_gate_up"));
   } else {
     MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_down, (int64_t)E * d * f * s / 4, 0u, stream), "zero"));
@@ -787,18 +789,15 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   // ---- router: dl from the gate gradients; dW_r = dl^T x, dx += dl W_r
   MOE_TRY(hcall(moe::launch_gates_bwd(ids, gates, dgate, T, E, k, (int)L.Epad, at<float>(ws, L.dl), W(L.dl16), stream),
               "gate backward"));
-  MOE_TRY(hcall(moe::launch_fill_u32(W(L.dlT), L.Epad * L.Tpad * s / 4, 0u, stream), "zero"));
-  MOE_TRY(hcall(moe::launch_fill_u32(W(L.xTT), d * L.Tpad * s / 4, 0u, stream), "zero"));
-  MOE_TRY(hcall(moe::launch_fill_u32(W(L.wrT), d * L.Epad * s / 4, 0u, stream), "zero"));
-  MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dl16), 0, T, (int)L.Epad, 1, nullptr, nullptr, nullptr, 0, nullptr,
+  MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dl16), 0, T, (int)L.Epad, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
                                          W(L.dlT), L.Tpad, 0, stream),
               "dl transpose"));
-  MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, T, d, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.xTT), L.Tpad, 0,
+  MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.xTT), L.Tpad, 0,
                                          stream),
               "x transpose"));
-  MOE_TRY(hcall(moe::launch_wgrad(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, E, d, true, grads->dw_router, stream),
+  MOE_TRY(hcall(wgrad(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, E, d, true, grads->dw_router, T),
               "dW_router"));
-  MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_router, 0, E, d, 1, nullptr, nullptr, nullptr, 0, nullptr,
+  MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_router, 0, E, d, 1, nullptr, nullptr, nullptr, 0, L.Epad,
                                          W(L.wrT), L.Epad, 0, stream),
               "w_router transpose"));
   MOE_TRY(gemm(gemm_args(1, T, T, W(L.dl16), nullptr, 0, sh_off, W(L.wrT), (int64_t)d * L.Epad, d, (int32_t)L.Epad,
@@ -811,7 +810,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(gemm(gemm_args(1, T, T, x, nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, 2 * fs, d,
                            W(L.gus), true),
                  "shared gate_up recompute"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_down, 0, d, fs, 1, nullptr, nullptr, nullptr, 0, nullptr,
+    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_down, 0, d, fs, 1, nullptr, nullptr, nullptr, 0, d,
                                            W(L.wsdT), d, 0, stream),
                 "shared w_down transpose"));
     MOE_TRY(gemm(gemm_args(1, T, T, dy, nullptr, 0, sh_off, W(L.wsdT), (int64_t)fs * d, fs, d, W(L.dhs)), "shared dH'"));
@@ -819,27 +818,23 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                                        1, W(L.dgus), W(L.hs), nullptr, stream),
                 "shared SwiGLU backward"));
     MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_gate_up, 0, 2 * fs, d, 1, nullptr, nullptr, nullptr, 0,
-                                           nullptr, W(L.wsguT), 2 * fs, 0, stream),
+                                           2 * fs, W(L.wsguT), 2 * fs, 0, stream),
                 "shared w_gate_up transpose"));
     MOE_TRY(gemm(gemm_args(1, T, T, W(L.dgus), nullptr, 0, sh_off, W(L.wsguT), (int64_t)d * 2 * fs, d, 2 * fs,
                            W(L.dxs)), "shared dx"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dyTT), d * L.Tpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.hsT), fs * L.Tpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_fill_u32(W(L.dgusT), 2 * fs * L.Tpad * s / 4, 0u, stream), "zero"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.dyTT), L.Tpad,
+    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT), L.Tpad,
                                            0, stream),
                 "dy transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, nullptr, W(L.hsT),
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.hsT),
                                            L.Tpad, 0, stream),
                 "shared H transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, nullptr,
+    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
                                            W(L.dgusT), L.Tpad, 0, stream),
                 "shared dGU transpose"));
-    MOE_TRY(hcall(moe::launch_wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false,
-                                  grads->dw_shared_down, stream),
+    MOE_TRY(hcall(wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false, grads->dw_shared_down, T),
                 "dW_shared_down"));
-    MOE_TRY(hcall(moe::launch_wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false,
-                                  grads->dw_shared_gate_up, stream),
+    MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false, grads->dw_shared_gate_up,
+                        T),
                 "dW_shared_gate_up"));
     dxs = W(L.dxs);
   }

@@ -23,49 +23,61 @@ namespace {
 
 constexpr int TR = 64;  // transpose tile
 
-// out[b][c][pos(r)] = in[b][src(r)][c] for r < rows, c < cols (bf16), where src(r) =
-// row_index[r] (or r) and pos(r) = r, or, with group offsets, the row's place in a
-// layout whose groups start on padded offsets: pos(r) = r - off[g] + poff[g].
+// out[b][c][p] = in[b][src(p)][c] for every position p < P and c < cols (bf16), zero where
+// p has no source row.  Plain: src(p) = p for p < rows.  Grouped (off / poff, G groups):
+// position p of group g (poff[g] <= p < poff[g+1]) holds row off[g] + (p - poff[g]) while
+// that row belongs to the group, through row_index when given, and zero in the group's
+// padding.  64 x 64 tiles through LDS, 16-byte loads and stores; cols and P multiples of 8.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t *__restrict__ in, int64_t in_stride_b,
-                                                             int64_t rows, int cols, const int32_t *__restrict__ row_index,
+                                                             int64_t rows, int cols,
+                                                             const int32_t *__restrict__ row_index,
                                                              const int32_t *__restrict__ off,
-                                                             const int32_t *__restrict__ poff, int G,
-                                                             const int32_t *__restrict__ rows_dev,
+                                                             const int32_t *__restrict__ poff, int G, int64_t P,
                                                              bf16_t *__restrict__ out, int64_t out_ld,
                                                              int64_t out_stride_b) {
-  __shared__ bf16_t tile[TR][TR + 2];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TR][TR + 8];
   const int b = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.x * TR;
+  const int64_t p0 = (int64_t)blockIdx.x * TR;
   const int c0 = blockIdx.y * TR;
-  const int64_t nrows = rows_dev ? min<int64_t>(rows, (int64_t)*rows_dev) : rows;
-  if (r0 >= nrows) return;
   const bf16_t *src = in + (size_t)b * in_stride_b;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < TR; i += 4) {
-    const int64_t r = r0 + i;
-    bf16_t v = 0;
-    if (r < nrows && c0 + tx < cols) {
-      const int64_t sr = row_index ? (int64_t)row_index[r] : r;
-      v = src[(size_t)sr * cols + c0 + tx];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int v = tid + 256 * j;
+    const int pl = v >> 3, cv = (v & 7) * 8;
+    const int64_t p = p0 + pl;
+    int64_t r = -1;
+    if (p < P) {
+      if (!off) {
+        r = p < rows ? p : -1;
+      } else if (p < poff[G]) {
+        int lo = 0, hi = G;  // largest g with poff[g] <= p
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (poff[mid] <= p) lo = mid; else hi = mid;
+        }
+        const int64_t local = p - poff[lo];
+        if (local < off[lo + 1] - off[lo]) r = off[lo] + local;
+      }
     }
-    tile[i][tx] = v;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r >= 0 && c0 + cv < cols) {
+      const int64_t sr = row_index ? (int64_t)row_index[r] : r;
+      val = ldg16(src + (size_t)sr * cols + c0 + cv);
+    }
+    *reinterpret_cast<u32x4 *>(&tile[pl][cv]) = val;
   }
   __syncthreads();
-  // destination position of this thread's row (column of out)
-  const int64_t r = r0 + tx;
-  int64_t pos = r;
-  if (off && r < nrows) {
-    int lo = 0, hi = G;  // largest g with off[g] <= r
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= r) lo = mid; else hi = mid;
-    }
-    pos = r - off[lo] + poff[lo];
-  }
   bf16_t *dst = out + (size_t)b * out_stride_b;
-  for (int i = ty; i < TR; i += 4) {
-    const int c = c0 + i;
-    if (r < nrows && c < cols) dst[(size_t)c * out_ld + pos] = tile[tx][i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int v = tid + 256 * j;
+    const int cl = v >> 3, pv = (v & 7) * 8;
+    if (c0 + cl >= cols || p0 + pv >= P) continue;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = uint32_t(tile[pv + 2 * q][cl]) | (uint32_t(tile[pv + 2 * q + 1][cl]) << 16);
+    stg16(dst + (size_t)(c0 + cl) * out_ld + p0 + pv, o);
   }
 }
 
@@ -305,13 +317,12 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const bf16_t *__restrict__ A
 }  // namespace
 
 hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
-                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G,
-                                 const int32_t *rows_dev, void *out, int64_t out_ld, int64_t out_stride_b,
-                                 hipStream_t s) {
-  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
-  dim3 grid((unsigned)((rows + TR - 1) / TR), (unsigned)((cols + TR - 1) / TR), (unsigned)batch);
+                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G, int64_t P,
+                                 void *out, int64_t out_ld, int64_t out_stride_b, hipStream_t s) {
+  if (P <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)((P + TR - 1) / TR), (unsigned)((cols + TR - 1) / TR), (unsigned)batch);
   hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t *>(in), in_stride_b, rows,
-                     cols, row_index, off, poff, G, rows_dev, static_cast<bf16_t *>(out), out_ld, out_stride_b);
+                     cols, row_index, off, poff, G, P, static_cast<bf16_t *>(out), out_ld, out_stride_b);
   return hipGetLastError();
 }
 

@@ -41,14 +41,19 @@ constexpr int BG_BM = 256, BG_BN = 256;
 //
 // WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
 // 4: eight waves of 128 x 64, two per SIMD).
-template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t>
+// WG: the weight-gradient form, grouped over the contraction instead of the rows:
+//   out[g][m][n] = sum over k in [offsets[g], offsets[g+1]) of A[m][k] * W[n][k],
+// A [M, lda] and W [n_out, ldb] (both K-contiguous, e.g. transposed activations whose
+// groups start on multiples of 32), every group M x n_out, written at out + g * M * n_out.
+template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t, bool WG = false>
 __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
                                                                          const int32_t *__restrict__ offsets, int G,
                                                                          const bf16_t *__restrict__ W,
                                                                          int64_t wstride, int n_out, int K,
-                                                                         OutT *__restrict__ out, int n_tiles) {
+                                                                         OutT *__restrict__ out, int n_tiles,
+                                                                         int64_t lda, int64_t ldb, int M) {
   constexpr int BK = BKP;                        // K per step: 32 or 64
   constexpr int RB = BK * 2;                     // bytes per tile row
   constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
@@ -67,48 +72,8 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t * { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
-  // The grid is sized from a bound on the rows; blocks past the real tile count leave, and
-  // the real tiles are spread over the XCDs by the remap over their own count (a remap over
-  // the whole grid would crowd them onto the first XCDs when the bound is loose).
-  const int real_blocks = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
-  if ((int)blockIdx.x >= real_blocks) return;
-  const int lin = xcd_remap(blockIdx.x, real_blocks);
-  const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles (n tile folded below)
-  int g, mt_first, mt_count;
-  // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
-  // (mt_first + mt_count) * n_tiles).  Within a group the order is chosen below.
-  find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count);
-  // the scan's results are equal in every lane: keep them (and all that derives from
-  // them, like the buffer resources) in scalar registers
-  g = __builtin_amdgcn_readfirstlane(g);
-  mt_first = __builtin_amdgcn_readfirstlane(mt_first);
-  mt_count = __builtin_amdgcn_readfirstlane(mt_count);
-  if (g < 0) return;
-  const int local = lin - mt_first * n_tiles;  // 0 .. mt_count * n_tiles - 1
-  const int row_begin = offsets[g], row_end = offsets[g + 1];
-  const int64_t a_bytes = (int64_t)(row_end - row_begin) * K;
-  const int64_t b_bytes = (int64_t)(SWIGLU ? 2 : 1) * n_out * K;
-  int mt, nt;
-  if (a_bytes <= b_bytes) {  // weights larger: weight tile outermost, row tiles reuse it
-    nt = local / mt_count;
-    mt = local - nt * mt_count;
-  } else {
-    mt = local / n_tiles;
-    nt = local - mt * n_tiles;
-  }
-  const int m0 = row_begin + mt * BG_BM;
-  const int rows = min(BG_BM, row_end - m0);
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN_W, wn = wave % WN_W;
-  const uint32_t kbytes = (uint32_t)K * 2u;
-  const int n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
-
-  // A rows: contiguous from m0, or gathered from the unpermuted activations by row_index
-  const rsrc_t ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes))
-                                : make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
-  const rsrc_t wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
-
   // Swizzle of a row's 16-byte chunks.  32-wide steps: 64-byte rows, chunk c of row r
   // at c ^ ((r >> 2) & 3); 64-wide steps: 128-byte rows, at c ^ ((r >> 1) & 7).  Either
   // way 16 consecutive rows read at one logical chunk land on 16 distinct 16-byte bank
@@ -116,25 +81,102 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto swz = [&](int r) -> int { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int blk = wave * IPW + i;
-    const int r = blk * RPI + lane / NCH;
-    const int c = (lane % NCH) ^ swz(r);
-    if (row_index)
-      agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
-    else
-      agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
-    int wr;  // weight row held in tile row r, -1 past n_out
-    if (SWIGLU) {
-      const int col = n0 + (r & 127);
-      wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
+  int m0, rows, n0, nk;
+  rsrc_t ares, wres;
+  OutT *obase;
+  int64_t ostride;
+  if constexpr (!WG) {
+    // The grid is sized from a bound on the rows; blocks past the real tile count leave,
+    // and the real tiles are spread over the XCDs by the remap over their own count (a
+    // remap over the whole grid would crowd them onto the first XCDs when the bound is
+    // loose).
+    const int real_blocks = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+    if ((int)blockIdx.x >= real_blocks) return;
+    const int lin = xcd_remap(blockIdx.x, real_blocks);
+    const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles
+    int g, mt_first, mt_count;
+    // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
+    // (mt_first + mt_count) * n_tiles).  Within a group the order is chosen below.
+    find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count);
+    // the scan's results are equal in every lane: keep them (and all that derives from
+    // them, like the buffer resources) in scalar registers
+    g = __builtin_amdgcn_readfirstlane(g);
+    mt_first = __builtin_amdgcn_readfirstlane(mt_first);
+    mt_count = __builtin_amdgcn_readfirstlane(mt_count);
+    if (g < 0) return;
+    const int local = lin - mt_first * n_tiles;  // 0 .. mt_count * n_tiles - 1
+    const int row_begin = offsets[g], row_end = offsets[g + 1];
+    const int64_t a_bytes = (int64_t)(row_end - row_begin) * K;
+    const int64_t b_bytes = (int64_t)(SWIGLU ? 2 : 1) * n_out * K;
+    int mt, nt;
+    if (a_bytes <= b_bytes) {  // weights larger: weight tile outermost, row tiles reuse it
+      nt = local / mt_count;
+      mt = local - nt * mt_count;
     } else {
-      wr = n0 + r < n_out ? n0 + r : -1;
+      mt = local / n_tiles;
+      nt = local - mt * n_tiles;
     }
-    bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
+    m0 = row_begin + mt * BG_BM;
+    rows = min(BG_BM, row_end - m0);
+    n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
+    const uint32_t kbytes = (uint32_t)K * 2u;
+    // A rows: contiguous from m0, or gathered from the unpermuted activations by row_index
+    ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes)) : make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
+    wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int blk = wave * IPW + i;
+      const int r = blk * RPI + lane / NCH;
+      const int c = (lane % NCH) ^ swz(r);
+      if (row_index)
+        agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
+      else
+        agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
+      int wr;  // weight row held in tile row r, -1 past n_out
+      if (SWIGLU) {
+        const int col = n0 + (r & 127);
+        wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
+      } else {
+        wr = n0 + r < n_out ? n0 + r : -1;
+      }
+      bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
+    }
+    nk = K / BK;
+    obase = out;
+    ostride = n_out;
+  } else {
+    const int m_tiles = (M + BG_BM - 1) / BG_BM;
+    const int per_g = m_tiles * n_tiles;
+    const int real_blocks = G * per_g;
+    if ((int)blockIdx.x >= real_blocks) return;
+    const int lin = xcd_remap(blockIdx.x, real_blocks);
+    const int g = lin / per_g, local = lin - g * per_g;
+    int mt, nt;
+    if (M <= n_out) {  // the B operand larger: its tile outermost
+      nt = local / m_tiles;
+      mt = local - nt * m_tiles;
+    } else {
+      mt = local / n_tiles;
+      nt = local - mt * n_tiles;
+    }
+    m0 = mt * BG_BM;
+    rows = min(BG_BM, M - m0);
+    n0 = nt * BG_BN;
+    const int kb = offsets[g];
+    nk = (offsets[g + 1] - kb) / BK;
+    ares = make_rsrc(A, (uint32_t)(M * lda * 2));
+    wres = make_rsrc(W, (uint32_t)(n_out * ldb * 2));
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int blk = wave * IPW + i;
+      const int r = blk * RPI + lane / NCH;
+      const int c = (lane % NCH) ^ swz(r);
+      agoff[i] = r < rows ? (uint32_t)(((int64_t)(m0 + r) * lda + kb) * 2) + (uint32_t)c * 16u : kOob;
+      bgoff[i] = n0 + r < n_out ? (uint32_t)(((int64_t)(n0 + r) * ldb + kb) * 2) + (uint32_t)c * 16u : kOob;
+    }
+    obase = out + (size_t)g * M * n_out;
+    ostride = n_out;
   }
-  const int nk = K / BK;
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
     const uint32_t kc = (uint32_t)kt * (BK * 2);
@@ -305,7 +347,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
         } else {
           v = acc[i][j][r];
         }
-        store_out(out + (size_t)(m0 + row) * n_out + col, v);
+        store_out(obase + (size_t)(m0 + row) * ostride + col, v);
       }
     }
   }
@@ -322,7 +364,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles);
+                     n_tiles, (int64_t)0, (int64_t)0, 0);
   return hipGetLastError();
 }
 
@@ -331,6 +373,25 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_t
   if (a.swiglu) return launch_big<true, 4, 4, true>(a, rows_total_max, s);
   return a.out_f32 ? launch_big<false, 4, 4, true, 32, float>(a, rows_total_max, s)
                    : launch_big<false, 4, 4, true>(a, rows_total_max, s);
+}
+
+// Weight gradients: out[g][m][n] = sum over k in [koff[g], koff[g+1]) of AT[m][k] BT[n][k],
+// group ranges multiples of 32; an empty group writes zeros.
+hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
+                            int N, bool out_f32, void *out, hipStream_t s) {
+  const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
+  const int64_t grid = (int64_t)G * m_tiles * n_tiles;
+  if (out_f32)
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, float, true>), dim3((unsigned)grid), dim3(512),
+                       0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
+                       static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<float *>(out), n_tiles, lda,
+                       ldb, M);
+  else
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true>), dim3((unsigned)grid),
+                       dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
+                       static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
+                       ldb, M);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -84,13 +84,12 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, int T, in
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v0, int32_t step, hipStream_t s);
 
 // ---- backward (backward.hip); bf16 activations and weights
-// out[b][c][pos(r)] = in[b][src(r)][c]: src(r) = row_index[r] or r; pos(r) = r, or with
-// group offsets off/poff (G groups) the row's place in the padded layout; rows past
-// *rows_dev (when given) are skipped.
+// out[b][c][p] = in[b][src(p)][c] for p < P (zero where p has no source): src(p) = p for
+// p < rows, or with group offsets off / poff (G groups) row off[g] + (p - poff[g]) inside
+// group g's rows (through row_index when given) and zero in its padding.
 hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
-                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G,
-                                 const int32_t *rows_dev, void *out, int64_t out_ld, int64_t out_stride_b,
-                                 hipStream_t s);
+                                 const int32_t *row_index, const int32_t *off, const int32_t *poff, int G, int64_t P,
+                                 void *out, int64_t out_ld, int64_t out_stride_b, hipStream_t s);
 // poff[g] = sum over g' < g of ceil32(off[g'+1] - off[g']), poff[G] = total
 hipError_t launch_pad_offsets(const int32_t *off, int G, int32_t *poff, hipStream_t s);
 hipError_t launch_fill_u32(void *p, int64_t n_words, uint32_t v, hipStream_t s);
@@ -104,6 +103,9 @@ hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float 
 hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
                             int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
 // out[g][m][n] = sum_{k in [poff[g], poff[g+1])} AT[m][k] BT[n][k]; ranges multiples of 32
+// (gemm_big.hip: 256 x 256 tiles; backward.hip: 64 x 64 tiles for short ranges)
+hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
+                            int N, bool out_f32, void *out, hipStream_t s);
 hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
                         int N, bool out_f32, void *out, hipStream_t s);
 
