@@ -111,7 +111,7 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
   size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, hidden, y_perm, sh_hidden,
-      sh_out, sh_offsets, total;
+      sh_out, sh_offsets, router_part, total;
 };
 
 bool rerouting(const moe_desc &D) { return D.overflow == MOE_OVERFLOW_REROUTE && D.capacity != MOE_NO_CAPACITY; }
@@ -143,6 +143,7 @@ Layout layout(const moe_desc &D) {
   L.sh_hidden = take(fs ? T * fs * s : 0);
   L.sh_out = take(fs ? T * d * s : 0);
   L.sh_offsets = take(fs ? 2 * 4 : 0);
+  L.router_part = take(D.dtype == MOE_DTYPE_BF16 ? moe::router_partials_bytes((int)T, (int)d, (int)E) : 0);
   L.total = o;
   return L;
 }
@@ -497,26 +498,31 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
   const int64_t rmax = max_rows(D);
   void *y_perm = at<void>(ws, L.y_perm);
 
-  if (bf)
-    MOE_TRY_HIP(moe::launch_router_logits_bf16(x, weights->w_router, logit_offset, logits, T, d, E, stream),
-                "router logits");
-  else
+  if (!bf)
     MOE_TRY_HIP(moe::launch_router_logits_f32(static_cast<const float *>(x),
                                               static_cast<const float *>(weights->w_router), logit_offset, logits, T,
                                               d, E, stream),
                 "router logits");
+  // router linear + top-k (+ the next k ranks when redirecting overflow)
+  auto router = [&](int32_t *spare) -> moe_status {
+    if (bf)
+      return hip_status(moe::launch_router_bf16(x, weights->w_router, logit_offset, logits, T, d, E, k, ids, gates,
+                                                spare, at<float>(ws, L.router_part), stream),
+                        "router");
+    return hip_status(moe::launch_router_topk(logits, T, E, k, ids, gates, stream, spare), "router top-k");
+  };
   const bool rank_major = D.fill_order == MOE_FILL_RANK_MAJOR;
   const int32_t *serving = ids;  // expert of each assignment, as the combine reads it
   if (rerouting(D)) {
     int32_t *spare = at<int32_t>(ws, L.spare);
     int32_t *assigned = R.assigned_ids ? R.assigned_ids : at<int32_t>(ws, L.assigned);
-    MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream, spare), "router top-k");
+    MOE_TRY(router(spare));
     MOE_TRY_HIP(moe::launch_dispatch_reroute(ids, spare, T, k, E, D.capacity, rank_major, counts, offsets, slot,
                                              assigned, row_token, at<int32_t>(ws, L.hist), stream),
                 "dispatch with redirection");
     serving = assigned;
   } else {
-    MOE_TRY_HIP(moe::launch_router_topk(logits, T, E, k, ids, gates, stream), "router top-k");
+    MOE_TRY(router(nullptr));
     MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, rank_major, counts, offsets, slot, row_token,
                                      at<int32_t>(ws, L.hist), stream),
                 "dispatch");

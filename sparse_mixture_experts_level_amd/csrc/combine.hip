@@ -13,95 +13,104 @@ namespace moe {
 
 namespace {
 
-constexpr int CB_TOK = 4;  // tokens per workgroup, one wavefront each
-constexpr int CB_U = 4;    // 16-byte vectors per lane per pass
+constexpr int CB_TOK = 4;  // wavefronts per workgroup
 
-// One wavefront per token.  Lanes j < k fetch assignment j's slot, expert and gate in
-// parallel and resolve its row; the wave then streams the row vectors, each lane
-// summing its columns over j in order.
-template <bool BF16>
+// One wavefront per (token, column segment of 64 * U 16-byte vectors).  Lanes j < k
+// fetch assignment j's slot, expert and gate in parallel and resolve its row; the wave
+// then loads JU rows' vectors at a time (more loads in flight) and each lane sums its
+// columns over j in order, so the result does not depend on the segmentation.
+template <bool BF16, int U, int JU>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ gates,
                                                       const int32_t *__restrict__ slot,
                                                       const int32_t *__restrict__ offsets,
                                                       const void *__restrict__ shared, void *__restrict__ out, int T,
-                                                      int d, int k, int e_begin, int e_end) {
+                                                      int d, int k, int e_begin, int e_end, int nseg) {
   constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * CB_TOK + (threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * CB_TOK + (threadIdx.x >> 6);
+  const int t = (int)(gw / nseg);
   if (t >= T) return;
+  const int v0 = (int)(gw - (int64_t)t * nseg) * 64 * U;
   const int nvec = d / VEC;
   const size_t es = BF16 ? 2 : 4;
   const uint8_t *yb = static_cast<const uint8_t *>(y_perm);
-  for (int v0 = 0; v0 < nvec; v0 += 64 * CB_U) {
-    float acc[CB_U][VEC];
+  auto unpack = [&](const u32x4 &q, float *o) {
 #pragma unroll
-    for (int u = 0; u < CB_U; ++u) {
-      const int c = v0 + lane + 64 * u;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
-      if (shared && c < nvec) {
-        const u32x4 q = ldg16(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (BF16) {
-            acc[u][2 * i] = __uint_as_float(q[i] << 16);
-            acc[u][2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
-          } else {
-            acc[u][i] = __uint_as_float(q[i]);
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BF16) {
+        o[2 * i] = __uint_as_float(q[i] << 16);
+        o[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+      } else {
+        o[i] = __uint_as_float(q[i]);
       }
     }
-    for (int j0 = 0; j0 < k; j0 += 64) {
-      // lane j holds assignment j0 + j: its row (or -1) and gate
-      int64_t my_row = -1;
-      float my_gate = 0.f;
-      if (j0 + lane < k) {
-        const size_t q = (size_t)t * k + j0 + lane;
-        const int sl = slot[q];
-        const int e = ids[q];
-        my_gate = gates[q];
-        if (sl >= 0 && e >= e_begin && e < e_end) my_row = (int64_t)offsets[e] + sl;
-      }
-      const int kn = min(64, k - j0);
-      for (int j = 0; j < kn; ++j) {
-        const int64_t row = __shfl(my_row, j, 64);
-        const float gj = __shfl(my_gate, j, 64);
-        if (row < 0) continue;
-        const uint8_t *yr = yb + (size_t)row * d * es;
+  };
+  float acc[U][VEC];
 #pragma unroll
-        for (int u = 0; u < CB_U; ++u) {
+  for (int u = 0; u < U; ++u) {
+    const int c = v0 + lane + 64 * u;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
+    if (shared && c < nvec)
+      unpack(ldg16(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es), acc[u]);
+  }
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    // lane j holds assignment j0 + j: its row (or -1) and gate
+    int64_t my_row = -1;
+    float my_gate = 0.f;
+    if (j0 + lane < k) {
+      const size_t q = (size_t)t * k + j0 + lane;
+      const int sl = slot[q];
+      const int e = ids[q];
+      my_gate = gates[q];
+      if (sl >= 0 && e >= e_begin && e < e_end) my_row = (int64_t)offsets[e] + sl;
+    }
+    const int kn = min(64, k - j0);
+    for (int j1 = 0; j1 < kn; j1 += JU) {
+      u32x4 q[JU][U];
+      float gj[JU];
+      bool live[JU];
+#pragma unroll
+      for (int jj = 0; jj < JU; ++jj) {
+        const int j = j1 + jj;
+        const int64_t row = __shfl(my_row, j < kn ? j : 0, 64);
+        gj[jj] = __shfl(my_gate, j < kn ? j : 0, 64);
+        live[jj] = j < kn && row >= 0;
+        const uint8_t *yr = yb + (size_t)(live[jj] ? row : 0) * d * es;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
           const int c = v0 + lane + 64 * u;
-          if (c >= nvec) continue;
-          const u32x4 q = ldg16(yr + (size_t)c * VEC * es);
+          q[jj][u] = (live[jj] && c < nvec) ? ldg16(yr + (size_t)c * VEC * es) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (BF16) {
-              acc[u][2 * i] = fmaf(gj, __uint_as_float(q[i] << 16), acc[u][2 * i]);
-              acc[u][2 * i + 1] = fmaf(gj, __uint_as_float(q[i] & 0xffff0000u), acc[u][2 * i + 1]);
-            } else {
-              acc[u][i] = fmaf(gj, __uint_as_float(q[i]), acc[u][i]);
-            }
-          }
+      for (int jj = 0; jj < JU; ++jj) {
+        if (!live[jj]) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float v[VEC];
+          unpack(q[jj][u], v);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[u][i] = fmaf(gj[jj], v[i], acc[u][i]);
         }
       }
     }
+  }
 #pragma unroll
-    for (int u = 0; u < CB_U; ++u) {
-      const int c = v0 + lane + 64 * u;
-      if (c >= nvec) continue;
-      u32x4 q;
+  for (int u = 0; u < U; ++u) {
+    const int c = v0 + lane + 64 * u;
+    if (c >= nvec) continue;
+    u32x4 q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (BF16) {
-          q[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
-        } else {
-          q[i] = __float_as_uint(acc[u][i]);
-        }
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BF16) {
+        q[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
+      } else {
+        q[i] = __float_as_uint(acc[u][i]);
       }
-      stg16(static_cast<uint8_t *>(out) + ((size_t)t * d + (size_t)c * VEC) * es, q);
     }
+    stg16(static_cast<uint8_t *>(out) + ((size_t)t * d + (size_t)c * VEC) * es, q);
   }
 }
 
@@ -140,13 +149,30 @@ hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *g
                           hipStream_t s, int e_begin, int e_end) {
   const int vec = bf16 ? 8 : 4;
   if (d % vec == 0) {
-    const int grid = (T + CB_TOK - 1) / CB_TOK;
-    if (bf16)
-      hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, T, d, k, e_begin, e_end);
-    else
-      hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, s, y_perm, ids, gates, slot, offsets, shared,
-                         out, T, d, k, e_begin, e_end);
+    // Wide segments (up to 4 vectors per lane, no more than a row holds) when there are
+    // tokens enough to fill the GPU, else one vector per lane and more wavefronts per
+    // token; rows fetched four at a time when a token has several.
+    const int nvec = d / vec;
+    const bool wide = (int64_t)T * ((nvec + 255) / 256) >= 4096;
+    const int U = !wide ? 1 : nvec >= 256 ? 4 : nvec >= 128 ? 2 : 1;
+    const int nseg = (nvec + 64 * U - 1) / (64 * U);
+    const int64_t grid = ((int64_t)T * nseg + CB_TOK - 1) / CB_TOK;
+#define CB_LAUNCH(B, UU, J)                                                                                        \
+  hipLaunchKernelGGL((combine_kernel<B, UU, J>), dim3((unsigned)grid), dim3(256), 0, s, y_perm, ids, gates, slot,     \
+                     offsets, shared, out, T, d, k, e_begin, e_end, nseg)
+#define CB_U(B, J)                      \
+  do {                                  \
+    if (U == 4) CB_LAUNCH(B, 4, J);     \
+    else if (U == 2) CB_LAUNCH(B, 2, J); \
+    else CB_LAUNCH(B, 1, J);            \
+  } while (0)
+    if (bf16) {
+      if (k == 1) CB_U(true, 1); else CB_U(true, 4);
+    } else {
+      if (k == 1) CB_U(false, 1); else CB_U(false, 4);
+    }
+#undef CB_U
+#undef CB_LAUNCH
   } else {
     if (bf16) return hipErrorInvalidValue;  // bf16 rows are validated to be multiples of 64
     hipLaunchKernelGGL(combine_f32_scalar_kernel, dim3(T), dim3(256), 0, s, static_cast<const float *>(y_perm), ids,

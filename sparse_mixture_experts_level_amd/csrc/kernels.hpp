@@ -14,6 +14,14 @@ hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const 
                                      int T, int d, int E, hipStream_t s);
 hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits,
                                     int T, int d, int E, hipStream_t s);
+// Router linear and top-k in one call for bf16 layers; with few tokens the linear is
+// split over d into router_splits() parts whose partial sums (router_partials_bytes()
+// of workspace) the top-k kernel adds in order.
+int router_splits(int T, int d, int E);
+size_t router_partials_bytes(int T, int d, int E);
+hipError_t launch_router_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T, int d,
+                              int E, int k, int32_t *ids, float *gates, int32_t *spare, float *partials,
+                              hipStream_t s);
 // ids / gates may be NULL (not written).  With `spare`, also writes the experts ranked
 // k .. 2k-1 per token into spare [T, k] (-1 where the rank is >= E).
 hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s,

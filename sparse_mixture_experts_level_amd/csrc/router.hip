@@ -1,6 +1,8 @@
 // Router of the sparse MoE layer on gfx950: bias-free linear (logits), then softmax,
 // top-k and renormalised gates ("Sparse Mixture-of-Experts", bigdataschool.ru wiki,
 // section "Роутер и top-k gating").
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,12 +22,15 @@ constexpr int RT_TOK = 64;   // tokens per workgroup
 constexpr int RT_KC = 64;    // d values per LDS stage (8 x 16-byte chunks per row)
 constexpr int RT_EMAX = 256; // experts per pass
 
+// Split over d (few tokens, long rows): workgroup (blockIdx.x, blockIdx.y) covers the
+// chunks [y * cps, (y + 1) * cps) of d and writes its partial sums (without the offset)
+// to partials[y][T][E]; the top-k kernel adds the splits in order.
 template <int NSUB>  // 16-expert subtiles per pass
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *__restrict__ x,
                                                                  const bf16_t *__restrict__ w,
                                                                  const float *__restrict__ offset,
                                                                  float *__restrict__ logits, int T, int d, int E,
-                                                                 int e_base) {
+                                                                 int e_base, int cps, float *__restrict__ partials) {
   constexpr int EC = NSUB * 16;
   constexpr int P = 4;  // chunks in flight
   constexpr int PER_T = (EC * 8 + 255) / 256;
@@ -49,10 +54,11 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *_
     u32x4 w[PER_T];
   };
   Slot slot[P];
-  const int nk = d / RT_KC;
+  const int kb = partials ? blockIdx.y * cps : 0;
+  const int nk = partials ? min(cps, d / RT_KC - kb) : d / RT_KC;  // chunks of this workgroup
   auto issue = [&](Slot &sl, int it) {
     const bool ok = it < nk;
-    const uint32_t kc = (uint32_t)it * (RT_KC * 2);
+    const uint32_t kc = (uint32_t)(kb + it) * (RT_KC * 2);
     sl.a[0] = buf_ld16(xres, ok ? xoff + kc : kOob);
     sl.a[1] = buf_ld16(xres, ok ? xoff + 64u + kc : kOob);
 #pragma unroll
@@ -104,11 +110,12 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *_
   for (int n = 0; n < NSUB; ++n) {
     const int e = e_base + n * 16 + (lane & 15);
     if (e >= E) continue;
-    const float off = offset ? offset[e] : 0.f;
+    const float off = offset && !partials ? offset[e] : 0.f;
+    float *dst = partials ? partials + (size_t)blockIdx.y * T * E : logits;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + (lane >> 4) * 4 + i;
-      if (t < T) logits[(size_t)t * E + e] = acc[n][i] + off;
+      if (t < T) dst[(size_t)t * E + e] = acc[n][i] + off;
     }
   }
 }
@@ -164,19 +171,33 @@ constexpr int TK_WAVES = 4;
 // slot j / 64 and writes it at the end.  No LDS and no barriers.  With `spare`, the
 // selection goes on for k more rounds (the experts ranked k .. 2k-1, used to redirect
 // overflowing assignments) without gates.
+// With `partials` (S splits of the router linear), the logits are first formed as the
+// splits' sum in order s = 0..S-1 plus the offset, and written to `logits`.
 template <int VPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void router_topk_kernel(float *__restrict__ logits, int T, int E, int k,
                                                           int32_t *__restrict__ ids, float *__restrict__ gates,
-                                                          int32_t *__restrict__ spare) {
+                                                          int32_t *__restrict__ spare,
+                                                          const float *__restrict__ partials, int S,
+                                                          const float *__restrict__ offset) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * TK_WAVES + wave;
   if (t >= T) return;
-  const float *row = logits + (size_t)t * E;
+  float *row = logits + (size_t)t * E;
   uint64_t key[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = lane + 64 * v;
-    key[v] = e < E ? topk_key(row[e], e) : 0ull;  // 0 ranks below every real key
+    float val = 0.f;
+    if (e < E) {
+      if (partials) {
+        for (int sp = 0; sp < S; ++sp) val += partials[((size_t)sp * T + t) * E + e];
+        if (offset) val += offset[e];
+        row[e] = val;
+      } else {
+        val = row[e];
+      }
+    }
+    key[v] = e < E ? topk_key(val, e) : 0ull;  // 0 ranks below every real key
   }
   int my_id[VPL], my_sp[VPL];
   float my_z[VPL];
@@ -232,9 +253,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 
 }  // namespace
 
-hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T,
-                                     int d, int E, hipStream_t s) {
+namespace {
+
+hipError_t router_logits_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T, int d,
+                              int E, int splits, float *partials, hipStream_t s) {
   const int grid = (T + RT_TOK - 1) / RT_TOK;
+  const int nk = d / RT_KC;
+  const int cps = (nk + splits - 1) / splits;
   for (int e0 = 0; e0 < E; e0 += RT_EMAX) {
     const int ec = min(RT_EMAX, E - e0);
     const int nsub = (ec + 15) / 16;
@@ -242,8 +267,8 @@ hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const 
     const bf16_t *wp = static_cast<const bf16_t *>(w_router);
 #define RT_CASE(N)                                                                                      \
   case N:                                                                                               \
-    hipLaunchKernelGGL(router_logits_bf16_kernel<N>, dim3(grid), dim3(256), 0, s, xp, wp, offset, logits, \
-                       T, d, E, e0);                                                                    \
+    hipLaunchKernelGGL(router_logits_bf16_kernel<N>, dim3(grid, splits), dim3(256), 0, s, xp, wp, offset,    \
+                       logits, T, d, E, e0, cps, partials);                                             \
     break;
     switch (nsub <= 1 ? 1 : nsub <= 2 ? 2 : nsub <= 4 ? 4 : nsub <= 8 ? 8 : 16) {
       RT_CASE(1)
@@ -259,21 +284,14 @@ hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const 
   return hipSuccess;
 }
 
-hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits, int T,
-                                    int d, int E, hipStream_t s) {
-  const int64_t n = (int64_t)T * E;
-  const int grid = int((n + 255) / 256);
-  hipLaunchKernelGGL(router_logits_f32_kernel, dim3(grid), dim3(256), 0, s, x, w_router, offset, logits, T, d, E);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s,
-                              int32_t *spare) {
+hipError_t router_topk(float *logits, int T, int E, int k, int32_t *ids, float *gates, int32_t *spare,
+                       const float *partials, int S, const float *offset, hipStream_t s) {
   const int grid = (T + TK_WAVES - 1) / TK_WAVES;
   const int vpl = (E + 63) / 64;
-#define TK_CASE(V)                                                                                          \
-  case V:                                                                                                   \
-    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates, spare); \
+#define TK_CASE(V)                                                                                             \
+  case V:                                                                                                      \
+    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates, spare, \
+                       partials, S, offset);                                                                   \
     break;
   switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
     TK_CASE(1)
@@ -284,6 +302,55 @@ hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t 
   }
 #undef TK_CASE
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_logits_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T,
+                                     int d, int E, hipStream_t s) {
+  return router_logits_bf16(x, w_router, offset, logits, T, d, E, 1, nullptr, s);
+}
+
+// Splits of d for the router linear: enough workgroups to fill the GPU when the tokens
+// are few, at least two chunks of 64 per split, at most 8 splits and 64 MiB of partials.
+int router_splits(int T, int d, int E) {
+  const int64_t base = (int64_t)((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EMAX - 1) / RT_EMAX);
+  int S = base >= 256 ? 1 : (int)std::min<int64_t>(8, 256 / std::max<int64_t>(base, 1));
+  S = std::max(1, std::min(S, (d / RT_KC) / 2));
+  while (S > 1 && (int64_t)S * T * E * 4 > ((int64_t)64 << 20)) S /= 2;
+  return S;
+}
+
+size_t router_partials_bytes(int T, int d, int E) {
+  const int S = router_splits(T, d, E);
+  return S > 1 ? (size_t)S * T * E * 4 : 0;
+}
+
+hipError_t launch_router_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T, int d,
+                              int E, int k, int32_t *ids, float *gates, int32_t *spare, float *partials,
+                              hipStream_t s) {
+  const int S = router_splits(T, d, E);
+  if (S == 1) {
+    hipError_t e = router_logits_bf16(x, w_router, offset, logits, T, d, E, 1, nullptr, s);
+    if (e != hipSuccess) return e;
+    return router_topk(logits, T, E, k, ids, gates, spare, nullptr, 1, nullptr, s);
+  }
+  hipError_t e = router_logits_bf16(x, w_router, offset, logits, T, d, E, S, partials, s);
+  if (e != hipSuccess) return e;
+  return router_topk(logits, T, E, k, ids, gates, spare, partials, S, offset, s);
+}
+
+hipError_t launch_router_logits_f32(const float *x, const float *w_router, const float *offset, float *logits, int T,
+                                    int d, int E, hipStream_t s) {
+  const int64_t n = (int64_t)T * E;
+  const int grid = int((n + 255) / 256);
+  hipLaunchKernelGGL(router_logits_f32_kernel, dim3(grid), dim3(256), 0, s, x, w_router, offset, logits, T, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *gates, hipStream_t s,
+                              int32_t *spare) {
+  return router_topk(const_cast<float *>(logits), T, E, k, ids, gates, spare, nullptr, 1, nullptr, s);
 }
 
 }  // namespace moe
