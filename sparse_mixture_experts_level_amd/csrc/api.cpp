@@ -99,6 +99,14 @@ int64_t max_rows(const moe_desc &D) {
   return std::min<int64_t>(tk, (int64_t)D.num_experts * D.capacity);
 }
 
+// Workspace of float partials for K splits of the down projection: layers of few
+// experts (large groups, large-tile regime), where one rank's share of expert
+// parallelism can leave a handful of tiles.
+size_t down_split_bytes(const moe_desc &D) {
+  if (D.dtype != MOE_DTYPE_BF16 || D.num_experts > 16) return 0;
+  return (size_t)4 * max_rows(D) * D.d_model * 4;
+}
+
 // Largest number of rows any one expert can hold: min(T, C).
 int32_t group_rows_bound(const moe_desc &D) {
   if (D.capacity == MOE_NO_CAPACITY) return D.num_tokens;
@@ -111,7 +119,7 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
   size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, hidden, y_perm, sh_hidden,
-      sh_out, sh_offsets, router_part, total;
+      sh_out, sh_offsets, router_part, down_split, total;
 };
 
 bool rerouting(const moe_desc &D) { return D.overflow == MOE_OVERFLOW_REROUTE && D.capacity != MOE_NO_CAPACITY; }
@@ -144,6 +152,7 @@ Layout layout(const moe_desc &D) {
   L.sh_out = take(fs ? T * d * s : 0);
   L.sh_offsets = take(fs ? 2 * 4 : 0);
   L.router_part = take(D.dtype == MOE_DTYPE_BF16 ? moe::router_partials_bytes((int)T, (int)d, (int)E) : 0);
+  L.down_split = take(down_split_bytes(D));
   L.total = o;
   return L;
 }
@@ -189,14 +198,16 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
-                           int64_t x_row_count = 0) {
+                           int64_t x_row_count = 0, float *split_ws = nullptr) {
   MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true,
                                          row_index, x_row_count),
                          dtype, s, "gate_up grouped GEMM"));
-  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false),
-                         dtype, s, "down grouped GEMM"));
+  moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false);
+  down.split_ws = split_ws;  // lets the large-tile kernel cut few tiles along K
+  MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
   return MOE_OK;
 }
+
 
 }  // namespace
 
@@ -536,7 +547,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
     // [e_begin, e_end] of the offsets (rows stay in the whole layer's row space)
     MOE_TRY(run_grouped_ffn(e_end - e_begin, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x,
                             offsets + e_begin, weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden),
-                            stream, row_token, T));
+                            stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr));
   }
   const void *shared = nullptr;
   if (fs > 0 && add_shared) {

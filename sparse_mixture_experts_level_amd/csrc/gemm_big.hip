@@ -17,6 +17,8 @@
 // A block finds its group from the offsets (one wavefront scan), and walks the
 // group's tiles with the larger operand outermost, so the smaller one is reused
 // from cache.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +43,55 @@ constexpr int BG_BM = 256, BG_BN = 256;
 //
 // WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
 // 4: eight waves of 128 x 64, two per SIMD).
+// K splits for a launch with `tiles` output tiles and `steps` 32-wide K steps, for
+// launches of fewer tiles than CUs: the split count (at most 4, at least 64 steps per
+// split) whose blocks fill the 256 CUs' last round best, the larger one on a tie.
+// Evaluated identically by the GEMM and by the reduction that adds the splits.
+__host__ __device__ __forceinline__ int big_ksplit(int tiles, int steps) {
+  if (tiles <= 0 || tiles >= 256) return 1;
+  int best = 1;
+  float best_fill = 0.f;
+  for (int s = 1; s <= 4; ++s) {
+    if (s > 1 && steps / s < 64) break;
+    const int blocks = tiles * s;
+    const float fill = (float)blocks / (float)(((blocks + 255) / 256) * 256);
+    if (fill >= best_fill) {
+      best_fill = fill;
+      best = s;
+    }
+  }
+  return best;
+}
+
+// Sum of the K splits' float partials in order, rounded to bf16, for the rows below
+// offsets[G]; nothing to do when the launch was not split.
+__global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__restrict__ part, int64_t stride,
+                                                               const int32_t *__restrict__ offsets, int G,
+                                                               int n_tiles, int steps, int n_out,
+                                                               bf16_t *__restrict__ out) {
+  const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+  const int ks = big_ksplit(tiles, steps);
+  if (ks == 1) return;
+  const int64_t rows = offsets[G];
+  const int64_t n8 = rows * n_out / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ks; ++s) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(part + s * stride + i * 8);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(part + s * stride + i * 8 + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] += a[q];
+        acc[4 + q] += b[q];
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    stg16(out + i * 8, o);
+  }
+}
+
 // WG: the weight-gradient form, grouped over the contraction instead of the rows:
 //   out[g][m][n] = sum over k in [offsets[g], offsets[g+1]) of A[m][k] * W[n][k],
 // A [M, lda] and W [n_out, ldb] (both K-contiguous, e.g. transposed activations whose
@@ -53,7 +104,9 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
                                                                          const bf16_t *__restrict__ W,
                                                                          int64_t wstride, int n_out, int K,
                                                                          OutT *__restrict__ out, int n_tiles,
-                                                                         int64_t lda, int64_t ldb, int M) {
+                                                                         int64_t lda, int64_t ldb, int M,
+                                                                         float *__restrict__ split_out,
+                                                                         int64_t split_stride) {
   constexpr int BK = BKP;                        // K per step: 32 or 64
   constexpr int RB = BK * 2;                     // bytes per tile row
   constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
@@ -81,7 +134,8 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto swz = [&](int r) -> int { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
-  int m0, rows, n0, nk;
+  int m0, rows, n0, nk, ks = 0, kbase = 0;
+  bool partial = false;
   rsrc_t ares, wres;
   OutT *obase;
   int64_t ostride;
@@ -90,9 +144,15 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     // and the real tiles are spread over the XCDs by the remap over their own count (a
     // remap over the whole grid would crowd them onto the first XCDs when the bound is
     // loose).
-    const int real_blocks = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+    // With split_out, few tiles are cut along K as well (big_ksplit()): split ks writes
+    // its float partial sums to split_out + ks * split_stride, and a reduction adds them.
+    const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+    const int ksplit = split_out ? big_ksplit(tiles, K / BK) : 1;
+    const int real_blocks = tiles * ksplit;
     if ((int)blockIdx.x >= real_blocks) return;
-    const int lin = xcd_remap(blockIdx.x, real_blocks);
+    const int lin0 = xcd_remap(blockIdx.x, real_blocks);
+    ks = lin0 / tiles;
+    const int lin = lin0 - ks * tiles;
     const int m_lin = lin / n_tiles;  // rank of this block's tile among all groups' m tiles
     int g, mt_first, mt_count;
     // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
@@ -141,7 +201,10 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
       }
       bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
     }
-    nk = K / BK;
+    const int steps = K / BK, sps = (steps + ksplit - 1) / ksplit;
+    kbase = ks * sps;
+    nk = max(0, min(sps, steps - kbase));
+    partial = ksplit > 1;
     obase = out;
     ostride = n_out;
   } else {
@@ -179,7 +242,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   }
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
-    const uint32_t kc = (uint32_t)kt * (BK * 2);
+    const uint32_t kc = (uint32_t)(kbase + kt) * (BK * 2);
     uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -347,7 +410,10 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
         } else {
           v = acc[i][j][r];
         }
-        store_out(obase + (size_t)(m0 + row) * ostride + col, v);
+        if (partial)
+          split_out[(size_t)ks * split_stride + (size_t)(m0 + row) * ostride + col] = v;
+        else
+          store_out(obase + (size_t)(m0 + row) * ostride + col, v);
       }
     }
   }
@@ -360,11 +426,20 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
-  const int64_t grid = m_tiles * n_tiles;
+  // K splits only for a plain bf16 store with a workspace for the partials
+  float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
+  const int64_t split_stride = rows_total_max * a.n_out;
+  const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
   hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles, (int64_t)0, (int64_t)0, 0);
+                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const int64_t blocks = std::min<int64_t>((rows_total_max * a.n_out / 8 + 255) / 256, 4096);
+  hipLaunchKernelGGL(big_split_reduce_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, split,
+                     split_stride, a.offsets, a.num_groups, n_tiles, a.K / BKP, a.n_out,
+                     static_cast<bf16_t *>(a.out));
   return hipGetLastError();
 }
 
@@ -385,12 +460,12 @@ hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, float, true>), dim3((unsigned)grid), dim3(512),
                        0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<float *>(out), n_tiles, lda,
-                       ldb, M);
+                       ldb, M, nullptr, (int64_t)0);
   else
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true>), dim3((unsigned)grid),
                        dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
-                       ldb, M);
+                       ldb, M, nullptr, (int64_t)0);
   return hipGetLastError();
 }
 

@@ -72,6 +72,9 @@ struct GroupedGemmArgs {
   void *out;
   bool swiglu;
   bool out_f32 = false;  // float output instead of the element type (bf16 kernels, no SwiGLU)
+  // Workspace for float partial sums when the large-tile kernel cuts few tiles along K
+  // (4 * rows_max * n_out floats); NULL: no K split.
+  float *split_ws = nullptr;
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);

@@ -82,6 +82,7 @@ def _to_dev(inp):
     (513, 128, 16, 4, 128, None, 0, None),
     (200, 128, 8, 8, 64, None, 0, None),  # k = E without capacity: the dense mixture
     (64, 128, 4, 1, 64, 0.2, 64, "boost4"),  # heavy dropping with a shared expert
+    (600, 256, 2, 1, 4096, None, 0, None),   # large-tile regime with few tiles: down cut along K
 ])
 def test_small_bf16_layers_all_tokens(T, d, E, k, f, cf, fs, offset):
     w = wl.Workload("small", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset=offset)
@@ -148,6 +149,7 @@ def test_full_size_workloads(name, nsample):
     (300, 256, 8, 2, 192, 1.25, 64, 2),
     (513, 128, 16, 4, 128, None, 0, 4),
     (256, 128, 8, 1, 64, 1.0, 64, 8),   # one expert per rank
+    (1024, 256, 8, 2, 8192, None, 0, 8),  # one large expert per rank: down cut along K
 ])
 def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards):
     """Each rank's partial equals the layer with the other experts masked (the oracle with their
