@@ -743,12 +743,14 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   auto gemm = [&](const moe::GroupedGemmArgs &a, const char *what) {
     return hcall(moe::launch_grouped_gemm_bf16(a, stream), what);
   };
-  // weight-gradient GEMM: 256 x 256 tiles when the groups' contraction ranges are long,
-  // 64 x 64 tiles for short ones (few rows per expert)
+  // weight-gradient GEMM: 256 x 256 tiles on the LDS pipeline when the groups'
+  // contraction ranges are long (matrix-core bound), the write-bound 128 x 128 kernel for
+  // short ranges (few rows per expert) and for outputs under 256 rows or columns
   auto wgrad = [&](const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M, int N,
                    bool f32, void *out, int64_t avg_k) {
-    return avg_k >= 128 ? moe::launch_wgrad_big(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream)
-                        : moe::launch_wgrad(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream);
+    return avg_k >= 256 && M >= 256 && N >= 256
+               ? moe::launch_wgrad_big(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream)
+               : moe::launch_wgrad(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream);
   };
   int32_t *poff = at<int32_t>(ws, L.poff), *tpoff = at<int32_t>(ws, L.tpoff), *sh_off = at<int32_t>(ws, L.sh_off);
   MOE_TRY(hcall(moe::launch_fill_i32(tpoff, 2, 0, (int32_t)L.Tpad, stream), "offsets"));
@@ -850,8 +852,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                 "shared dGU transpose"));
     MOE_TRY(hcall(wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false, grads->dw_shared_down, T),
                 "dW_shared_down"));
-    MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false, grads->dw_shared_gate_up,
-                        T),
+    MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false, grads->dw_shared_gate_up, T),
                 "dW_shared_gate_up"));
     dxs = W(L.dxs);
   }

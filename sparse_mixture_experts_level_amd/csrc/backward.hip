@@ -23,11 +23,15 @@ namespace {
 
 constexpr int TR = 64;  // transpose tile
 
-// out[b][c][p] = in[b][src(p)][c] for every position p < P and c < cols (bf16), zero where
-// p has no source row.  Plain: src(p) = p for p < rows.  Grouped (off / poff, G groups):
-// position p of group g (poff[g] <= p < poff[g+1]) holds row off[g] + (p - poff[g]) while
-// that row belongs to the group, through row_index when given, and zero in the group's
-// padding.  64 x 64 tiles through LDS, 16-byte loads and stores; cols and P multiples of 8.
+// Plain: out[b][c][p] = in[b][p][c] for p < P and c < cols (bf16), zero for p >= rows,
+// row stride out_ld.  Grouped (off / poff, G groups; batch 1): position p of group g
+// (poff[g] <= p < poff[g+1]) holds row off[g] + (p - poff[g]) while that row belongs to the
+// group (through row_index when given), zero in the group's padding, and the output is
+// group-major -- group g's [cols, K_g] block (K_g = poff[g+1] - poff[g]) at element
+// poff[g] * cols, row stride K_g -- so that each group's operand of the weight-gradient
+// GEMM is one contiguous block; positions past poff[G] are not written.  64 x 64 tiles
+// through LDS, 16-byte loads and stores; cols and P multiples of 8, group sizes multiples
+// of 8.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t *__restrict__ in, int64_t in_stride_b,
                                                              int64_t rows, int cols,
                                                              const int32_t *__restrict__ row_index,
@@ -73,11 +77,25 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t *__res
   for (int j = 0; j < 2; ++j) {
     const int v = tid + 256 * j;
     const int cl = v >> 3, pv = (v & 7) * 8;
-    if (c0 + cl >= cols || p0 + pv >= P) continue;
+    const int64_t p = p0 + pv;
+    if (c0 + cl >= cols || p >= P) continue;
+    int64_t o_idx;
+    if (!off) {
+      o_idx = (int64_t)(c0 + cl) * out_ld + p;
+    } else {
+      if (p >= poff[G]) continue;
+      int lo = 0, hi = G;  // largest g with poff[g] <= p
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (poff[mid] <= p) lo = mid; else hi = mid;
+      }
+      const int64_t kg = poff[lo + 1] - poff[lo];
+      o_idx = (int64_t)poff[lo] * cols + (int64_t)(c0 + cl) * kg + (p - poff[lo]);
+    }
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = uint32_t(tile[pv + 2 * q][cl]) | (uint32_t(tile[pv + 2 * q + 1][cl]) << 16);
-    stg16(dst + (size_t)(c0 + cl) * out_ld + p0 + pv, o);
+    stg16(dst + o_idx, o);
   }
 }
 
@@ -235,83 +253,133 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const bf16_t *__restrict
   }
 }
 
-// Weight-gradient GEMM grouped over the contraction: for group g,
-//   out[g][m][n] = sum over k in [poff[g], poff[g+1]) of AT[m][k] * BT[n][k]
-// AT [M, lda], BT [N, ldb] bf16, K-contiguous; group ranges are multiples of 32 (padding
-// columns hold zeros).  64 x 64 output tile per workgroup, 4 waves of 32 x 32
-// (2 x 2 16x16x32 MFMA subtiles), operands straight from memory into MFMA registers,
-// P chunks of 32 in flight.  Rows past M / columns past N read zeros and are not stored.
-// An empty group writes zeros.
+// Weight-gradient GEMM grouped over the contraction: for group g with K_g = poff[g+1] -
+// poff[g] (a multiple of 32; padding columns hold zeros),
+//   out[g][m][n] = sum over k < K_g of AT_g[m][k] * BT_g[n][k],
+// AT_g = AT + poff[g] * M and BT_g = BT + poff[g] * N, both K-contiguous with row stride
+// K_g (the group-major layout of the grouped transpose); lda, ldb bound the buffers
+// (M * lda and N * ldb elements).  Sized for short ranges (few rows per expert), where writing the
+// gradient is the cost: 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2
+// blocks of the 32x32x16 MFMA), operand fragments straight from memory into registers
+// (two 32-wide chunks in flight), and a register footprint that lets three workgroups
+// share a CU, so that one's loads overlap another's MFMAs and stores.  The BT fragment is
+// the MFMA's first operand, so a lane's accumulator holds four consecutive output
+// columns; the tile is staged through LDS and written as 16-byte runs.  Rows past M
+// read zeros and are not stored; N must be a multiple of 8.  An empty group writes zeros.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void wgrad_kernel(const bf16_t *__restrict__ AT, int64_t lda,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void wgrad_kernel(const bf16_t *__restrict__ AT, int64_t lda,
                                                     const bf16_t *__restrict__ BT, int64_t ldb,
                                                     const int32_t *__restrict__ poff, int M, int N, int m_tiles,
                                                     int n_tiles, void *__restrict__ out) {
-  constexpr int P = 4;
+  constexpr int ES = OUT_F32 ? 4 : 2;            // output element bytes
+  __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][64 * 64 * ES];
+  const int per_g = m_tiles * n_tiles;
+  // Tiles in launch order, dealt round-robin to the XCDs: groups' row counts are skewed,
+  // and contiguous ranges per XCD would leave the heavy groups on a few XCDs.
   const int tile = blockIdx.x;
-  const int g = tile / (m_tiles * n_tiles);
-  const int rem = tile - g * m_tiles * n_tiles;
+  const int g = tile / per_g;
+  const int rem = tile - g * per_g;
   const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = mt * 64 + (wave >> 1) * 32, n0 = nt * 64 + (wave & 1) * 32;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int m0 = mt * 128 + (wave >> 1) * 64, n0 = nt * 128 + (wave & 1) * 64;
   const int kb = poff[g], ke = poff[g + 1];
   const int nk = (ke - kb) / 32;
   const rsrc_t ares = make_rsrc(AT, (uint32_t)min<int64_t>((int64_t)M * lda * 2, 0x7fffffffLL));
   const rsrc_t bres = make_rsrc(BT, (uint32_t)min<int64_t>((int64_t)N * ldb * 2, 0x7fffffffLL));
+  // 32x32x16 operand fragment: lane holds row (lane & 31), k = 8 * (lane >> 5) .. + 7.
+  // Group g's operands are the contiguous blocks [M, K_g] at AT + kb * M and [N, K_g] at
+  // BT + kb * N (row stride K_g).
+  const int64_t kg = ke - kb;
   uint32_t ao[2], bo[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int m = m0 + i * 16 + (lane & 15), n = n0 + i * 16 + (lane & 15);
-    ao[i] = m < M ? (uint32_t)(((int64_t)m * lda + kb) * 2) + (uint32_t)(lane >> 4) * 16u : kOob;
-    bo[i] = n < N ? (uint32_t)(((int64_t)n * ldb + kb) * 2) + (uint32_t)(lane >> 4) * 16u : kOob;
+    const int m = m0 + i * 32 + lr, n = n0 + i * 32 + lr;
+    ao[i] = m < M ? (uint32_t)(((int64_t)kb * M + (int64_t)m * kg) * 2) + (uint32_t)lh * 16u : kOob;
+    bo[i] = n < N ? (uint32_t)(((int64_t)kb * N + (int64_t)n * kg) * 2) + (uint32_t)lh * 16u : kOob;
   }
-  f32x4 acc[2][2];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 fa[P][2], fb[P][2];
-  auto issue = [&](int s, int c) {
-    const bool ok = c < nk;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  // two 32-wide chunks in flight: the next chunk's loads overlap this chunk's MFMAs
+  u32x4 fa[2][2][2], fb[2][2][2];  // [stage][block][16-wide half of the chunk]
+  auto issue = [&](int st, int c) {
     const uint32_t kc = (uint32_t)c * 64u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      fa[s][i] = buf_ld16(ares, ok && ao[i] != kOob ? ao[i] + kc : kOob);
-      fb[s][i] = buf_ld16(bres, ok && bo[i] != kOob ? bo[i] + kc : kOob);
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fa[st][i][h] = buf_ld16(ares, ao[i] != kOob ? ao[i] + kc + h * 32u : kOob);
+        fb[st][i][h] = buf_ld16(bres, bo[i] != kOob ? bo[i] + kc + h * 32u : kOob);
+      }
   };
+  if (nk > 0) issue(0, 0);
+  for (int c0 = 0; c0 < nk; c0 += 2) {
 #pragma unroll
-  for (int s = 0; s < P - 1; ++s) issue(s, s);
-  for (int c0 = 0; c0 < nk; c0 += P) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) {
-      const int c = c0 + s;
+    for (int st = 0; st < 2; ++st) {
+      const int c = c0 + st;
       if (c >= nk) break;
-      issue((s + P - 1) % P, c + P - 1);
+      if (c + 1 < nk) issue(st ^ 1, c + 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(fa[s][i], fb[s][j], acc[i][j]);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[st][j][h], fa[st][i][h], acc[i][j]);
     }
   }
-  // C layout of the 16x16 MFMA: column (lane & 15), rows 4 * (lane >> 4) + q
+  // acc[i][j] element r: row m0 + i * 32 + (lane & 31), column n0 + j * 32 + 8 * (r / 4) +
+  // 4 * (lane / 32) + r % 4.  Each wave stages its 64 x 64 in its own LDS region.
+  uint8_t *stage = stage_all[wave];
   const size_t obase = (size_t)g * M * N;
+  if constexpr (OUT_F32) {
+    // 256-byte rows; 16-byte chunk c (4 columns) of row r at c ^ (r & 15)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 32 + lr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + j * 16 + (lane & 15);
-      if (n >= N) continue;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + i * 16 + (lane >> 4) * 4 + q;
-        if (m >= M) continue;
-        if constexpr (OUT_F32)
-          static_cast<float *>(out)[obase + (size_t)m * N + n] = acc[i][j][q];
-        else
-          static_cast<bf16_t *>(out)[obase + (size_t)m * N + n] = f32_to_bf16(acc[i][j][q]);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int c = j * 8 + q * 2 + lh;
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4)) = v;
+        }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane & 15, n = n0 + c * 4;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 4 + (lane >> 4), m = m0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+      if (m < M && n < N) stg16(static_cast<float *>(out) + obase + (size_t)m * N + n, v);
+    }
+  } else {
+    // 128-byte rows; 16-byte chunk c (8 columns) of row r at c ^ ((r >> 1) & 7)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<uint2 *>(stage + row * 128 + (((j * 4 + q) ^ ((row >> 1) & 7)) << 4) + lh * 8) = v;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int c = lane & 7, n = n0 + c * 8;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = it * 8 + (lane >> 3), m = m0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+      if (m < M && n < N) stg16(static_cast<bf16_t *>(out) + obase + (size_t)m * N + n, v);
+    }
+  }
 }
 
 }  // namespace
@@ -366,8 +434,11 @@ hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32
 
 hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
                         int N, bool out_f32, void *out, hipStream_t s) {
-  const int m_tiles = (M + 63) / 64, n_tiles = (N + 63) / 64;
+  if (N % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
+  const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_f32)
     hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT), lda,
                        static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out);

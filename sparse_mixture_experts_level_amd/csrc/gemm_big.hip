@@ -92,10 +92,12 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
   }
 }
 
-// WG: the weight-gradient form, grouped over the contraction instead of the rows:
-//   out[g][m][n] = sum over k in [offsets[g], offsets[g+1]) of A[m][k] * W[n][k],
-// A [M, lda] and W [n_out, ldb] (both K-contiguous, e.g. transposed activations whose
-// groups start on multiples of 32), every group M x n_out, written at out + g * M * n_out.
+// WG: the weight-gradient form, grouped over the contraction instead of the rows: with
+// K_g = offsets[g+1] - offsets[g] (a multiple of 32),
+//   out[g][m][n] = sum over k < K_g of A_g[m][k] * W_g[n][k],
+// A_g = A + offsets[g] * M and W_g = W + offsets[g] * n_out, K-contiguous with row stride
+// K_g (group-major transposed activations; lda and ldb bound the buffers), every group
+// M x n_out, written at out + g * M * n_out.
 template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t, bool WG = false>
 __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
@@ -226,7 +228,8 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     rows = min(BG_BM, M - m0);
     n0 = nt * BG_BN;
     const int kb = offsets[g];
-    nk = (offsets[g + 1] - kb) / BK;
+    const int64_t kg = offsets[g + 1] - kb;
+    nk = (int)(kg / BK);
     ares = make_rsrc(A, (uint32_t)(M * lda * 2));
     wres = make_rsrc(W, (uint32_t)(n_out * ldb * 2));
 #pragma unroll
@@ -234,8 +237,9 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
       const int blk = wave * IPW + i;
       const int r = blk * RPI + lane / NCH;
       const int c = (lane % NCH) ^ swz(r);
-      agoff[i] = r < rows ? (uint32_t)(((int64_t)(m0 + r) * lda + kb) * 2) + (uint32_t)c * 16u : kOob;
-      bgoff[i] = n0 + r < n_out ? (uint32_t)(((int64_t)(n0 + r) * ldb + kb) * 2) + (uint32_t)c * 16u : kOob;
+      agoff[i] = r < rows ? (uint32_t)(((int64_t)kb * M + (int64_t)(m0 + r) * kg) * 2) + (uint32_t)c * 16u : kOob;
+      bgoff[i] = n0 + r < n_out ? (uint32_t)(((int64_t)kb * n_out + (int64_t)(n0 + r) * kg) * 2) + (uint32_t)c * 16u
+                                : kOob;
     }
     obase = out + (size_t)g * M * n_out;
     ostride = n_out;
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
     }
   };
 
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(af[kk][i], bfr[kk][j], acc[i][j]);
+          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(bfr[kk][j], af[kk][i], acc[i][j]);
       __builtin_amdgcn_s_setprio(0);
     };
     auto bar = [&]() {
@@ -390,30 +394,96 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     if (!second) bar();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may outlive the block
+  // every wave's loads have landed and its LDS reads are done: the stages are free
+  __syncthreads();
 
-  // Epilogue.  32x32 MFMA layout: lane holds column (lane & 31) and rows
-  // 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
-  constexpr int NJ = SWIGLU ? NI / 2 : NI;
+  // Epilogue through LDS.  The weight fragment is the MFMA's first operand, so the
+  // 32x32 accumulator of block (i, j) holds, in lane l, tile row i * 32 + (l & 31) and
+  // the four consecutive columns j * 32 + 8 * (r / 4) + 4 * (l / 32) + (r % 4), r % 4 =
+  // 0..3.  Each wave stages its 128-row part of the tile in its own 16 KB stage array,
+  // then stores whole 16-byte column runs, 8 .. 16 lanes per row.
+  static_assert(NBUF == 4 && WN_W == 4 && BK == 32, "the epilogue uses the eight 16 KB stage arrays");
+  uint8_t *stage = wave < 4 ? bufA(wave) : bufB(wave - 4);
+  const int lr = lane & 31, lh = lane >> 5;
+  if constexpr (SWIGLU) {
+    static_assert(sizeof(OutT) == 2 && NI == 2, "SwiGLU: bf16 output, one gate and one up block per wave");
+    // 128 rows x 32 columns of H, 64-byte rows; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + lr;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + wn * NJ * 32 + j * 32 + (lane & 31);
-      if (col >= n_out) continue;
+      for (int q = 0; q < 4; ++q) {
+        uint2 v;
+        v.x = pack_bf16x2(silu_f32(acc[i][0][4 * q]) * acc[i][1][4 * q],
+                          silu_f32(acc[i][0][4 * q + 1]) * acc[i][1][4 * q + 1]);
+        v.y = pack_bf16x2(silu_f32(acc[i][0][4 * q + 2]) * acc[i][1][4 * q + 2],
+                          silu_f32(acc[i][0][4 * q + 3]) * acc[i][1][4 * q + 3]);
+        *reinterpret_cast<uint2 *>(stage + row * 64 + ((q ^ ((row >> 2) & 3)) << 4) + lh * 8) = v;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int gcol = n0 + wn * 32 + (lane & 3) * 8;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= rows) continue;
-        float v;
-        if constexpr (SWIGLU) {
-          v = silu_f32(acc[i][j][r]) * acc[i][j + NI / 2][r];
-        } else {
-          v = acc[i][j][r];
+    for (int it = 0; it < 8; ++it) {
+      const int row = it * 16 + (lane >> 2);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 64 + (((lane & 3) ^ ((row >> 2) & 3)) << 4));
+      const int grow = wm * 128 + row;
+      if (grow < rows && gcol < n_out) stg16(obase + (size_t)(m0 + grow) * ostride + gcol, v);
+    }
+  } else {
+    const int gcol0 = n0 + wn * 64;
+    if (partial || sizeof(OutT) == 4) {
+      // float: two passes of 64 rows x 64 columns, 256-byte rows; chunk c of row r at c ^ (r & 15)
+      float *fbase = partial ? split_out + (size_t)ks * split_stride : reinterpret_cast<float *>(obase);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int row = ii * 32 + lr;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = j * 8 + q * 2 + lh;
+              const f32x4 v = {acc[2 * p + ii][j][4 * q], acc[2 * p + ii][j][4 * q + 1], acc[2 * p + ii][j][4 * q + 2],
+                               acc[2 * p + ii][j][4 * q + 3]};
+              *reinterpret_cast<f32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4)) = v;
+            }
         }
-        if (partial)
-          split_out[(size_t)ks * split_stride + (size_t)(m0 + row) * ostride + col] = v;
-        else
-          store_out(obase + (size_t)(m0 + row) * ostride + col, v);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int c = lane & 15, gcol = gcol0 + c * 4;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int row = it * 4 + (lane >> 4);
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+          const int grow = wm * 128 + p * 64 + row;
+          if (grow < rows && gcol < n_out) stg16(fbase + (size_t)(m0 + grow) * ostride + gcol, v);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass writes
+      }
+    } else if constexpr (sizeof(OutT) == 2) {
+      // bf16: 128 rows x 64 columns, 128-byte rows; chunk c of row r at c ^ ((r >> 1) & 7)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + lr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2 *>(stage + row * 128 + (((j * 4 + q) ^ ((row >> 1) & 7)) << 4) + lh * 8) = v;
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int c = lane & 7, gcol = gcol0 + c * 8;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = it * 8 + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+        const int grow = wm * 128 + row;
+        if (grow < rows && gcol < n_out) stg16(obase + (size_t)(m0 + grow) * ostride + gcol, v);
       }
     }
   }
@@ -423,6 +493,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 
 template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32, typename OutT = bf16_t>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
@@ -454,6 +525,7 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_t
 // group ranges multiples of 32; an empty group writes zeros.
 hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
                             int N, bool out_f32, void *out, hipStream_t s) {
+  if (N % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
   if (out_f32)

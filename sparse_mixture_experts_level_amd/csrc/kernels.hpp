@@ -95,9 +95,11 @@ hipError_t launch_aux_loss(const float *logits, const int32_t *counts, int T, in
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v0, int32_t step, hipStream_t s);
 
 // ---- backward (backward.hip); bf16 activations and weights
-// out[b][c][p] = in[b][src(p)][c] for p < P (zero where p has no source): src(p) = p for
-// p < rows, or with group offsets off / poff (G groups) row off[g] + (p - poff[g]) inside
-// group g's rows (through row_index when given) and zero in its padding.
+// Plain: out[b][c][p] = in[b][p][c] for p < P, zero for p >= rows (row stride out_ld).
+// Grouped (group offsets off / poff, G groups): position p of group g holds row off[g] +
+// (p - poff[g]) inside the group's rows (through row_index when given), zero in its
+// padding, written group-major: group g's [cols, K_g] block at poff[g] * cols, row stride
+// K_g = poff[g+1] - poff[g].
 hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
                                  const int32_t *row_index, const int32_t *off, const int32_t *poff, int G, int64_t P,
                                  void *out, int64_t out_ld, int64_t out_stride_b, hipStream_t s);
@@ -113,8 +115,10 @@ hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float 
                             float *dl, void *dl16, hipStream_t s);
 hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
                             int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
-// out[g][m][n] = sum_{k in [poff[g], poff[g+1])} AT[m][k] BT[n][k]; ranges multiples of 32
-// (gemm_big.hip: 256 x 256 tiles; backward.hip: 64 x 64 tiles for short ranges)
+// out[g][m][n] = sum_{k < K_g} AT_g[m][k] BT_g[n][k], K_g = poff[g+1] - poff[g] (multiples of
+// 32), AT_g = AT + poff[g] * M, BT_g = BT + poff[g] * N, row stride K_g (group-major); lda
+// and ldb bound the buffers.  gemm_big.hip: 256 x 256 tiles for long ranges; backward.hip:
+// 128 x 128 tiles for short ones.
 hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
                             int N, bool out_f32, void *out, hipStream_t s);
 hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
