@@ -619,8 +619,11 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dgu = take(R * 2 * f * s);
   L.hg = take(R * f * s);
   L.dxr = take(R * d * s);
-  L.wdT = take(E * f * d * s);
-  L.wguT = take(E * d * 2 * f * s);
+  // the weights transposed for the dgrad GEMMs, only when they take the large-tile
+  // kernel; the streaming kernel reads the K-major weights as they are
+  const bool big = moe::grouped_gemm_big_regime(R, (int)E, std::max(1, group_rows_bound(D)));
+  L.wdT = take(big ? E * f * d * s : 0);
+  L.wguT = take(big ? E * d * 2 * f * s : 0);
   L.poff = take((E + 1) * 4);
   L.dyT = take(d * L.Rpad * s);
   L.hgT = take(f * L.Rpad * s);
@@ -736,6 +739,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   const float *gates = routing->topk_gates;
   const int64_t R = max_rows(D);
   const int32_t grb = std::max(1, group_rows_bound(D));
+  const bool dgrad_big = moe::grouped_gemm_big_regime(R, E, grb);
   const int32_t *rows_dev = offsets + E;  // kept rows, on the device
   auto W = [&](size_t off) { return at<void>(ws, off); };
   const int64_t s = 2;
@@ -763,12 +767,19 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(gemm(gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d,
                            W(L.gu), true),
                  "gate_up recompute"));
-    // dH' = dy W_d (weights transposed to [f, d] per expert)
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0, d,
-                                           W(L.wdT), d, (int64_t)f * d, stream),
-                "w_down transpose"));
-    MOE_TRY(gemm(gemm_args(E, R, grb, dy, row_token, T, offsets, W(L.wdT), (int64_t)f * d, f, d, W(L.dhp)),
-                 "dH' grouped GEMM"));
+    // dH' = dy W_d: W_d [d, f] is K-major for this product; the large-tile kernel takes it
+    // transposed to [f, d] per expert
+    if (dgrad_big) {
+      MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0,
+                                             d, W(L.wdT), d, (int64_t)f * d, stream),
+                  "w_down transpose"));
+      MOE_TRY(gemm(gemm_args(E, R, grb, dy, row_token, T, offsets, W(L.wdT), (int64_t)f * d, f, d, W(L.dhp)),
+                   "dH' grouped GEMM"));
+    } else {
+      auto a = gemm_args(E, R, grb, dy, row_token, T, offsets, weights->w_down, (int64_t)d * f, f, d, W(L.dhp));
+      a.w_kn = true;
+      MOE_TRY(gemm(a, "dH' grouped GEMM"));
+    }
   }
   float *dgate = at<float>(ws, L.dgate);
   MOE_TRY(hcall(moe::launch_fill_u32(dgate, (int64_t)T * k, 0u, stream), "zero gate gradients"));
@@ -776,13 +787,21 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gu), W(L.dhp), R, rows_dev, f, row_token, serving, slot, offsets, gates,
                                        k, W(L.dgu), W(L.hg), dgate, stream),
                 "SwiGLU backward"));
-    // dx rows = [dG dU] W_gu (weights transposed to [d, 2f] per expert)
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d, E, nullptr, nullptr,
-                                           nullptr, 0, 2 * f, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
-                "w_gate_up transpose"));
-    MOE_TRY(gemm(gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, W(L.wguT), (int64_t)d * 2 * f, d, 2 * f,
-                           W(L.dxr)),
-                 "dx grouped GEMM"));
+    // dx rows = [dG dU] W_gu (W_gu [2f, d] is K-major for this product; transposed to
+    // [d, 2f] per expert for the large-tile kernel)
+    if (dgrad_big) {
+      MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d, E, nullptr, nullptr,
+                                             nullptr, 0, 2 * f, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
+                  "w_gate_up transpose"));
+      MOE_TRY(gemm(gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, W(L.wguT), (int64_t)d * 2 * f, d, 2 * f,
+                             W(L.dxr)),
+                   "dx grouped GEMM"));
+    } else {
+      auto a = gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, weights->w_gate_up, (int64_t)2 * f * d, d, 2 * f,
+                         W(L.dxr));
+      a.w_kn = true;
+      MOE_TRY(gemm(a, "dx grouped GEMM"));
+    }
     // weight gradients, grouped over each expert's rows (padded to 32, zeros in the pad)
     MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad, 0,
                                            stream),

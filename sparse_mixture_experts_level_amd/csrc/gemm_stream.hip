@@ -34,6 +34,34 @@ constexpr int sg_stage_bytes() {
   return (BM * 8 < 64 * NW ? 64 * NW : BM * 8) * 16;
 }
 
+// K-major weight tile in LDS: 64 k-rows of 64 columns (8 pieces of 8 columns, 16 bytes
+// each); piece p of row r is stored at slot 8 r + (p ^ wt_swz(r)).  The swizzle spreads
+// the transpose reads of one instruction -- per 16 lanes, rows r0 .. r0 + 3 of two
+// adjacent pieces; the four 16-lane groups 8 rows apart -- over all 64 banks, two groups
+// per LDS cycle.
+__device__ __forceinline__ int wt_swz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16), 16-lane groups: lane 4a + c of a group
+// receives element c of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12 of
+// the group, in that order.  For the 16x16x32 MFMA B operand (lane: column n = lane & 15,
+// k = 8 (lane >> 4) .. + 7) a lane addresses k-row k0 + (lane & 15) / 4 and columns
+// 4 ((lane & 15) % 4) .. + 3 of its wave's 16, for k0 = 32 s + 8 (lane >> 4) and k0 + 4.
+__device__ __forceinline__ u32x4 wt_frag(const uint8_t *tile, int s, int wave, int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int l16 = lane & 15;
+  const int piece = 2 * wave + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+  u32x4 out;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 32 * s + 8 * (lane >> 4) + 4 * t + (l16 >> 2);
+    const uint8_t *p = tile + (r * 8 + (piece ^ wt_swz(r))) * 16 + half;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+    out[2 * t] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+    out[2 * t + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+  }
+  return out;
+}
+
 // Loop over K for one block of `rows` <= BM rows starting at m0, specialised on NA,
 // the number of workgroup-wide rounds of 16-byte A pieces the block needs
 // (ceil(rows * 8 / (64 * NW))): blocks of few rows issue few A loads and run only the
@@ -47,25 +75,36 @@ constexpr int sg_stage_bytes() {
 // Loads are issued unconditionally through buffer resources: token rows past the
 // block's end and weight subtiles past n_out get an out-of-range offset and read as
 // zeros without a memory access, which keeps the count of loads per step static.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT, bool WT>
 __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t ares, const uint32_t *boff,
                                              const uint32_t *aoff, uint8_t *sA0, uint8_t *sA1, uint8_t *sA2,
-                                             uint8_t *sA3, int nk, int rows, int m0, int ncol0, int nvalid,
-                                             int n_out, OutT *__restrict__ out) {
+                                             uint8_t *sA3, uint8_t *const *sW, int nk, int rows, int m0, int ncol0,
+                                             int nvalid, int n_out, OutT *__restrict__ out) {
   static_assert(S == 3 || S == 4, "three or four stages");
+  static_assert(!WT || (NSUB == 1 && NW == 4 && !SWIGLU), "K-major weights: one 64-column tile of four waves");
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;
   constexpr int MS = NA * NW / 2 < BM / 16 ? NA * NW / 2 : BM / 16;  // 16-row subtiles the block can fill
-  constexpr int LOADS = NA + 2 * NB;                       // loads per thread and chunk
+  constexpr int LOADS = NA + 2 * (WT ? 1 : NB);            // loads per thread and chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   auto stage = [&](int i) -> uint8_t * { return i == 0 ? sA0 : i == 1 ? sA1 : i == 2 ? sA2 : sA3; };
-  u32x4 slot[S][2][NB];
+  u32x4 slot[WT ? 1 : S][2][NB];
+  // K-major weights: a chunk's 64 x 64 weight tile moves into LDS as rows of 128 bytes,
+  // two 1 KB instructions per wave (8 rows each, boff[0] and boff[1]); a chunk advances
+  // 64 rows.
+  const uint32_t wchunk = (uint32_t)SG_KC * (uint32_t)n_out * 2u;
 
   auto issue = [&](int sl, int c) {
     const uint32_t kc = (uint32_t)c * (SG_KC * 2);
+    if constexpr (WT) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int p = 0; p < 2; ++p)
+        buf_ld16_lds(wres, boff[p] == kOob ? kOob : boff[p] + (uint32_t)c * wchunk, sW[sl] + (wave * 2 + p) * 1024);
+    } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) slot[sl][s][b] = buf_ld16(wres, boff[b] + kc + s * 64u);
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) slot[sl][s][b] = buf_ld16(wres, boff[b] + kc + s * 64u);
+    }
     uint8_t *st = stage(sl);
 #pragma unroll
     for (int i = 0; i < NA; ++i) buf_ld16_lds(ares, aoff[i] + kc, st + (i * 64 * NW + wave * 64) * 16);
@@ -86,10 +125,18 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
         const int c = s * 4 + (lane >> 4);
         a[i] = *reinterpret_cast<const u32x4 *>(st + (r * 8 + (c ^ (r & 7))) * 16);
       }
+      if constexpr (WT) {
+        // B fragment (column lane & 15, k = 32 s + 8 (lane >> 4) .. + 7) from the
+        // row-major tile with two LDS transpose reads of four k each (wt_frag_addr)
+        const u32x4 b = wt_frag(sW[sl], s, wave, lane);
 #pragma unroll
-      for (int i = 0; i < MS; ++i)
+        for (int i = 0; i < MS; ++i) acc[i][0] = mfma16(a[i], b, acc[i][0]);
+      } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], slot[sl][s][b], acc[i][b]);
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], slot[sl][s][b], acc[i][b]);
+      }
     }
   };
   auto bar = [&]() {
@@ -155,7 +202,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 // deals consecutive blocks to the 8 XCDs round-robin, which spreads every expert --
 // including the few heavily loaded ones -- over all XCDs.  NW waves per workgroup
 // share the staged A rows: wider workgroups load each token row fewer times.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW, typename OutT>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, typename OutT, bool WT = false>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
                                                                      const int32_t *__restrict__ row_index,
                                                                      int64_t a_rows,
@@ -170,6 +217,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   // one LDS array per stage, so that waiting for the loads into one stage never waits
   // for the loads into another
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[S > 3 ? STAGE : 16];
+  // K-major weights: one 8 KB weight tile per stage
+  constexpr int WSTAGE = WT ? SG_KC * 64 * 2 : 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t sW0[WSTAGE], sW1[WSTAGE], sW2[WSTAGE],
+      sW3[S > 3 ? WSTAGE : 16];
+  uint8_t *const sW[4] = {sW0, sW1, sW2, sW3};
 
   const int tile = blockIdx.x;
   const int g = tile / n_tiles, nt = tile - g * n_tiles;
@@ -182,12 +234,24 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   const uint32_t kbytes = (uint32_t)K * 2u;
   const rsrc_t wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
 
-  uint32_t boff[NB];  // byte offset of this lane's 16 bytes in weight subtile b at k = 0
+  uint32_t boff[NB < 2 ? 2 : NB];
+  if constexpr (WT) {
+    // this lane's piece of weight-tile instruction q = 2 wave + p at k = 0: k-row
+    // 8 q + lane / 8, piece (lane % 8) ^ wt_swz(row), columns nt * 64 + 8 piece .. + 7
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int sidx = b % NSUB;
-    const int r = ncol0 + sidx * 16 + (lane & 15) + (b >= NSUB ? n_out : 0);
-    boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane >> 4) * 16u : kOob;
+    for (int p = 0; p < 2; ++p) {
+      const int r = (wave * 2 + p) * 8 + (lane >> 3);
+      const int col = nt * 64 + ((lane & 7) ^ wt_swz(r)) * 8;
+      boff[p] = col < n_out ? ((uint32_t)r * (uint32_t)n_out + (uint32_t)col) * 2u : kOob;
+    }
+  } else {
+    // byte offset of this lane's 16 bytes in weight subtile b at k = 0
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int sidx = b % NSUB;
+      const int r = ncol0 + sidx * 16 + (lane & 15) + (b >= NSUB ? n_out : 0);
+      boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane >> 4) * 16u : kOob;
+    }
   }
   const int nk = K / SG_KC;
 
@@ -214,8 +278,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
 #define SG_BLOCK(N)                                                                                              \
   if constexpr (N <= A_PER_T) {                                                                                  \
     if (na == N) {                                                                                               \
-      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, nk, rows, m0, ncol0, nvalid, \
-                                           n_out, out);                                                          \
+      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT, WT>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, sW, nk, rows, m0, \
+                                                     ncol0, nvalid, n_out, out);                                  \
       continue;                                                                                                  \
     }                                                                                                            \
   }
@@ -227,16 +291,27 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   }
 }
 
-template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4, typename OutT = bf16_t>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4, typename OutT = bf16_t, bool WT = false>
 hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
   const int cols_per_tile = 16 * NW * NSUB;
   const int n_tiles = (a.n_out + cols_per_tile - 1) / cols_per_tile;
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT, WT>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                      static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles);
   return hipGetLastError();
+}
+
+// K-major weights (no SwiGLU, bf16 output): weight tiles share LDS with the A stages, so
+// 128-row blocks take three stages to keep two workgroups per CU.
+hipError_t launch_stream_kn(const GroupedGemmArgs &a, hipStream_t s) {
+  if (a.n_out % 64) return hipErrorInvalidValue;  // whole 64-column weight tiles
+  const int r = a.group_rows_max;
+  if (r <= 16) return launch_stream<16, 1, false, 4, 4, bf16_t, true>(a, s);
+  if (r <= 32) return launch_stream<32, 1, false, 4, 4, bf16_t, true>(a, s);
+  if (r <= 64) return launch_stream<64, 1, false, 4, 4, bf16_t, true>(a, s);
+  return launch_stream<128, 1, false, 3, 4, bf16_t, true>(a, s);
 }
 
 template <bool SWIGLU, typename OutT = bf16_t>
@@ -254,6 +329,7 @@ hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s) {
+  if (a.w_kn) return (a.swiglu || a.out_f32) ? hipErrorInvalidValue : launch_stream_kn(a, s);
   if (a.swiglu) return launch_stream_bm<true>(a, s);
   return a.out_f32 ? launch_stream_bm<false, float>(a, s) : launch_stream_bm<false>(a, s);
 }
@@ -262,9 +338,13 @@ hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t
 // weight byte feeds few MFMAs, HBM bound), the 256 x 256 tile kernel when they hold
 // many (MFMA bound).  The row bounds are the caller's; either kernel computes any
 // group size correctly.
+bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_max) {
+  return num_groups > 0 && rows_max / num_groups >= 256 && group_rows_max >= 256;
+}
+
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s) {
-  const int64_t avg_rows = a.rows_max / a.num_groups;
-  if (avg_rows >= 256 && a.group_rows_max >= 256) return launch_grouped_gemm_big_bf16(a, a.rows_max, s);
+  if (!a.w_kn && grouped_gemm_big_regime(a.rows_max, a.num_groups, a.group_rows_max))
+    return launch_grouped_gemm_big_bf16(a, a.rows_max, s);
   return launch_grouped_gemm_stream_bf16(a, s);
 }
 

@@ -75,8 +75,14 @@ struct GroupedGemmArgs {
   // Workspace for float partial sums when the large-tile kernel cuts few tiles along K
   // (4 * rows_max * n_out floats); NULL: no K split.
   float *split_ws = nullptr;
+  // Weights stored K-major: group g's matrix is [K, n_out] (row stride n_out) instead of
+  // [n_out, K] -- the layout the backward pass multiplies by (dy W_d, dGU W_gu).  No SwiGLU.
+  bool w_kn = false;
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
+// Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group) for
+// weights in the [n_out, K] layout; K-major weights (w_kn) take the streaming kernel only.
+bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_max);
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GroupedGemmArgs &a, hipStream_t s);
