@@ -595,7 +595,7 @@ namespace {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdLayout {
-  size_t gu, dhp, dgu, hg, dxr, wdT, wguT, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wrT, dxrt, tpoff,
+  size_t gu, dhp, dgu, hg, dxr, wdT, wguT, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wrT, wr_part, dxrt, tpoff,
       sh_off, gus, dhs, dgus, hs, dxs, wsdT, wsguT, dyTT, hsT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
 };
@@ -635,6 +635,8 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dlT = take(L.Epad * L.Tpad * s);
   L.xTT = take(d * L.Tpad * s);
   L.wrT = take(d * L.Epad * s);
+  const int64_t wr_split = moe::wgrad_ksplit((int)E, (int)d, L.Tpad);
+  L.wr_part = take(wr_split > 1 ? wr_split * E * d * 4 : 0);
   L.dxrt = take(T * d * s);
   L.tpoff = take(2 * 4);
   L.sh_off = take(2 * 4);
@@ -833,7 +835,8 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.xTT), L.Tpad, 0,
                                          stream),
               "x transpose"));
-  MOE_TRY(hcall(wgrad(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, E, d, true, grads->dw_router, T),
+  MOE_TRY(hcall(moe::launch_wgrad_ksplit(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, E, d, L.Tpad, at<float>(ws, L.wr_part),
+                                        static_cast<float *>(grads->dw_router), stream),
               "dW_router"));
   MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_router, 0, E, d, 1, nullptr, nullptr, nullptr, 0, L.Epad,
                                          W(L.wrT), L.Epad, 0, stream),

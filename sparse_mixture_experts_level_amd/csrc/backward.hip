@@ -270,13 +270,19 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void wgrad_kernel(const bf16_t *__restrict__ AT, int64_t lda,
                                                     const bf16_t *__restrict__ BT, int64_t ldb,
                                                     const int32_t *__restrict__ poff, int M, int N, int m_tiles,
-                                                    int n_tiles, void *__restrict__ out) {
+                                                    int n_tiles, void *__restrict__ out, int ksplit) {
   constexpr int ES = OUT_F32 ? 4 : 2;            // output element bytes
   __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][64 * 64 * ES];
   const int per_g = m_tiles * n_tiles;
   // Tiles in launch order, dealt round-robin to the XCDs: groups' row counts are skewed,
   // and contiguous ranges per XCD would leave the heavy groups on a few XCDs.
-  const int tile = blockIdx.x;
+  // With ksplit > 1 (one group, float output) block b computes K slice b / per_g of the
+  // tile b % per_g into its own [M, N] slice of out; a reduction adds the slices.
+  int tile = blockIdx.x, ks = 0;
+  if (ksplit > 1) {
+    ks = tile / per_g;
+    tile -= ks * per_g;
+  }
   const int g = tile / per_g;
   const int rem = tile - g * per_g;
   const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
@@ -284,7 +290,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int lr = lane & 31, lh = lane >> 5;
   const int m0 = mt * 128 + (wave >> 1) * 64, n0 = nt * 128 + (wave & 1) * 64;
   const int kb = poff[g], ke = poff[g + 1];
-  const int nk = (ke - kb) / 32;
+  const int nk_all = (ke - kb) / 32, per = (nk_all + ksplit - 1) / ksplit;
+  const int k_lo = min(nk_all, ks * per), nk = min(nk_all, k_lo + per) - k_lo;  // in 32-wide chunks
   const rsrc_t ares = make_rsrc(AT, (uint32_t)min<int64_t>((int64_t)M * lda * 2, 0x7fffffffLL));
   const rsrc_t bres = make_rsrc(BT, (uint32_t)min<int64_t>((int64_t)N * ldb * 2, 0x7fffffffLL));
   // 32x32x16 operand fragment: lane holds row (lane & 31), k = 8 * (lane >> 5) .. + 7.
@@ -295,8 +302,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + i * 32 + lr, n = n0 + i * 32 + lr;
-    ao[i] = m < M ? (uint32_t)(((int64_t)kb * M + (int64_t)m * kg) * 2) + (uint32_t)lh * 16u : kOob;
-    bo[i] = n < N ? (uint32_t)(((int64_t)kb * N + (int64_t)n * kg) * 2) + (uint32_t)lh * 16u : kOob;
+    ao[i] = m < M ? (uint32_t)(((int64_t)kb * M + (int64_t)m * kg + k_lo * 32) * 2) + (uint32_t)lh * 16u : kOob;
+    bo[i] = n < N ? (uint32_t)(((int64_t)kb * N + (int64_t)n * kg + k_lo * 32) * 2) + (uint32_t)lh * 16u : kOob;
   }
   f32x16 acc[2][2];
 #pragma unroll
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   // acc[i][j] element r: row m0 + i * 32 + (lane & 31), column n0 + j * 32 + 8 * (r / 4) +
   // 4 * (lane / 32) + r % 4.  Each wave stages its 64 x 64 in its own LDS region.
   uint8_t *stage = stage_all[wave];
-  const size_t obase = (size_t)g * M * N;
+  const size_t obase = (size_t)(g + ks) * M * N;  // ks > 0 only for one group
   if constexpr (OUT_F32) {
     // 256-byte rows; 16-byte chunk c (4 columns) of row r at c ^ (r & 15)
 #pragma unroll
@@ -382,7 +389,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
 }
 
+// out[i] = sum over s < S of part[s * n + i], in order (float, n a multiple of 4).
+__global__ __launch_bounds__(256) void ksplit_sum_kernel(const float *__restrict__ part, int S, int64_t n,
+                                                         float *__restrict__ out) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 1024) {
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(part + i);
+    for (int s = 1; s < S; ++s) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * n + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[q];
+    }
+    *reinterpret_cast<f32x4 *>(out + i) = acc;
+  }
+}
+
 }  // namespace
+
+int wgrad_ksplit(int M, int N, int64_t K) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t chunks = K / 32;
+  if (tiles >= 256 || chunks < 16) return 1;
+  return (int)std::min<int64_t>({64, std::max(1, 512 / tiles), chunks / 8});
+}
+
+hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int M,
+                               int N, int64_t K, float *part, float *out, hipStream_t s) {
+  if (N % 8) return hipErrorInvalidValue;
+  const int S = wgrad_ksplit(M, N, K);
+  const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
+  if (S == 1) {
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s,
+                       static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
+                       n_tiles, static_cast<void *>(out), 1);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)(m_tiles * n_tiles * S)), dim3(256), 0, s,
+                     static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
+                     n_tiles, static_cast<void *>(part), S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)M * N;
+  const int64_t blocks = std::min<int64_t>((n / 4 + 255) / 256, 2048);
+  hipLaunchKernelGGL(ksplit_sum_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, part, S, n, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t rows, int cols, int batch,
                                  const int32_t *row_index, const int32_t *off, const int32_t *poff, int G, int64_t P,
@@ -441,10 +491,10 @@ hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_f32)
     hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT), lda,
-                       static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out);
+                       static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out, 1);
   else
     hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT),
-                       lda, static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out);
+                       lda, static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out, 1);
   return hipGetLastError();
 }
 

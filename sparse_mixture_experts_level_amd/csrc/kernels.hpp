@@ -125,6 +125,12 @@ hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32
 // 32), AT_g = AT + poff[g] * M, BT_g = BT + poff[g] * N, row stride K_g (group-major); lda
 // and ldb bound the buffers.  gemm_big.hip: 256 x 256 tiles for long ranges; backward.hip:
 // 128 x 128 tiles for short ones.
+// One group (koff = {0, K}), float output, split along K into wgrad_ksplit(M, N, K) slices
+// when the output has few tiles: slice partials in part (that many * M * N floats), added
+// in order into out.
+int wgrad_ksplit(int M, int N, int64_t K);
+hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int M,
+                               int N, int64_t K, float *part, float *out, hipStream_t s);
 hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
                             int N, bool out_f32, void *out, hipStream_t s);
 hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
