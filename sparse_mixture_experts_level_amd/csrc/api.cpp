@@ -595,8 +595,8 @@ namespace {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdLayout {
-  size_t gu, dhp, dgu, hg, dxr, wdT, wguT, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wrT, wr_part, dxrt, tpoff,
-      sh_off, gus, dhs, dgus, hs, dxs, wsdT, wsguT, dyTT, hsT, dgusT, total;
+  size_t gu, dhp, dgu, hg, dxr, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wr_part, dxrt, tpoff, sh_off, gus,
+      dhs, dgus, hs, dxs, dyTT, hsT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
 };
 
@@ -619,11 +619,6 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dgu = take(R * 2 * f * s);
   L.hg = take(R * f * s);
   L.dxr = take(R * d * s);
-  // the weights transposed for the dgrad GEMMs, only when they take the large-tile
-  // kernel; the streaming kernel reads the K-major weights as they are
-  const bool big = moe::grouped_gemm_big_regime(R, (int)E, std::max(1, group_rows_bound(D)));
-  L.wdT = take(big ? E * f * d * s : 0);
-  L.wguT = take(big ? E * d * 2 * f * s : 0);
   L.poff = take((E + 1) * 4);
   L.dyT = take(d * L.Rpad * s);
   L.hgT = take(f * L.Rpad * s);
@@ -634,7 +629,6 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dl16 = take(T * L.Epad * s);
   L.dlT = take(L.Epad * L.Tpad * s);
   L.xTT = take(d * L.Tpad * s);
-  L.wrT = take(d * L.Epad * s);
   const int64_t wr_split = moe::wgrad_ksplit((int)E, (int)d, L.Tpad);
   L.wr_part = take(wr_split > 1 ? wr_split * E * d * 4 : 0);
   L.dxrt = take(T * d * s);
@@ -645,8 +639,6 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dgus = take(fs ? T * 2 * fs * s : 0);
   L.hs = take(fs ? T * fs * s : 0);
   L.dxs = take(fs ? T * d * s : 0);
-  L.wsdT = take(fs ? fs * d * s : 0);
-  L.wsguT = take(fs ? d * 2 * fs * s : 0);
   L.dyTT = take(fs ? d * L.Tpad * s : 0);
   L.hsT = take(fs ? fs * L.Tpad * s : 0);
   L.dgusT = take(fs ? 2 * fs * L.Tpad * s : 0);
@@ -741,7 +733,6 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   const float *gates = routing->topk_gates;
   const int64_t R = max_rows(D);
   const int32_t grb = std::max(1, group_rows_bound(D));
-  const bool dgrad_big = moe::grouped_gemm_big_regime(R, E, grb);
   const int32_t *rows_dev = offsets + E;  // kept rows, on the device
   auto W = [&](size_t off) { return at<void>(ws, off); };
   const int64_t s = 2;
@@ -769,19 +760,10 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(gemm(gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d,
                            W(L.gu), true),
                  "gate_up recompute"));
-    // dH' = dy W_d: W_d [d, f] is K-major for this product; the large-tile kernel takes it
-    // transposed to [f, d] per expert
-    if (dgrad_big) {
-      MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_down, (int64_t)d * f, d, f, E, nullptr, nullptr, nullptr, 0,
-                                             d, W(L.wdT), d, (int64_t)f * d, stream),
-                  "w_down transpose"));
-      MOE_TRY(gemm(gemm_args(E, R, grb, dy, row_token, T, offsets, W(L.wdT), (int64_t)f * d, f, d, W(L.dhp)),
-                   "dH' grouped GEMM"));
-    } else {
-      auto a = gemm_args(E, R, grb, dy, row_token, T, offsets, weights->w_down, (int64_t)d * f, f, d, W(L.dhp));
-      a.w_kn = true;
-      MOE_TRY(gemm(a, "dH' grouped GEMM"));
-    }
+    // dH' = dy W_d: W_d [d, f] per expert is K-major for this product
+    auto a = gemm_args(E, R, grb, dy, row_token, T, offsets, weights->w_down, (int64_t)d * f, f, d, W(L.dhp));
+    a.w_kn = true;
+    MOE_TRY(gemm(a, "dH' grouped GEMM"));
   }
   float *dgate = at<float>(ws, L.dgate);
   MOE_TRY(hcall(moe::launch_fill_u32(dgate, (int64_t)T * k, 0u, stream), "zero gate gradients"));
@@ -789,21 +771,11 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gu), W(L.dhp), R, rows_dev, f, row_token, serving, slot, offsets, gates,
                                        k, W(L.dgu), W(L.hg), dgate, stream),
                 "SwiGLU backward"));
-    // dx rows = [dG dU] W_gu (W_gu [2f, d] is K-major for this product; transposed to
-    // [d, 2f] per expert for the large-tile kernel)
-    if (dgrad_big) {
-      MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d, E, nullptr, nullptr,
-                                             nullptr, 0, 2 * f, W(L.wguT), 2 * f, (int64_t)d * 2 * f, stream),
-                  "w_gate_up transpose"));
-      MOE_TRY(gemm(gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, W(L.wguT), (int64_t)d * 2 * f, d, 2 * f,
-                             W(L.dxr)),
-                   "dx grouped GEMM"));
-    } else {
-      auto a = gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, weights->w_gate_up, (int64_t)2 * f * d, d, 2 * f,
-                         W(L.dxr));
-      a.w_kn = true;
-      MOE_TRY(gemm(a, "dx grouped GEMM"));
-    }
+    // dx rows = [dG dU] W_gu (W_gu [2f, d] per expert is K-major for this product)
+    auto a = gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, weights->w_gate_up, (int64_t)2 * f * d, d, 2 * f,
+                       W(L.dxr));
+    a.w_kn = true;
+    MOE_TRY(gemm(a, "dx grouped GEMM"));
     // weight gradients, grouped over each expert's rows (padded to 32, zeros in the pad)
     MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad, 0,
                                            stream),
@@ -838,12 +810,14 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   MOE_TRY(hcall(moe::launch_wgrad_ksplit(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, E, d, L.Tpad, at<float>(ws, L.wr_part),
                                         static_cast<float *>(grads->dw_router), stream),
               "dW_router"));
-  MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_router, 0, E, d, 1, nullptr, nullptr, nullptr, 0, L.Epad,
-                                         W(L.wrT), L.Epad, 0, stream),
-              "w_router transpose"));
-  MOE_TRY(gemm(gemm_args(1, T, T, W(L.dl16), nullptr, 0, sh_off, W(L.wrT), (int64_t)d * L.Epad, d, (int32_t)L.Epad,
-                         W(L.dxrt)),
-               "router dx"));
+  {
+    // dl W_r: W_r [E, d] is K-major for this product; the contraction runs over Epad, rows
+    // past E read as zeros (and dl16's padding columns are zero)
+    auto a = gemm_args(1, T, T, W(L.dl16), nullptr, 0, sh_off, weights->w_router, (int64_t)E * d, d, (int32_t)L.Epad,
+                       W(L.dxrt));
+    a.w_kn = true;
+    MOE_TRY(gemm(a, "router dx"));
+  }
 
   // ---- shared expert (weight 1, every token)
   const void *dxs = nullptr;
@@ -851,18 +825,20 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     MOE_TRY(gemm(gemm_args(1, T, T, x, nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, 2 * fs, d,
                            W(L.gus), true),
                  "shared gate_up recompute"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_down, 0, d, fs, 1, nullptr, nullptr, nullptr, 0, d,
-                                           W(L.wsdT), d, 0, stream),
-                "shared w_down transpose"));
-    MOE_TRY(gemm(gemm_args(1, T, T, dy, nullptr, 0, sh_off, W(L.wsdT), (int64_t)fs * d, fs, d, W(L.dhs)), "shared dH'"));
+    {
+      auto a = gemm_args(1, T, T, dy, nullptr, 0, sh_off, weights->w_shared_down, (int64_t)d * fs, fs, d, W(L.dhs));
+      a.w_kn = true;  // W_sd [d, f_s] is K-major for dy W_sd
+      MOE_TRY(gemm(a, "shared dH'"));
+    }
     MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gus), W(L.dhs), T, nullptr, fs, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        1, W(L.dgus), W(L.hs), nullptr, stream),
                 "shared SwiGLU backward"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(weights->w_shared_gate_up, 0, 2 * fs, d, 1, nullptr, nullptr, nullptr, 0,
-                                           2 * fs, W(L.wsguT), 2 * fs, 0, stream),
-                "shared w_gate_up transpose"));
-    MOE_TRY(gemm(gemm_args(1, T, T, W(L.dgus), nullptr, 0, sh_off, W(L.wsguT), (int64_t)d * 2 * fs, d, 2 * fs,
-                           W(L.dxs)), "shared dx"));
+    {
+      auto a = gemm_args(1, T, T, W(L.dgus), nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, d,
+                         2 * fs, W(L.dxs));
+      a.w_kn = true;  // W_sgu [2 f_s, d] is K-major for [dG dU] W_sgu
+      MOE_TRY(gemm(a, "shared dx"));
+    }
     MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT), L.Tpad,
                                            0, stream),
                 "dy transpose"));

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // A_g = A + offsets[g] * M and W_g = W + offsets[g] * n_out, K-contiguous with row stride
 // K_g (group-major transposed activations; lda and ldb bound the buffers), every group
 // M x n_out, written at out + g * M * n_out.
-template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t, bool WG = false>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t, bool WG = false,
+          bool BKN = false>
 __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
   static_assert(NBUF >= 2 && NBUF <= 4, "stages");
   static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(!BKN || (!SWIGLU && !WG && BK == 32 && WN_W == 4), "K-major weights: plain store, 32-wide steps");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[NBUF > 2 ? TILE : 16],
       sA3[NBUF > 3 ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[NBUF > 2 ? TILE : 16],
@@ -194,14 +196,23 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
         agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
       else
         agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
-      int wr;  // weight row held in tile row r, -1 past n_out
-      if (SWIGLU) {
-        const int col = n0 + (r & 127);
-        wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
+      if constexpr (BKN) {
+        // K-major weights [K, n_out]: instruction blk brings k-rows 2 blk and 2 blk + 1 of
+        // the step, 512 bytes (256 columns) each; lane p of a row stores the row's chunk
+        // p ^ (4 (row & 3)) at slot p
+        const int kr = 2 * blk + (lane >> 5);
+        const int col = n0 + (((lane & 31) ^ (4 * (kr & 3))) << 3);
+        bgoff[i] = col < n_out ? ((uint32_t)kr * (uint32_t)n_out + (uint32_t)col) * 2u : kOob;
       } else {
-        wr = n0 + r < n_out ? n0 + r : -1;
+        int wr;  // weight row held in tile row r, -1 past n_out
+        if (SWIGLU) {
+          const int col = n0 + (r & 127);
+          wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
+        } else {
+          wr = n0 + r < n_out ? n0 + r : -1;
+        }
+        bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
       }
-      bgoff[i] = wr >= 0 ? (uint32_t)wr * kbytes + (uint32_t)c * 16u : kOob;
     }
     const int steps = K / BK, sps = (steps + ksplit - 1) / ksplit;
     kbase = ks * sps;
@@ -247,13 +258,36 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
     const uint32_t kc = (uint32_t)(kbase + kt) * (BK * 2);
+    // K-major weights advance BK rows of n_out elements per step
+    const uint32_t kcb = BKN ? (uint32_t)(kbase + kt) * (uint32_t)BK * (uint32_t)n_out * 2u : kc;
     uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
       buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kc : kOob, la + blk * 1024);
-      buf_ld16_lds(wres, (ok && bgoff[i] != kOob) ? bgoff[i] + kc : kOob, lb + blk * 1024);
+      buf_ld16_lds(wres, (ok && bgoff[i] != kOob) ? bgoff[i] + kcb : kOob, lb + blk * 1024);
     }
+  };
+  // K-major weights: the 32x32x16 MFMA fragment of weight block j (columns nb .. nb + 31 of
+  // the tile, k = 16 kk + 8 (lane >> 5) .. + 7 for column nb + (lane & 31)) from the
+  // [32 k-rows][256 columns] stage, with two LDS transpose reads of four k each.  In a
+  // 16-lane group lane 4a + c receives element c of the 8-byte chunks addressed by lanes
+  // a, a + 4, a + 8, a + 12; so lane s of group G addresses k-row k0 + s / 4 and columns
+  // nb + 16 (G & 1) + 4 (s % 4) .. + 3, with k0 = 16 kk + 8 (G >> 1) (+ 4 for the second).
+  auto kn_frag = [&](const uint8_t *lb, int kk, int nb) -> u32x4 {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int G = lane >> 4, sl = lane & 15;
+    const int col = nb + (G & 1) * 16 + 4 * (sl & 3);
+    u32x4 out;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = kk * 16 + (G >> 1) * 8 + 4 * t + (sl >> 2);
+      const uint8_t *p = lb + r * 512 + (((col >> 3) ^ (4 * (r & 3))) << 4) + (col & 7) * 2;
+      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+      out[2 * t] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+      out[2 * t + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+    }
+    return out;
   };
 
   f32x16 acc[4][NI];
@@ -279,8 +313,12 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
       for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * RB);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
-        bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
+        if constexpr (BKN) {
+          bfr[j] = kn_frag(lb, kk, wn * NI * 32 + j * 32);
+        } else {
+          const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
+          bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -352,8 +390,12 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
         for (int i = 0; i < 4; ++i) af[kk][i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * RB);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
-          bfr[kk][j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
+          if constexpr (BKN) {
+            bfr[kk][j] = kn_frag(lb, kk, wn * NI * 32 + j * 32);
+          } else {
+            const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
+            bfr[kk][j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
+          }
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -491,7 +533,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 
 }  // namespace
 
-template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32, typename OutT = bf16_t>
+template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32, typename OutT = bf16_t, bool BKN = false>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
@@ -501,7 +543,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
   const int64_t split_stride = rows_total_max * a.n_out;
   const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT, false, BKN>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride);
@@ -516,6 +558,10 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
 
 // Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  if (a.w_kn) {  // K-major weights: bf16 output, no SwiGLU
+    if (a.swiglu || a.out_f32) return hipErrorInvalidValue;
+    return launch_big<false, 4, 4, true, 32, bf16_t, true>(a, rows_total_max, s);
+  }
   if (a.swiglu) return launch_big<true, 4, 4, true>(a, rows_total_max, s);
   return a.out_f32 ? launch_big<false, 4, 4, true, 32, float>(a, rows_total_max, s)
                    : launch_big<false, 4, 4, true>(a, rows_total_max, s);

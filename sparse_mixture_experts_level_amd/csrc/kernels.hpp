@@ -80,8 +80,8 @@ struct GroupedGemmArgs {
   bool w_kn = false;
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
-// Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group) for
-// weights in the [n_out, K] layout; K-major weights (w_kn) take the streaming kernel only.
+// Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group)
+// rather than the streaming one; either reads weights in both layouts (w_kn).
 bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_max);
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s);
