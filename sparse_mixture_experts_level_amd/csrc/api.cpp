@@ -598,6 +598,7 @@ struct BwdLayout {
   size_t gu, dhp, dgu, hg, dxr, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wr_part, dxrt, tpoff, sh_off, gus,
       dhs, dgus, hs, dxs, dyTT, hsT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
+  bool long_k, shared_long;
 };
 
 BwdLayout bwd_layout(const moe_desc &D) {
@@ -620,10 +621,13 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.hg = take(R * f * s);
   L.dxr = take(R * d * s);
   L.poff = take((E + 1) * 4);
+  // weight gradients: when experts hold many rows the second operand is read K-major (x
+  // gathered to [R, d], H and the shared expert's H as they are); padded transposes otherwise
+  L.long_k = R / E >= 256 && d >= 256 && f >= 256;
   L.dyT = take(d * L.Rpad * s);
-  L.hgT = take(f * L.Rpad * s);
+  L.hgT = take(L.long_k ? 0 : f * L.Rpad * s);
   L.dguT = take(2 * f * L.Rpad * s);
-  L.xT = take(d * L.Rpad * s);
+  L.xT = take(L.long_k ? R * d * s : d * L.Rpad * s);
   L.dgate = take(T * k * 4);
   L.dl = take(T * E * 4);
   L.dl16 = take(T * L.Epad * s);
@@ -639,8 +643,9 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dgus = take(fs ? T * 2 * fs * s : 0);
   L.hs = take(fs ? T * fs * s : 0);
   L.dxs = take(fs ? T * d * s : 0);
+  L.shared_long = T >= 256 && d >= 256 && fs >= 256;
   L.dyTT = take(fs ? d * L.Tpad * s : 0);
-  L.hsT = take(fs ? fs * L.Tpad * s : 0);
+  L.hsT = take(fs && !L.shared_long ? fs * L.Tpad * s : 0);
   L.dgusT = take(fs ? 2 * fs * L.Tpad * s : 0);
   L.total = o;
   return L;
@@ -776,23 +781,44 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                        W(L.dxr));
     a.w_kn = true;
     MOE_TRY(gemm(a, "dx grouped GEMM"));
-    // weight gradients, grouped over each expert's rows (padded to 32, zeros in the pad)
-    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad, 0,
+    // weight gradients, grouped over each expert's rows
+    if (L.long_k) {
+      // many rows per expert (matrix-core bound): the first operand transposed (padded
+      // groups), the second K-major straight from the row-major activations (x rows
+      // gathered into expert order)
+      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad,
+                                             0, stream),
+                  "dy transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad,
+                                             W(L.dguT), L.Rpad, 0, stream),
+                  "dGU transpose"));
+      MOE_TRY(hcall(moe::launch_gather_rows(x, row_token, rows_dev, R, d, 2, W(L.xT), stream), "x gather"));
+      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyT), L.Rpad, poff, W(L.hg), R, offsets, E, d, f, grads->dw_down,
                                            stream),
-                "dy transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.xT), L.Rpad, 0,
-                                           stream),
-                "x transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.hgT),
-                                           L.Rpad, 0, stream),
-                "H transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.dguT),
-                                           L.Rpad, 0, stream),
-                "dGU transpose"));
-    MOE_TRY(hcall(wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, R / E),
-                "dW_down"));
-    MOE_TRY(hcall(wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up, R / E),
-                "dW_gate_up"));
+                  "dW_down"));
+      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dguT), L.Rpad, poff, W(L.xT), R, offsets, E, 2 * f, d,
+                                           grads->dw_gate_up, stream),
+                  "dW_gate_up"));
+    } else {
+      // few rows per expert (write bound): transposed operands, each expert's rows padded
+      // to 32 with zeros
+      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad,
+                                             0, stream),
+                  "dy transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.xT), L.Rpad, 0,
+                                             stream),
+                  "x transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.hgT),
+                                             L.Rpad, 0, stream),
+                  "H transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad,
+                                             W(L.dguT), L.Rpad, 0, stream),
+                  "dGU transpose"));
+      MOE_TRY(hcall(wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, R / E),
+                  "dW_down"));
+      MOE_TRY(hcall(wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up, R / E),
+                    "dW_gate_up"));
+    }
   } else {
     MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_down, (int64_t)E * d * f * s / 4, 0u, stream), "zero"));
     MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_gate_up, (int64_t)E * 2 * f * d * s / 4, 0u, stream), "zero"));
@@ -839,19 +865,35 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
       a.w_kn = true;  // W_sgu [2 f_s, d] is K-major for [dG dU] W_sgu
       MOE_TRY(gemm(a, "shared dx"));
     }
-    MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT), L.Tpad,
-                                           0, stream),
-                "dy transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.hsT),
-                                           L.Tpad, 0, stream),
-                "shared H transpose"));
-    MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
-                                           W(L.dgusT), L.Tpad, 0, stream),
-                "shared dGU transpose"));
-    MOE_TRY(hcall(wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false, grads->dw_shared_down, T),
-                "dW_shared_down"));
-    MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false, grads->dw_shared_gate_up, T),
-                "dW_shared_gate_up"));
+    if (L.shared_long) {
+      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT),
+                                             L.Tpad, 0, stream),
+                  "dy transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
+                                             W(L.dgusT), L.Tpad, 0, stream),
+                  "shared dGU transpose"));
+      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyTT), L.Tpad, tpoff, W(L.hs), T, sh_off, 1, d, fs,
+                                           grads->dw_shared_down, stream),
+                  "dW_shared_down"));
+      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dgusT), L.Tpad, tpoff, x, T, sh_off, 1, 2 * fs, d,
+                                           grads->dw_shared_gate_up, stream),
+                  "dW_shared_gate_up"));
+    } else {
+      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT),
+                                             L.Tpad, 0, stream),
+                  "dy transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.hsT),
+                                             L.Tpad, 0, stream),
+                  "shared H transpose"));
+      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
+                                             W(L.dgusT), L.Tpad, 0, stream),
+                  "shared dGU transpose"));
+      MOE_TRY(hcall(wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false, grads->dw_shared_down, T),
+                  "dW_shared_down"));
+      MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false,
+                          grads->dw_shared_gate_up, T),
+                  "dW_shared_gate_up"));
+    }
     dxs = W(L.dxs);
   }
 

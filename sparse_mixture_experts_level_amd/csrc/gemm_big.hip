@@ -109,7 +109,8 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
                                                                          OutT *__restrict__ out, int n_tiles,
                                                                          int64_t lda, int64_t ldb, int M,
                                                                          float *__restrict__ split_out,
-                                                                         int64_t split_stride) {
+                                                                         int64_t split_stride,
+                                                                         const int32_t *__restrict__ offsets_b) {
   constexpr int BK = BKP;                        // K per step: 32 or 64
   constexpr int RB = BK * 2;                     // bytes per tile row
   constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
   static_assert(NBUF >= 2 && NBUF <= 4, "stages");
   static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(!BKN || (!SWIGLU && !WG && BK == 32 && WN_W == 4), "K-major weights: plain store, 32-wide steps");
+  static_assert(!BKN || (!SWIGLU && BK == 32 && WN_W == 4), "K-major operands: plain store, 32-wide steps");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[NBUF > 2 ? TILE : 16],
       sA3[NBUF > 3 ? TILE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[NBUF > 2 ? TILE : 16],
@@ -138,7 +139,8 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   auto swz = [&](int r) -> int { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
-  int m0, rows, n0, nk, ks = 0, kbase = 0;
+  int krow[IPW];  // WG with K-major operands: this lane's k-row within a step, per instruction
+  int m0, rows, n0, nk, ks = 0, kbase = 0, kvalid = 0;
   bool partial = false;
   rsrc_t ares, wres;
   OutT *obase;
@@ -240,6 +242,31 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     n0 = nt * BG_BN;
     const int kb = offsets[g];
     const int64_t kg = offsets[g + 1] - kb;
+    if constexpr (BKN) {
+      // A transposed as below (group g's [M, K_g] block at offsets[g] * M, K_g a multiple of
+      // 32, zero padding); W K-major: [ldb rows, n_out] row-major with group g's k-rows
+      // offsets_b[g] .. offsets_b[g+1] - 1 (unpadded; k-rows past them read zeros).
+      // Instruction blk of W brings k-rows 2 blk and 2 blk + 1 of the step (512 bytes
+      // each), chunk p of a row at slot p ^ (4 (row & 3)), as the forward mode's W.
+      nk = (int)(kg / BK);
+      const int kbb = offsets_b[g];
+      kvalid = offsets_b[g + 1] - kbb;
+      ares = make_rsrc(A, (uint32_t)(M * lda * 2));
+      wres = make_rsrc(W, (uint32_t)(ldb * n_out * 2));
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int blk = wave * IPW + i;
+        const int r = blk * RPI + lane / NCH;
+        const int c = (lane % NCH) ^ swz(r);
+        agoff[i] = r < rows ? (uint32_t)(((int64_t)kb * M + (int64_t)(m0 + r) * kg) * 2) + (uint32_t)c * 16u : kOob;
+        const int kr = 2 * blk + (lane >> 5);
+        const int cs = ((lane & 31) ^ (4 * (kr & 3))) << 3;
+        krow[i] = kr;
+        bgoff[i] = n0 + cs < n_out ? ((uint32_t)(kbb + kr) * (uint32_t)n_out + (uint32_t)(n0 + cs)) * 2u : kOob;
+      }
+      obase = out + (size_t)g * M * n_out;
+      ostride = n_out;
+    } else {
     nk = (int)(kg / BK);
     ares = make_rsrc(A, (uint32_t)(M * lda * 2));
     wres = make_rsrc(W, (uint32_t)(n_out * ldb * 2));
@@ -254,18 +281,21 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     }
     obase = out + (size_t)g * M * n_out;
     ostride = n_out;
+    }
   }
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
     const uint32_t kc = (uint32_t)(kbase + kt) * (BK * 2);
-    // K-major weights advance BK rows of n_out elements per step
+    // K-major operands advance BK rows per step
     const uint32_t kcb = BKN ? (uint32_t)(kbase + kt) * (uint32_t)BK * (uint32_t)n_out * 2u : kc;
     uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
+      bool okb = ok;
+      if constexpr (BKN && WG) okb = ok && kt * BK + krow[i] < kvalid;  // k-rows past the group: zeros
       buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kc : kOob, la + blk * 1024);
-      buf_ld16_lds(wres, (ok && bgoff[i] != kOob) ? bgoff[i] + kcb : kOob, lb + blk * 1024);
+      buf_ld16_lds(wres, (okb && bgoff[i] != kOob) ? bgoff[i] + kcb : kOob, lb + blk * 1024);
     }
   };
   // K-major weights: the 32x32x16 MFMA fragment of weight block j (columns nb .. nb + 31 of
@@ -444,8 +474,10 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   // the four consecutive columns j * 32 + 8 * (r / 4) + 4 * (l / 32) + (r % 4), r % 4 =
   // 0..3.  Each wave stages its 128-row part of the tile in its own 16 KB stage array,
   // then stores whole 16-byte column runs, 8 .. 16 lanes per row.
-  static_assert(NBUF == 4 && WN_W == 4 && BK == 32, "the epilogue uses the eight 16 KB stage arrays");
-  uint8_t *stage = wave < 4 ? bufA(wave) : bufB(wave - 4);
+  static_assert(WN_W == 4 && NBUF * TILE >= 4 * 16384, "the epilogue needs 16 KB per wave in the stages");
+  // wave w's 16 KB: the w-th 16 KB of the A stages (waves 0-3) or of the B stages (4-7)
+  constexpr int PER = TILE / 16384;  // 16 KB regions per stage array
+  uint8_t *stage = (wave < 4 ? bufA((wave & 3) / PER) : bufB((wave & 3) / PER)) + ((wave & 3) % PER) * 16384;
   const int lr = lane & 31, lh = lane >> 5;
   if constexpr (SWIGLU) {
     static_assert(sizeof(OutT) == 2 && NI == 2, "SwiGLU: bf16 output, one gate and one up block per wave");
@@ -546,7 +578,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT, false, BKN>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride);
+                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t blocks = std::min<int64_t>((rows_total_max * a.n_out / 8 + 255) / 256, 4096);
@@ -569,6 +601,23 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_t
 
 // Weight gradients: out[g][m][n] = sum over k in [koff[g], koff[g+1]) of AT[m][k] BT[n][k],
 // group ranges multiples of 32; an empty group writes zeros.
+// Weight gradients with the second operand K-major: out[g][m][n] = sum over k < K_g of
+// AT_g[m][k] B[off_b[g] + k][n], AT_g = AT + poff[g] * M with row stride K_g = poff[g+1] -
+// poff[g] (group-major transposed, zero padded to multiples of 32), B [b_rows, N] row-major
+// with group g's rows off_b[g] .. off_b[g+1] - 1 (k past them: zero).  M and N multiples of 8.
+hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
+                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s) {
+  if (N % 8 || M % 8) return hipErrorInvalidValue;
+  const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
+  const int64_t grid = (int64_t)G * m_tiles * n_tiles;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true, true>), dim3((unsigned)grid),
+                     dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G,
+                     static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
+                     M, nullptr, (int64_t)0, off_b);
+  return hipGetLastError();
+}
+
 hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
                             int N, bool out_f32, void *out, hipStream_t s) {
   if (N % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
@@ -578,12 +627,12 @@ hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, float, true>), dim3((unsigned)grid), dim3(512),
                        0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<float *>(out), n_tiles, lda,
-                       ldb, M, nullptr, (int64_t)0);
+                       ldb, M, nullptr, (int64_t)0, nullptr);
   else
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true>), dim3((unsigned)grid),
                        dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
-                       ldb, M, nullptr, (int64_t)0);
+                       ldb, M, nullptr, (int64_t)0, nullptr);
   return hipGetLastError();
 }
 

@@ -131,6 +131,11 @@ hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32
 int wgrad_ksplit(int M, int N, int64_t K);
 hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int M,
                                int N, int64_t K, float *part, float *out, hipStream_t s);
+// out[g][m][n] = sum over k < K_g of AT_g[m][k] B[off_b[g] + k][n]: AT group-major transposed
+// (as for launch_wgrad_big, K_g = poff[g+1] - poff[g]), B [b_rows, N] row-major (K-major,
+// unpadded; k past the group's rows reads zero); 256 x 256 tiles.
+hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
+                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s);
 hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
                             int N, bool out_f32, void *out, hipStream_t s);
 hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
