@@ -125,3 +125,103 @@ def test_backward_switch_workload_full_size():
     ref = _reference(w, inp, cap, layer, dy)
     errs = _compare(w, ref, dx, grads)
     say(f"errors {errs}")
+
+
+def _unit_grads(x64, dy64, w_gate_up, w_down, toks, scale, units):
+    """The weight gradients of single hidden units of one SwiGLU FFN: the units of a
+    SwiGLU FFN are independent (y = sum over u of W_d[:, u] H_u), so the oracle's FFN
+    backward on the sub-FFN of unit u (gate row u, up row f + u, down column u) gives
+    exactly rows u and f + u of dW_gate_up and column u of dW_down."""
+    f = w_down.shape[-1]
+    out = {}
+    for u in units:
+        wgu = np.stack([to_np(w_gate_up[u]), to_np(w_gate_up[f + u])]).astype(np.float64)
+        wd = to_np(w_down[:, u:u + 1]).astype(np.float64)
+        b = oracle.swiglu_ffn_backward(x64[toks], wgu, wd, dy64[toks], scale=scale)
+        out[u] = (b["dw_gate_up"], b["dw_down"][:, 0])
+    return out
+
+
+def _vec_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got))
+    m = np.abs(ref).max()
+    if m == 0:
+        assert np.all(got == 0)
+        return 0.0
+    return float(np.abs(got - ref).max() / m)
+
+
+@pytest.mark.parametrize("name,ntok", [("mixtral_bf16", 8), ("deepseek_v3_bf16", 6), ("gptoss_decode_bf16", 16)])
+def test_backward_full_size_sampled(name, ntok):
+    """Full-size workloads (the bench's configuration) on sampled outputs the oracle computes
+    one by one: dx of sampled tokens (their kept assignments' FFN backward, the router term
+    and the shared expert, from the oracle's pieces), and single hidden units of the weight
+    gradients of the most, a middle and the least loaded expert and of the shared expert."""
+    w = wl.get_workload(name)
+    say(f"backward {name} full size, sampled")
+    inp, cap, layer, dy, dx, grads, _ = _run(w, seed=0)
+    T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
+    r = {kk: to_np(v) for kk, v in layer.routing.items()}
+    ids, slot, gates = r["topk_ids"].astype(np.int64), r["slot"], r["topk_gates"].astype(np.float64)
+    serving = ids
+    x64 = to_np(inp.x).astype(np.float64)
+    dy64 = to_np(dy).astype(np.float64)
+    wr = to_np(inp.w_router).astype(np.float64)
+    off = None if inp.logit_offset is None else to_np(inp.logit_offset)
+    gu, dn = HostExperts(inp.w_gate_up), HostExperts(inp.w_down)
+    sgu = sd = None
+    if fs:
+        sgu = to_np(inp.w_shared_gate_up).astype(np.float64)
+        sd = to_np(inp.w_shared_down).astype(np.float64)
+
+    # dx of sampled tokens
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([rng.choice(T, max(ntok - 2, 1), replace=False), [T - 2, T - 1]]))[:ntok]
+    got = to_np(dx)[toks]
+    ref = np.zeros((toks.size, d))
+    for n, t in enumerate(toks):
+        dg = np.zeros((1, k))
+        for j in range(k):
+            if slot[t, j] >= 0:
+                e = int(serving[t, j])
+                b = oracle.swiglu_ffn_backward(x64[t:t + 1], gu[e], dn[e], dy64[t:t + 1], scale=gates[t, j:j + 1])
+                ref[n] += b["dx"][0]
+                dg[0, j] = b["dscale"][0]
+        lt = oracle.router_logits(x64[t:t + 1], wr, off)
+        ref[n] += (oracle.topk_gates_backward(lt, ids[t:t + 1], dg) @ wr)[0]
+        if fs:
+            ref[n] += oracle.swiglu_ffn_backward(x64[t:t + 1], sgu, sd, dy64[t:t + 1])["dx"][0]
+    errs = {"dx": row_rel_err(got, ref)}
+
+    # single units of the weight gradients of three experts
+    counts = np.diff(r["expert_offsets"].astype(np.int64))
+    nz = np.flatnonzero(counts)
+    order = nz[np.argsort(counts[nz], kind="stable")]
+    experts = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
+    units = sorted({0, f - 1, int(rng.integers(1, f - 1))})
+    dgu_all, ddn_all = grads["dw_gate_up"], grads["dw_down"]
+    for e in experts:
+        tt, jj = np.nonzero((slot >= 0) & (serving == e))  # the expert's kept rows
+        etoks, scale = tt, gates[tt, jj]
+        ref_u = _unit_grads(x64, dy64, inp.w_gate_up[e], inp.w_down[e], etoks, scale, units)
+        for u, (rgu, rdn) in ref_u.items():
+            g_gu = to_np(dgu_all[e, [u, f + u]])
+            errs[f"dw_gate_up[{e}][{u}]"] = max(row_rel_err(g_gu[0:1], rgu[0:1]), row_rel_err(g_gu[1:2], rgu[1:2]))
+            errs[f"dw_down[{e}][:,{u}]"] = _vec_rel_err(to_np(ddn_all[e, :, u]), rdn)
+    empty = np.flatnonzero(counts == 0)
+    if empty.size:
+        e0 = int(empty[0])
+        assert torch.all(dgu_all[e0] == 0) and torch.all(ddn_all[e0] == 0)
+    if fs:
+        allt = np.arange(T)
+        su = sorted({0, fs - 1, int(rng.integers(1, fs - 1))})
+        ref_u = _unit_grads(x64, dy64, inp.w_shared_gate_up, inp.w_shared_down, allt, None, su)
+        for u, (rgu, rdn) in ref_u.items():
+            g_gu = to_np(grads["dw_shared_gate_up"][[u, fs + u]])
+            errs[f"dw_shared_gate_up[{u}]"] = max(row_rel_err(g_gu[0:1], rgu[0:1]), row_rel_err(g_gu[1:2], rgu[1:2]))
+            errs[f"dw_shared_down[:,{u}]"] = _vec_rel_err(to_np(grads["dw_shared_down"][:, u]), rdn)
+    worst = max(errs.values())
+    say(f"  worst sampled error {worst:.3e} over {len(errs)} checks (experts {experts}, units {units})")
+    assert worst <= TOL, errs
