@@ -83,6 +83,11 @@ def _to_dev(inp):
     (200, 128, 8, 8, 64, None, 0, None),  # k = E without capacity: the dense mixture
     (64, 128, 4, 1, 64, 0.2, 64, "boost4"),  # heavy dropping with a shared expert
     (600, 256, 2, 1, 4096, None, 0, None),   # large-tile regime with few tiles: down cut along K
+    # small batches
+    (16, 256, 32, 4, 128, None, 0, None),    # decode-sized
+    (64, 128, 256, 8, 64, 1.0, 64, "boost4"),  # T k = 512 and E = 256, the largest such batch, drops
+    (1, 64, 8, 2, 64, None, 0, None),        # a single token
+    (37, 192, 20, 3, 64, 0.5, 0, "boost4"),  # ragged tiles, drops
 ])
 def test_small_bf16_layers_all_tokens(T, d, E, k, f, cf, fs, offset):
     w = wl.Workload("small", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset=offset)
@@ -197,6 +202,7 @@ def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards)
     (513, 128, 16, 4, 128, 2.0, "rank", "reroute"),
     (513, 128, 16, 4, 128, 0.5, "token", "reroute"),   # every expert full after pass 1
     (257, 64, 4, 1, 64, 0.75, "token", "reroute"),
+    (48, 128, 16, 2, 64, 0.5, "rank", "drop"),          # small batch
 ])
 def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
     """moe_forward with the rank-major fill and/or redirection of overflow vs the oracle."""
