@@ -29,20 +29,15 @@ namespace {
 constexpr int BG_BM = 256, BG_BN = 256;
 
 // Pipeline: K advances in steps of 32.  Operand tiles go from HBM straight into LDS
-// (buffer loads with an LDS destination, no registers), into NBUF stages that are
-// separate LDS arrays, NBUF - 1 steps ahead of the MFMAs.  Each step: wait for this
-// wave's loads of the current stage (a fixed count of younger loads may stay in
-// flight), one barrier (all waves' loads landed; all waves are done with the stage
-// about to be refilled), issue the loads of step kt + NBUF - 1, then the MFMAs.
+// (buffer loads with an LDS destination, no registers), into four stages that are
+// separate LDS arrays, three steps ahead of the MFMAs (schedule at the main loop).
 //
 // LDS tile layout: 256 rows of 64 bytes (4 chunks of 16 bytes); chunk c of row r is
 // stored at chunk c ^ ((r >> 2) & 3).  An MFMA operand load reads one chunk of 32
 // consecutive rows; LDS serves 16 lanes (256 bytes, 64 banks) at a time, and any 16
 // consecutive rows then fall on 16 distinct 16-byte bank groups.  One load instruction fills 1 KB = 16 rows; lane p of it
 // brings row 16 * blk + p / 4, stored chunk p % 4.
-//
-// WN_W: waves along the weight rows (2: four waves of 128 x 128, one per SIMD;
-// 4: eight waves of 128 x 64, two per SIMD).
+
 // K splits for a launch with `tiles` output tiles and `steps` 32-wide K steps, for
 // launches of fewer tiles than CUs: the split count (at most 4, at least 64 steps per
 // split) whose blocks fill the 256 CUs' last round best, the larger one on a tie.
@@ -98,9 +93,8 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // A_g = A + offsets[g] * M and W_g = W + offsets[g] * n_out, K-contiguous with row stride
 // K_g (group-major transposed activations; lda and ldb bound the buffers), every group
 // M x n_out, written at out + g * M * n_out.
-template <bool SWIGLU, int WN_W, int NBUF, bool PING, int BKP = 32, typename OutT = bf16_t, bool WG = false,
-          bool BKN = false>
-__global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
+template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
                                                                          const int32_t *__restrict__ offsets, int G,
@@ -111,32 +105,30 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
                                                                          float *__restrict__ split_out,
                                                                          int64_t split_stride,
                                                                          const int32_t *__restrict__ offsets_b) {
-  constexpr int BK = BKP;                        // K per step: 32 or 64
+  // Eight waves (two per SIMD) in a 2 x 4 arrangement, each 128 rows x 64 weight rows.
+  constexpr int WN_W = 4;                        // waves along the weight rows
+  constexpr int NBUF = 4;                        // LDS stages
+  constexpr int BK = 32;                         // K per step
   constexpr int RB = BK * 2;                     // bytes per tile row
-  constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row (4 or 8)
-  constexpr int RPI = 1024 / RB;                 // tile rows per 1 KB load instruction (16 or 8)
-  constexpr int NT = 128 * WN_W;                 // threads
-  constexpr int NW = NT / 64;                    // waves
+  constexpr int NCH = RB / 16;                   // 16-byte chunks per tile row
+  constexpr int RPI = 1024 / RB;                 // tile rows per 1 KB load instruction
+  constexpr int NW = 8;                          // waves
   constexpr int NI = BG_BN / WN_W / 32;          // 32-wide weight blocks per wave
   constexpr int TILE = BG_BM * BK * 2;           // 16 KB per operand and stage
   constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
-  static_assert(NBUF >= 2 && NBUF <= 4, "stages");
-  static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(!BKN || (!SWIGLU && BK == 32 && WN_W == 4), "K-major operands: plain store, 32-wide steps");
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[NBUF > 2 ? TILE : 16],
-      sA3[NBUF > 3 ? TILE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[NBUF > 2 ? TILE : 16],
-      sB3[NBUF > 3 ? TILE : 16];
+  static_assert(!BKN || !SWIGLU, "K-major operands: plain store");
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
   auto bufB = [&](int b) -> uint8_t * { return b == 0 ? sB0 : b == 1 ? sB1 : b == 2 ? sB2 : sB3; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN_W, wn = wave % WN_W;
-  // Swizzle of a row's 16-byte chunks.  32-wide steps: 64-byte rows, chunk c of row r
-  // at c ^ ((r >> 2) & 3); 64-wide steps: 128-byte rows, at c ^ ((r >> 1) & 7).  Either
-  // way 16 consecutive rows read at one logical chunk land on 16 distinct 16-byte bank
-  // groups of a 256-byte LDS cycle, and rows 32 apart keep the same swizzle.
-  auto swz = [&](int r) -> int { return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7); };
+  // Swizzle of a row's 16-byte chunks (64-byte rows): chunk c of row r at
+  // c ^ ((r >> 2) & 3), so 16 consecutive rows read at one logical chunk land on 16
+  // distinct 16-byte bank groups of a 256-byte LDS cycle, and rows 32 apart keep the
+  // same swizzle.
+  auto swz = [&](int r) -> int { return (r >> 2) & 3; };
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
   int krow[IPW];  // WG with K-major operands: this lane's k-row within a step, per instruction
@@ -331,60 +323,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
   const int ar0 = wm * 128 + (lane & 31);
   const int br0 = SWIGLU ? wn * (NI / 2) * 32 + (lane & 31) : wn * NI * 32 + (lane & 31);
   auto roff = [&](int r, int c) -> int { return r * RB + ((c ^ swz(r)) << 4); };
-  auto compute = [&](int b) {
-    const uint8_t *la = bufA(b), *lb = bufB(b);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      const uint8_t *pa = la + roff(ar0, c);
-      const uint8_t *pb = lb + roff(br0, c);
-      u32x4 af[4], bfr[NI];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4 *>(pa + i * 32 * RB);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        if constexpr (BKN) {
-          bfr[j] = kn_frag(lb, kk, wn * NI * 32 + j * 32);
-        } else {
-          const int dr = SWIGLU ? (j < NI / 2 ? j * 32 : 128 + (j - NI / 2) * 32) : j * 32;
-          bfr[j] = *reinterpret_cast<const u32x4 *>(pb + dr * RB);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
-    }
-  };
-
-  if constexpr (!PING) {
-    // prologue: steps 0 .. NBUF-2 in flight
-#pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b) issue(b, b);
-    for (int k0 = 0; k0 < nk; k0 += NBUF) {
-#pragma unroll
-      for (int b = 0; b < NBUF; ++b) {
-        const int kt = k0 + b;
-        if (kt >= nk) break;
-        // this wave's loads of step kt are done once at most (NBUF - 2) younger steps remain
-        if constexpr (NBUF == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if constexpr (NBUF == 3) {
-          if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-          if constexpr (IPW == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        }
-        if constexpr (NBUF == 4) {
-          if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-          if constexpr (IPW == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        }
-        // Bare barrier: a fenced one would also wait for the younger loads still in
-        // flight.  LDS reads of the stage refilled next are complete (lgkmcnt(0)).
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        issue(kt + NBUF - 1, (b + NBUF - 1) % NBUF);
-        compute(b);
-      }
-    }
-  } else {
+  {
     // Ping-pong: the two waves of each SIMD (group 0 = waves 0..3, group 1 = waves
     // 4..7) alternate between a memory phase -- issue the loads of step k + 3, wait
     // for this wave's loads of step k + 1, read step k's operand fragments from LDS --
@@ -396,16 +335,13 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     //   that follows both groups' reads of its previous step k - 1.
     // Prefetch distance D = NBUF - 1 steps; a wave in mem(k) issues step k + D and
     // completes its own loads of step k + 1 (at most D - 1 younger steps in flight).
-    static_assert(IPW == 2 || IPW == 4, "ping-pong schedule is written for eight waves");
     constexpr int D = NBUF - 1;
+    static_assert(IPW == 2 && D == 3, "the waits below count two loads per operand and step, three steps ahead");
     const bool second = wave >= 4;
     u32x4 af[BK / 16][4], bfr[BK / 16][NI];
     auto wait_next = [&]() {
-      if constexpr (D == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if constexpr (D == 2 && IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      if constexpr (D == 2 && IPW == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      if constexpr (D == 3 && IPW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      if constexpr (D == 3 && IPW == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      // the two younger steps' loads (2 operands x 2 instructions each) may stay in flight
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     };
     auto mem = [&](int kt, int b) {
       issue(kt + D, (b + D) % NBUF);
@@ -448,8 +384,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
     // prologue: steps 0 .. D-1 issued; step 0 landed for every wave before the first read
 #pragma unroll
     for (int b = 0; b < D; ++b) issue(b, b);
-    if constexpr (D == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else wait_next();
+    wait_next();
     bar();
     if (second) bar();
     for (int k0 = 0; k0 < nk; k0 += NBUF) {
@@ -565,7 +500,7 @@ __global__ __launch_bounds__(128 * WN_W, 1) void grouped_gemm_big_kernel(const b
 
 }  // namespace
 
-template <bool SWIGLU, int WN_W, int NBUF, bool PING = false, int BKP = 32, typename OutT = bf16_t, bool BKN = false>
+template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
@@ -575,7 +510,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
   const int64_t split_stride = rows_total_max * a.n_out;
   const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, WN_W, NBUF, PING, BKP, OutT, false, BKN>), dim3((unsigned)grid), dim3(128 * WN_W), 0,
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN>), dim3((unsigned)grid), dim3(512), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr);
@@ -583,7 +518,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   if (e != hipSuccess || !split) return e;
   const int64_t blocks = std::min<int64_t>((rows_total_max * a.n_out / 8 + 255) / 256, 4096);
   hipLaunchKernelGGL(big_split_reduce_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, split,
-                     split_stride, a.offsets, a.num_groups, n_tiles, a.K / BKP, a.n_out,
+                     split_stride, a.offsets, a.num_groups, n_tiles, a.K / 32, a.n_out,
                      static_cast<bf16_t *>(a.out));
   return hipGetLastError();
 }
@@ -592,11 +527,10 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.w_kn) {  // K-major weights: bf16 output, no SwiGLU
     if (a.swiglu || a.out_f32) return hipErrorInvalidValue;
-    return launch_big<false, 4, 4, true, 32, bf16_t, true>(a, rows_total_max, s);
+    return launch_big<false, bf16_t, true>(a, rows_total_max, s);
   }
-  if (a.swiglu) return launch_big<true, 4, 4, true>(a, rows_total_max, s);
-  return a.out_f32 ? launch_big<false, 4, 4, true, 32, float>(a, rows_total_max, s)
-                   : launch_big<false, 4, 4, true>(a, rows_total_max, s);
+  if (a.swiglu) return launch_big<true>(a, rows_total_max, s);
+  return a.out_f32 ? launch_big<false, float>(a, rows_total_max, s) : launch_big<false>(a, rows_total_max, s);
 }
 
 // Weight gradients: out[g][m][n] = sum over k in [koff[g], koff[g+1]) of AT[m][k] BT[n][k],
@@ -611,7 +545,7 @@ hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff,
   const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true, true>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true>), dim3((unsigned)grid),
                      dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G,
                      static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
                      M, nullptr, (int64_t)0, off_b);
@@ -624,12 +558,12 @@ hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t
   const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
   if (out_f32)
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, float, true>), dim3((unsigned)grid), dim3(512),
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float, true>), dim3((unsigned)grid), dim3(512),
                        0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<float *>(out), n_tiles, lda,
                        ldb, M, nullptr, (int64_t)0, nullptr);
   else
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, 4, 4, true, 32, bf16_t, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true>), dim3((unsigned)grid),
                        dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
                        static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
                        ldb, M, nullptr, (int64_t)0, nullptr);
