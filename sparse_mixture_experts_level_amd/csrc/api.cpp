@@ -595,8 +595,8 @@ namespace {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdLayout {
-  size_t gu, dhp, dgu, hg, dxr, poff, dyT, hgT, dguT, xT, dgate, dl, dl16, dlT, xTT, wr_part, dxrt, tpoff, sh_off, gus,
-      dhs, dgus, hs, dxs, dyTT, hsT, dgusT, total;
+  size_t gu, dhp, dgu, hg, dxr, poff, dyT, dguT, xT, dgate, dl, dl16, dlT, xTT, wr_part, dxrt, tpoff, sh_off, gus,
+      dhs, dgus, hs, dxs, dyTT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
   bool long_k, shared_long;
 };
@@ -621,13 +621,13 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.hg = take(R * f * s);
   L.dxr = take(R * d * s);
   L.poff = take((E + 1) * 4);
-  // weight gradients: when experts hold many rows the second operand is read K-major (x
-  // gathered to [R, d], H and the shared expert's H as they are); padded transposes otherwise
+  // weight gradients: operands read K-major from the row-major activations (x and dy rows
+  // gathered to [R, d]); when experts hold many rows the first operand is transposed instead
+  // (padded groups), since the matrix cores then need the LDS read path for themselves
   L.long_k = R / E >= 256 && d >= 256 && f >= 256;
-  L.dyT = take(d * L.Rpad * s);
-  L.hgT = take(L.long_k ? 0 : f * L.Rpad * s);
-  L.dguT = take(2 * f * L.Rpad * s);
-  L.xT = take(L.long_k ? R * d * s : d * L.Rpad * s);
+  L.dyT = take(L.long_k ? d * L.Rpad * s : R * d * s);  // transposed, or gathered rows
+  L.dguT = take(L.long_k ? 2 * f * L.Rpad * s : 0);
+  L.xT = take(R * d * s);                                // gathered rows
   L.dgate = take(T * k * 4);
   L.dl = take(T * E * 4);
   L.dl16 = take(T * L.Epad * s);
@@ -644,9 +644,8 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.hs = take(fs ? T * fs * s : 0);
   L.dxs = take(fs ? T * d * s : 0);
   L.shared_long = T >= 256 && d >= 256 && fs >= 256;
-  L.dyTT = take(fs ? d * L.Tpad * s : 0);
-  L.hsT = take(fs && !L.shared_long ? fs * L.Tpad * s : 0);
-  L.dgusT = take(fs ? 2 * fs * L.Tpad * s : 0);
+  L.dyTT = take(fs && L.shared_long ? d * L.Tpad * s : 0);
+  L.dgusT = take(fs && L.shared_long ? 2 * fs * L.Tpad * s : 0);
   L.total = o;
   return L;
 }
@@ -745,22 +744,13 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   auto gemm = [&](const moe::GroupedGemmArgs &a, const char *what) {
     return hcall(moe::launch_grouped_gemm_bf16(a, stream), what);
   };
-  // weight-gradient GEMM: 256 x 256 tiles on the LDS pipeline when the groups'
-  // contraction ranges are long (matrix-core bound), the write-bound 128 x 128 kernel for
-  // short ranges (few rows per expert) and for outputs under 256 rows or columns
-  auto wgrad = [&](const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M, int N,
-                   bool f32, void *out, int64_t avg_k) {
-    return avg_k >= 256 && M >= 256 && N >= 256
-               ? moe::launch_wgrad_big(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream)
-               : moe::launch_wgrad(AT, lda, BT, ldb, koff, G, M, N, f32, out, stream);
-  };
   int32_t *poff = at<int32_t>(ws, L.poff), *tpoff = at<int32_t>(ws, L.tpoff), *sh_off = at<int32_t>(ws, L.sh_off);
   MOE_TRY(hcall(moe::launch_fill_i32(tpoff, 2, 0, (int32_t)L.Tpad, stream), "offsets"));
   MOE_TRY(hcall(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "offsets"));
 
   // ---- routed experts
   if (R > 0) {
-    MOE_TRY(hcall(moe::launch_pad_offsets(offsets, E, poff, stream), "padded offsets"));
+    if (L.long_k) MOE_TRY(hcall(moe::launch_pad_offsets(offsets, E, poff, stream), "padded offsets"));
     // G | U of every kept row, recomputed from x
     MOE_TRY(gemm(gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d,
                            W(L.gu), true),
@@ -800,24 +790,14 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                                            grads->dw_gate_up, stream),
                   "dW_gate_up"));
     } else {
-      // few rows per expert (write bound): transposed operands, each expert's rows padded
-      // to 32 with zeros
-      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad,
-                                             0, stream),
-                  "dy transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.xT), L.Rpad, 0,
-                                             stream),
-                  "x transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hg), 0, R, f, 1, nullptr, offsets, poff, E, L.Rpad, W(L.hgT),
-                                             L.Rpad, 0, stream),
-                  "H transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad,
-                                             W(L.dguT), L.Rpad, 0, stream),
-                  "dGU transpose"));
-      MOE_TRY(hcall(wgrad(W(L.dyT), L.Rpad, W(L.hgT), L.Rpad, poff, E, d, f, false, grads->dw_down, R / E),
+      // few rows per expert (write bound): both operands K-major straight from the
+      // row-major activations (dy and x rows gathered into expert order), no transposes
+      MOE_TRY(hcall(moe::launch_gather_rows(dy, row_token, rows_dev, R, d, 2, W(L.dyT), stream), "dy gather"));
+      MOE_TRY(hcall(moe::launch_gather_rows(x, row_token, rows_dev, R, d, 2, W(L.xT), stream), "x gather"));
+      MOE_TRY(hcall(moe::launch_wgrad_kn(W(L.dyT), R, W(L.hg), R, offsets, E, d, f, grads->dw_down, stream),
                   "dW_down"));
-      MOE_TRY(hcall(wgrad(W(L.dguT), L.Rpad, W(L.xT), L.Rpad, poff, E, 2 * f, d, false, grads->dw_gate_up, R / E),
-                    "dW_gate_up"));
+      MOE_TRY(hcall(moe::launch_wgrad_kn(W(L.dgu), R, W(L.xT), R, offsets, E, 2 * f, d, grads->dw_gate_up, stream),
+                  "dW_gate_up"));
     }
   } else {
     MOE_TRY(hcall(moe::launch_fill_u32(grads->dw_down, (int64_t)E * d * f * s / 4, 0u, stream), "zero"));
@@ -879,19 +859,9 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
                                            grads->dw_shared_gate_up, stream),
                   "dW_shared_gate_up"));
     } else {
-      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT),
-                                             L.Tpad, 0, stream),
-                  "dy transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.hs), 0, T, fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.hsT),
-                                             L.Tpad, 0, stream),
-                  "shared H transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
-                                             W(L.dgusT), L.Tpad, 0, stream),
-                  "shared dGU transpose"));
-      MOE_TRY(hcall(wgrad(W(L.dyTT), L.Tpad, W(L.hsT), L.Tpad, tpoff, 1, d, fs, false, grads->dw_shared_down, T),
+      MOE_TRY(hcall(moe::launch_wgrad_kn(dy, T, W(L.hs), T, sh_off, 1, d, fs, grads->dw_shared_down, stream),
                   "dW_shared_down"));
-      MOE_TRY(hcall(wgrad(W(L.dgusT), L.Tpad, W(L.xTT), L.Tpad, tpoff, 1, 2 * fs, d, false,
-                          grads->dw_shared_gate_up, T),
+      MOE_TRY(hcall(moe::launch_wgrad_kn(W(L.dgus), T, x, T, sh_off, 1, 2 * fs, d, grads->dw_shared_gate_up, stream),
                   "dW_shared_gate_up"));
     }
     dxs = W(L.dxs);

@@ -253,26 +253,20 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const bf16_t *__restrict
   }
 }
 
-// Weight-gradient GEMM grouped over the contraction: for group g with K_g = poff[g+1] -
-// poff[g] (a multiple of 32; padding columns hold zeros),
-//   out[g][m][n] = sum over k < K_g of AT_g[m][k] * BT_g[n][k],
-// AT_g = AT + poff[g] * M and BT_g = BT + poff[g] * N, both K-contiguous with row stride
-// K_g (the group-major layout of the grouped transpose); lda, ldb bound the buffers
-// (M * lda and N * ldb elements).  Sized for short ranges (few rows per expert), where writing the
-// gradient is the cost: 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2
-// blocks of the 32x32x16 MFMA), operand fragments straight from memory into registers
-// (two 32-wide chunks in flight), and a register footprint that lets three workgroups
-// share a CU, so that one's loads overlap another's MFMAs and stores.  The BT fragment is
-// the MFMA's first operand, so a lane's accumulator holds four consecutive output
-// columns; the tile is staged through LDS and written as 16-byte runs.  Rows past M
-// read zeros and are not stored; N must be a multiple of 8.  An empty group writes zeros.
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void wgrad_kernel(const bf16_t *__restrict__ AT, int64_t lda,
+// Weight gradient of the router, float: out[m][n] = sum over k < K of AT[m][k] * BT[n][k]
+// (K = poff[1] - poff[0], a multiple of 32, padding columns zero) with AT [M, lda] and BT
+// [N, ldb] K-contiguous (transposed dl and x).  128 x 128 output tile per workgroup, 4 waves
+// of 64 x 64 (2 x 2 blocks of the 32x32x16 MFMA), operand fragments straight from memory
+// into registers, two 32-wide chunks in flight.  With ksplit > 1 block b computes K slice
+// b / tiles into its own [M, N] slice of out (a reduction adds the slices in order).  The
+// BT fragment is the MFMA's first operand, so a lane's accumulator holds four consecutive
+// output columns; the tile is staged through LDS and written as 16-byte runs.  Rows past
+// M read zeros and are not stored; N must be a multiple of 8.
+__global__ __launch_bounds__(256) void wgrad_f32_kernel(const bf16_t *__restrict__ AT, int64_t lda,
                                                     const bf16_t *__restrict__ BT, int64_t ldb,
                                                     const int32_t *__restrict__ poff, int M, int N, int m_tiles,
                                                     int n_tiles, void *__restrict__ out, int ksplit) {
-  constexpr int ES = OUT_F32 ? 4 : 2;            // output element bytes
-  __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][64 * 64 * ES];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][64 * 64 * 4];
   const int per_g = m_tiles * n_tiles;
   // Tiles in launch order, dealt round-robin to the XCDs: groups' row counts are skewed,
   // and contiguous ranges per XCD would leave the heavy groups on a few XCDs.
@@ -341,51 +335,171 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   // 4 * (lane / 32) + r % 4.  Each wave stages its 64 x 64 in its own LDS region.
   uint8_t *stage = stage_all[wave];
   const size_t obase = (size_t)(g + ks) * M * N;  // ks > 0 only for one group
-  if constexpr (OUT_F32) {
-    // 256-byte rows; 16-byte chunk c (4 columns) of row r at c ^ (r & 15)
+  // 256-byte rows; 16-byte chunk c (4 columns) of row r at c ^ (r & 15)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = i * 32 + lr;
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + lr;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = j * 8 + q * 2 + lh;
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4)) = v;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int c = j * 8 + q * 2 + lh;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        *reinterpret_cast<f32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4)) = v;
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int c = lane & 15, n = n0 + c * 4;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 4 + (lane >> 4), m = m0 + row;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4));
+    if (m < M && n < N) stg16(static_cast<float *>(out) + obase + (size_t)m * N + n, v);
+  }
+}
+
+// The weight-gradient product straight from row-major activations, for short row
+// ranges (write bound): for group g with rows off[g] .. off[g+1] - 1,
+//   out[g][m][n] = sum over those rows r of A[r][m] * B[r][n]   (bf16 out),
+// A [a_rows, M] and B [b_rows, N] row-major -- the contraction runs over rows, so both
+// operands are K-major and need no transpose.  128 x 128 output tile per workgroup, 4
+// waves of 64 x 64 (2 x 2 blocks of the 32x32x16 MFMA).  Each 32-row chunk of both
+// operand tiles moves into LDS as 256-byte rows (direct-to-LDS loads, 16-byte chunk c of
+// row r stored at c ^ 4 (r mod 4)), and the MFMA fragments come from LDS transpose reads
+// (two per fragment, as in the large-tile kernel's K-major mode).  Two chunks in flight;
+// rows past the group read zeros; the tile is staged through LDS and written as 16-byte
+// runs.  M and N multiples of 8; an empty group writes zeros.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void wgrad_kn_kernel(const bf16_t *__restrict__ A, int64_t a_rows,
+                                                       const bf16_t *__restrict__ B, int64_t b_rows,
+                                                       const int32_t *__restrict__ off, int M, int N, int m_tiles,
+                                                       int n_tiles, bf16_t *__restrict__ out) {
+  constexpr int CH = 32 * 256;  // bytes of one operand's 32-row chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[CH], sA1[CH], sB0[CH], sB1[CH];
+  const int per_g = m_tiles * n_tiles;
+  const int tile = blockIdx.x;
+  const int g = tile / per_g;
+  const int rem = tile - g * per_g;
+  const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kb = off[g], kg = off[g + 1] - kb;
+  const int nk = (kg + 31) / 32;
+  const rsrc_t ares = make_rsrc(A, (uint32_t)min<int64_t>(a_rows * M * 2, 0x7fffffffLL));
+  const rsrc_t bres = make_rsrc(B, (uint32_t)min<int64_t>(b_rows * N * 2, 0x7fffffffLL));
+  // load instruction q = 2 wave + p brings rows 4 q .. 4 q + 3 of a chunk; lane i: row
+  // 4 q + i / 16, stored slot i % 16 holding logical chunk (i % 16) ^ 4 (row % 4)
+  int krow[2];
+  uint32_t ao[2], bo[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int kr = 4 * (2 * wave + p) + (lane >> 4);
+    const int cs = ((lane & 15) ^ (4 * (kr & 3))) << 3;
+    krow[p] = kr;
+    const int m = mt * 128 + cs, n = nt * 128 + cs;
+    ao[p] = m < M ? ((uint32_t)(kb + kr) * (uint32_t)M + (uint32_t)m) * 2u : kOob;
+    bo[p] = n < N ? ((uint32_t)(kb + kr) * (uint32_t)N + (uint32_t)n) * 2u : kOob;
+  }
+  auto issue = [&](int c, uint8_t *la, uint8_t *lb) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = c < nk && c * 32 + krow[p] < kg;  // rows past the group: zeros
+      const uint32_t ra = (uint32_t)c * 32u * (uint32_t)M * 2u, rb = (uint32_t)c * 32u * (uint32_t)N * 2u;
+      buf_ld16_lds(ares, ok && ao[p] != kOob ? ao[p] + ra : kOob, la + (2 * wave + p) * 1024);
+      buf_ld16_lds(bres, ok && bo[p] != kOob ? bo[p] + rb : kOob, lb + (2 * wave + p) * 1024);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int c = lane & 15, n = n0 + c * 4;
+  };
+  // 32x32x16 fragment of the 32 columns nb .. nb + 31 (k = 16 kk + 8 (lane >> 5) .. + 7
+  // for column nb + (lane & 31)) from a [32 rows][128 columns] chunk: in a 16-lane group
+  // lane 4a + c receives element c of the 8-byte chunks addressed by lanes a, a + 4, a + 8,
+  // a + 12, so lane s of group G addresses row k0 + s / 4, columns nb + 16 (G & 1) +
+  // 4 (s % 4) .. + 3, with k0 = 16 kk + 8 (G >> 1) (+ 4 for the second read).
+  auto frag = [&](const uint8_t *t, int kk, int nb) -> u32x4 {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int G = lane >> 4, sl = lane & 15;
+    const int col = nb + (G & 1) * 16 + 4 * (sl & 3);
+    u32x4 o;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int row = it * 4 + (lane >> 4), m = m0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4));
-      if (m < M && n < N) stg16(static_cast<float *>(out) + obase + (size_t)m * N + n, v);
+    for (int h = 0; h < 2; ++h) {
+      const int r = kk * 16 + (G >> 1) * 8 + 4 * h + (sl >> 2);
+      const uint8_t *q = t + r * 256 + (((col >> 3) ^ (4 * (r & 3))) << 4) + (col & 7) * 2;
+      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)q);
+      o[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+      o[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
     }
-  } else {
-    // 128-byte rows; 16-byte chunk c (8 columns) of row r at c ^ ((r >> 1) & 7)
+    return o;
+  };
+  f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = i * 32 + lr;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t *la, const uint8_t *lb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 v;
-          v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<uint2 *>(stage + row * 128 + (((j * 4 + q) ^ ((row >> 1) & 7)) << 4) + lh * 8) = v;
-        }
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = frag(la, kk, wm * 64 + i * 32);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = frag(lb, kk, wn * 64 + j * 32);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int c = lane & 7, n = n0 + c * 8;
+  };
+  // two stages: chunk c in stage c % 2; this wave's loads of chunk c are complete once
+  // at most the next chunk's four loads remain, then one barrier makes every wave's
+  // pieces visible; a second barrier keeps the stage until all waves have read it
+  if (nk > 0) issue(0, sA0, sB0);
+  for (int c0 = 0; c0 < nk; c0 += 2) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = it * 8 + (lane >> 3), m = m0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-      if (m < M && n < N) stg16(static_cast<bf16_t *>(out) + obase + (size_t)m * N + n, v);
+    for (int st = 0; st < 2; ++st) {
+      const int c = c0 + st;
+      if (c >= nk) break;
+      uint8_t *la = st ? sA1 : sA0, *lb = st ? sB1 : sB0;
+      uint8_t *na = st ? sA0 : sA1, *nb = st ? sB0 : sB1;
+      if (c + 1 < nk) {
+        issue(c + 1, na, nb);
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __builtin_amdgcn_s_barrier();
+      compute(la, lb);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
     }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // epilogue: acc[i][j] element r holds row mt * 128 + wm * 64 + i * 32 + (lane & 31),
+  // column nt * 128 + wn * 64 + j * 32 + 8 (r / 4) + 4 (lane / 32) + r % 4; each wave
+  // stages its 64 x 64 (8 KB) in one of the four chunk buffers, 128-byte rows, chunk c
+  // of row r at c ^ ((r >> 1) & 7)
+  uint8_t *stage = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  const int m0 = mt * 128 + wm * 64, n0 = nt * 128 + wn * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = i * 32 + lr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 v;
+        v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        *reinterpret_cast<uint2 *>(stage + row * 128 + (((j * 4 + q) ^ ((row >> 1) & 7)) << 4) + lh * 8) = v;
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const size_t obase = (size_t)g * M * N;
+  const int c = lane & 7, n = n0 + c * 8;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 8 + (lane >> 3), m = m0 + row;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+    if (m < M && n < N) stg16(out + obase + (size_t)m * N + n, v);
   }
 }
 
@@ -418,12 +532,12 @@ hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int6
   const int S = wgrad_ksplit(M, N, K);
   const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
   if (S == 1) {
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s,
+    hipLaunchKernelGGL(wgrad_f32_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s,
                        static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
                        n_tiles, static_cast<void *>(out), 1);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)(m_tiles * n_tiles * S)), dim3(256), 0, s,
+  hipLaunchKernelGGL(wgrad_f32_kernel, dim3((unsigned)(m_tiles * n_tiles * S)), dim3(256), 0, s,
                      static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
                      n_tiles, static_cast<void *>(part), S);
   hipError_t e = hipGetLastError();
@@ -482,19 +596,16 @@ hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
-                        int N, bool out_f32, void *out, hipStream_t s) {
-  if (N % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
+hipError_t launch_wgrad_kn(const void *A, int64_t a_rows, const void *B, int64_t b_rows, const int32_t *off, int G,
+                           int M, int N, void *out, hipStream_t s) {
+  if (N % 8 || M % 8) return hipErrorInvalidValue;  // whole 16-byte chunks of columns
+  if (a_rows * M * 2 >= ((int64_t)1 << 31) || b_rows * N * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (out_f32)
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT), lda,
-                       static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out, 1);
-  else
-    hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(AT),
-                       lda, static_cast<const bf16_t *>(BT), ldb, poff, M, N, m_tiles, n_tiles, out, 1);
+  hipLaunchKernelGGL(wgrad_kn_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(A), a_rows,
+                     static_cast<const bf16_t *>(B), b_rows, off, M, N, m_tiles, n_tiles, static_cast<bf16_t *>(out));
   return hipGetLastError();
 }
 

@@ -89,10 +89,10 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 
 // WG: the weight-gradient form, grouped over the contraction instead of the rows: with
 // K_g = offsets[g+1] - offsets[g] (a multiple of 32),
-//   out[g][m][n] = sum over k < K_g of A_g[m][k] * W_g[n][k],
-// A_g = A + offsets[g] * M and W_g = W + offsets[g] * n_out, K-contiguous with row stride
-// K_g (group-major transposed activations; lda and ldb bound the buffers), every group
-// M x n_out, written at out + g * M * n_out.
+//   out[g][m][n] = sum over k < K_g of A_g[m][k] * W[offsets_b[g] + k][n],
+// A_g = A + offsets[g] * M, K-contiguous with row stride K_g (group-major transposed
+// activations, zero padded; lda bounds the buffer), and W [ldb rows, n_out] K-major (BKN;
+// rows past offsets_b[g+1] read zeros); every group M x n_out, written at out + g * M * n_out.
 template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
@@ -234,46 +234,30 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     n0 = nt * BG_BN;
     const int kb = offsets[g];
     const int64_t kg = offsets[g + 1] - kb;
-    if constexpr (BKN) {
-      // A transposed as below (group g's [M, K_g] block at offsets[g] * M, K_g a multiple of
-      // 32, zero padding); W K-major: [ldb rows, n_out] row-major with group g's k-rows
-      // offsets_b[g] .. offsets_b[g+1] - 1 (unpadded; k-rows past them read zeros).
-      // Instruction blk of W brings k-rows 2 blk and 2 blk + 1 of the step (512 bytes
-      // each), chunk p of a row at slot p ^ (4 (row & 3)), as the forward mode's W.
-      nk = (int)(kg / BK);
-      const int kbb = offsets_b[g];
-      kvalid = offsets_b[g + 1] - kbb;
-      ares = make_rsrc(A, (uint32_t)(M * lda * 2));
-      wres = make_rsrc(W, (uint32_t)(ldb * n_out * 2));
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int blk = wave * IPW + i;
-        const int r = blk * RPI + lane / NCH;
-        const int c = (lane % NCH) ^ swz(r);
-        agoff[i] = r < rows ? (uint32_t)(((int64_t)kb * M + (int64_t)(m0 + r) * kg) * 2) + (uint32_t)c * 16u : kOob;
-        const int kr = 2 * blk + (lane >> 5);
-        const int cs = ((lane & 31) ^ (4 * (kr & 3))) << 3;
-        krow[i] = kr;
-        bgoff[i] = n0 + cs < n_out ? ((uint32_t)(kbb + kr) * (uint32_t)n_out + (uint32_t)(n0 + cs)) * 2u : kOob;
-      }
-      obase = out + (size_t)g * M * n_out;
-      ostride = n_out;
-    } else {
+    static_assert(BKN, "the weight-gradient form reads its second operand K-major");
+    // A transposed (group g's [M, K_g] block at offsets[g] * M, K_g a multiple of 32, zero
+    // padding); W K-major: [ldb rows, n_out] row-major with group g's k-rows
+    // offsets_b[g] .. offsets_b[g+1] - 1 (unpadded; k-rows past them read zeros).
+    // Instruction blk of W brings k-rows 2 blk and 2 blk + 1 of the step (512 bytes
+    // each), chunk p of a row at slot p ^ (4 (row & 3)), as the forward mode's W.
     nk = (int)(kg / BK);
+    const int kbb = offsets_b[g];
+    kvalid = offsets_b[g + 1] - kbb;
     ares = make_rsrc(A, (uint32_t)(M * lda * 2));
-    wres = make_rsrc(W, (uint32_t)(n_out * ldb * 2));
+    wres = make_rsrc(W, (uint32_t)(ldb * n_out * 2));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
       const int r = blk * RPI + lane / NCH;
       const int c = (lane % NCH) ^ swz(r);
       agoff[i] = r < rows ? (uint32_t)(((int64_t)kb * M + (int64_t)(m0 + r) * kg) * 2) + (uint32_t)c * 16u : kOob;
-      bgoff[i] = n0 + r < n_out ? (uint32_t)(((int64_t)kb * n_out + (int64_t)(n0 + r) * kg) * 2) + (uint32_t)c * 16u
-                                : kOob;
+      const int kr = 2 * blk + (lane >> 5);
+      const int cs = ((lane & 31) ^ (4 * (kr & 3))) << 3;
+      krow[i] = kr;
+      bgoff[i] = n0 + cs < n_out ? ((uint32_t)(kbb + kr) * (uint32_t)n_out + (uint32_t)(n0 + cs)) * 2u : kOob;
     }
     obase = out + (size_t)g * M * n_out;
     ostride = n_out;
-    }
   }
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
@@ -533,12 +517,11 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_t
   return a.out_f32 ? launch_big<false, float>(a, rows_total_max, s) : launch_big<false>(a, rows_total_max, s);
 }
 
-// Weight gradients: out[g][m][n] = sum over k in [koff[g], koff[g+1]) of AT[m][k] BT[n][k],
-// group ranges multiples of 32; an empty group writes zeros.
 // Weight gradients with the second operand K-major: out[g][m][n] = sum over k < K_g of
 // AT_g[m][k] B[off_b[g] + k][n], AT_g = AT + poff[g] * M with row stride K_g = poff[g+1] -
 // poff[g] (group-major transposed, zero padded to multiples of 32), B [b_rows, N] row-major
-// with group g's rows off_b[g] .. off_b[g+1] - 1 (k past them: zero).  M and N multiples of 8.
+// with group g's rows off_b[g] .. off_b[g+1] - 1 (k past them: zero).  M and N multiples of
+// 8; an empty group writes zeros.
 hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
                                const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s) {
   if (N % 8 || M % 8) return hipErrorInvalidValue;
@@ -549,24 +532,6 @@ hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff,
                      dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G,
                      static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
                      M, nullptr, (int64_t)0, off_b);
-  return hipGetLastError();
-}
-
-hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
-                            int N, bool out_f32, void *out, hipStream_t s) {
-  if (N % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
-  const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
-  const int64_t grid = (int64_t)G * m_tiles * n_tiles;
-  if (out_f32)
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float, true>), dim3((unsigned)grid), dim3(512),
-                       0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
-                       static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<float *>(out), n_tiles, lda,
-                       ldb, M, nullptr, (int64_t)0, nullptr);
-  else
-    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true>), dim3((unsigned)grid),
-                       dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, koff, G,
-                       static_cast<const bf16_t *>(BT), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
-                       ldb, M, nullptr, (int64_t)0, nullptr);
   return hipGetLastError();
 }
 

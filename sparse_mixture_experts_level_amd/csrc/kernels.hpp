@@ -121,11 +121,14 @@ hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float 
                             float *dl, void *dl16, hipStream_t s);
 hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
                             int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
-// out[g][m][n] = sum_{k < K_g} AT_g[m][k] BT_g[n][k], K_g = poff[g+1] - poff[g] (multiples of
-// 32), AT_g = AT + poff[g] * M, BT_g = BT + poff[g] * N, row stride K_g (group-major); lda
-// and ldb bound the buffers.  gemm_big.hip: 256 x 256 tiles for long ranges; backward.hip:
-// 128 x 128 tiles for short ones.
-// One group (koff = {0, K}), float output, split along K into wgrad_ksplit(M, N, K) slices
+// out[g][m][n] = sum over rows r in [off[g], off[g+1]) of A[r][m] B[r][n] from row-major
+// (K-major) A [a_rows, M] and B [b_rows, N], bf16 out; 128 x 128 tiles for short row
+// ranges, no transposes.  M, N multiples of 8; operands below 2 GiB.
+hipError_t launch_wgrad_kn(const void *A, int64_t a_rows, const void *B, int64_t b_rows, const int32_t *off, int G,
+                           int M, int N, void *out, hipStream_t s);
+// out[m][n] = sum_{k < K} AT[m][k] BT[n][k] for one group (koff = {0, K}), AT [M, lda] and BT
+// [N, ldb] K-contiguous, K a multiple of 32, float output, split along K into
+// wgrad_ksplit(M, N, K) slices
 // when the output has few tiles: slice partials in part (that many * M * N floats), added
 // in order into out.
 int wgrad_ksplit(int M, int N, int64_t K);
@@ -136,9 +139,4 @@ hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int6
 // unpadded; k past the group's rows reads zero); 256 x 256 tiles.
 hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
                                const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s);
-hipError_t launch_wgrad_big(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int G, int M,
-                            int N, bool out_f32, void *out, hipStream_t s);
-hipError_t launch_wgrad(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *poff, int G, int M,
-                        int N, bool out_f32, void *out, hipStream_t s);
-
 }  // namespace moe
