@@ -117,6 +117,30 @@ def test_backward_is_deterministic():
         assert torch.equal(grads[n], grads2[n]), n
 
 
+def test_backward_replays_from_a_captured_graph():
+    """moe_backward captured into a HIP graph: every replay equals the eager gradients bit
+    for bit (the library clears its buffers with kernels, never with memsets)."""
+    w = wl.Workload("bwd-graph", 400, 128, 16, 2, 128, 1.25, "bf16", d_ff_shared=64, offset="boost4")
+    say("backward graph capture")
+    inp, cap, layer, dy, dx, grads, ws = _run(w)
+    want_dx = dx.clone()
+    want = {n: v.clone() for n, v in grads.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx, grads, ws,
+                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down)
+    for i in range(3):
+        dx.fill_(3.0)
+        for v in grads.values():
+            v.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx, want_dx), i
+        for n in grads:
+            assert torch.equal(grads[n], want[n]), (i, n)
+
+
 def test_backward_switch_workload_full_size():
     """The Switch-style workload at full size (T = 8192, 64 experts, C = 128)."""
     w = wl.get_workload("switch_bf16")

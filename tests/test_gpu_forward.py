@@ -234,3 +234,33 @@ def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
         if room_after_pass1.sum() > 0 and ref["drops"] > 0:
             assert ref["rerouted"] > 0
     assert row_rel_err(to_np(layer.out), ref["out"]) <= 2e-2
+
+
+@pytest.mark.parametrize("T,d,E,k,f,cf,fs", [(300, 256, 8, 2, 192, 1.25, 64), (16, 256, 32, 4, 128, None, 0)])
+def test_forward_replays_from_a_captured_graph(T, d, E, k, f, cf, fs):
+    """moe_forward allocates, synchronises and clears nothing on the host side, so a caller
+    can capture it into a HIP graph: every replay (with eager work and synchronisation in
+    between) must equal the eager result bit for bit."""
+    w = wl.Workload("graph", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset="boost4")
+    say(f"graph capture T={T} E={E} k={k}")
+    inp = wl.make_inputs(w, seed=5, device=DEV)
+    layer = ops.MoELayer(inp, ops.moe_capacity(T, E, cf))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    want = layer.out.clone()
+    want_slot = layer.routing["slot"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward()
+    for i in range(4):
+        layer.out.fill_(7.0)
+        layer.routing["slot"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int16), want.view(torch.int16)), i
+        assert torch.equal(layer.routing["slot"], want_slot), i
