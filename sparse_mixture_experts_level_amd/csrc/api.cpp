@@ -118,9 +118,18 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, hidden, y_perm, sh_hidden,
-      sh_out, sh_offsets, router_part, down_split, total;
+  size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, x_packed, hidden, y_perm,
+      sh_hidden, sh_out, sh_offsets, router_part, down_split, total;
 };
+
+// Whether the routed experts may take the large-tile regime (an expert can hold 256 rows)
+// with packed operands below 2 GiB.
+bool packable(const moe_desc &D) {
+  if (D.dtype != MOE_DTYPE_BF16 || group_rows_bound(D) < 256) return false;
+  const int64_t R = max_rows(D);
+  return moe::packed_rows_bytes(R, D.num_experts, D.d_model) < ((int64_t)1 << 31) &&
+         moe::packed_rows_bytes(R, D.num_experts, D.d_ff) < ((int64_t)1 << 31);
+}
 
 bool rerouting(const moe_desc &D) { return D.overflow == MOE_OVERFLOW_REROUTE && D.capacity != MOE_NO_CAPACITY; }
 
@@ -146,7 +155,11 @@ Layout layout(const moe_desc &D) {
   L.assigned = take(D.overflow == MOE_OVERFLOW_REROUTE ? T * k * 4 : 0);
   L.hist = take(std::max(moe::dispatch_workspace_bytes((int)T, (int)k, (int)E, D.overflow == MOE_OVERFLOW_REROUTE),
                          moe::aux_loss_workspace_bytes((int)T, (int)E)));
-  L.hidden = take(R * f * s);
+  // packed tile layouts of the gathered x rows and of H when a group can reach the
+  // large-tile regime (any expert range holds all of a group's rows)
+  const bool pack = packable(D);
+  L.x_packed = take(pack ? (size_t)moe::packed_rows_bytes((int64_t)R, (int)E, (int)d) : 0);
+  L.hidden = take(std::max(R * f * s, pack ? (size_t)moe::packed_rows_bytes((int64_t)R, (int)E, (int)f) : (size_t)0));
   L.y_perm = take(R * d * s);
   L.sh_hidden = take(fs ? T * fs * s : 0);
   L.sh_out = take(fs ? T * d * s : 0);
@@ -198,7 +211,24 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
-                           int64_t x_row_count = 0, float *split_ws = nullptr) {
+                           int64_t x_row_count = 0, float *split_ws = nullptr, void *x_packed = nullptr) {
+  if (x_packed && dtype == MOE_DTYPE_BF16 && moe::grouped_gemm_big_regime(rows_max, G, group_rows_max)) {
+    // Large-tile regime: the gathered rows of x are first copied into the packed tile
+    // layout, so that every stage of the gate_up projection loads one contiguous 16 KB
+    // block; the projection writes H in the same layout for the down projection.
+    const int64_t xb = moe::packed_rows_bytes(rows_max, G, d), hb = moe::packed_rows_bytes(rows_max, G, f);
+    MOE_TRY_HIP(moe::launch_pack_rows(x_rows, row_index, offsets, G, rows_max, d, x_packed, s), "pack x rows");
+    moe::GroupedGemmArgs gu = projection_args(G, rows_max, group_rows_max, d, f, x_packed, offsets, w_gate_up, hidden,
+                                              true, nullptr, xb);
+    gu.a_packed = gu.out_packed = true;
+    MOE_TRY(run_projection(gu, dtype, s, "gate_up grouped GEMM"));
+    moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows,
+                                                false, nullptr, hb);
+    down.a_packed = true;
+    down.split_ws = split_ws;
+    MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
+    return MOE_OK;
+  }
   MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true,
                                          row_index, x_row_count),
                          dtype, s, "gate_up grouped GEMM"));
@@ -547,7 +577,8 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
     // [e_begin, e_end] of the offsets (rows stay in the whole layer's row space)
     MOE_TRY(run_grouped_ffn(e_end - e_begin, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x,
                             offsets + e_begin, weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden),
-                            stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr));
+                            stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr,
+                            packable(D) ? at<void>(ws, L.x_packed) : nullptr));
   }
   const void *shared = nullptr;
   if (fs > 0 && add_shared) {

@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // A_g = A + offsets[g] * M, K-contiguous with row stride K_g (group-major transposed
 // activations, zero padded; lda bounds the buffer), and W [ldb rows, n_out] K-major (BKN;
 // rows past offsets_b[g+1] read zeros); every group M x n_out, written at out + g * M * n_out.
-template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false>
+// APK: A is in the packed tile layout (pack_rows_kernel); OPK: the SwiGLU output is
+// written in that layout, for a following large-tile GEMM over the same groups.
+template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false, bool APK = false, bool OPK = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
@@ -117,6 +119,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   constexpr int TILE = BG_BM * BK * 2;           // 16 KB per operand and stage
   constexpr int IPW = TILE / 1024 / NW;          // 1 KB load instructions per wave, operand and stage
   static_assert(!BKN || !SWIGLU, "K-major operands: plain store");
+  static_assert(!(APK || OPK) || !WG, "packed operands: the forward form");
+  static_assert(!OPK || SWIGLU, "packed output: the SwiGLU projection");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
   int krow[IPW];  // WG with K-major operands: this lane's k-row within a step, per instruction
-  int m0, rows, n0, nk, ks = 0, kbase = 0, kvalid = 0;
+  int m0, rows, n0, nk, ks = 0, kbase = 0, kvalid = 0, m_tile = 0;
   bool partial = false;
   rsrc_t ares, wres;
   OutT *obase;
@@ -176,17 +180,23 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     }
     m0 = row_begin + mt * BG_BM;
     rows = min(BG_BM, row_end - m0);
+    m_tile = mt_first + mt;  // rank of this row tile among all groups' row tiles
     n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
     const uint32_t kbytes = (uint32_t)K * 2u;
     // A rows: contiguous from m0, or gathered from the unpermuted activations by row_index
-    ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes)) : make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
+    if constexpr (APK)  // the tiles' K steps are 16 KB blocks, a_rows bounds the buffer in bytes
+      ares = make_rsrc(A, (uint32_t)a_rows);
+    else
+      ares = row_index ? make_rsrc(A, (uint32_t)(a_rows * kbytes)) : make_rsrc(A + (size_t)m0 * K, (uint32_t)rows * kbytes);
     wres = make_rsrc(W + (size_t)g * wstride, (uint32_t)(wstride * 2));
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
       const int r = blk * RPI + lane / NCH;
       const int c = (lane % NCH) ^ swz(r);
-      if (row_index)
+      if (APK)  // a stage image: instruction blk copies bytes blk * 1 KB .. + 1 KB of the block
+        agoff[i] = (uint32_t)blk * 1024u + (uint32_t)lane * 16u;
+      else if (row_index)
         agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
       else
         agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
@@ -264,13 +274,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     const uint32_t kc = (uint32_t)(kbase + kt) * (BK * 2);
     // K-major operands advance BK rows per step
     const uint32_t kcb = BKN ? (uint32_t)(kbase + kt) * (uint32_t)BK * (uint32_t)n_out * 2u : kc;
+    // packed A: block (m_tile, step) of the tile-major layout
+    const uint32_t kca = APK ? ((uint32_t)m_tile * (uint32_t)(K / BK) + (uint32_t)(kbase + kt)) * (uint32_t)TILE : kc;
     uint8_t *la = bufA(b), *lb = bufB(b);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
       bool okb = ok;
       if constexpr (BKN && WG) okb = ok && kt * BK + krow[i] < kvalid;  // k-rows past the group: zeros
-      buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kc : kOob, la + blk * 1024);
+      buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kca : kOob, la + blk * 1024);
       buf_ld16_lds(wres, (okb && bgoff[i] != kOob) ? bgoff[i] + kcb : kOob, lb + blk * 1024);
     }
   };
@@ -415,13 +427,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int gcol = n0 + wn * 32 + (lane & 3) * 8;
+    if constexpr (OPK) {
+      // The staged 128 x 32 is exactly one half (rows wm * 128 ..) of block (m_tile, k step
+      // (n0 + wn * 32) / 32) of H in the packed layout -- 64-byte rows, chunk c of tile row
+      // R at c ^ ((R >> 2) & 3), as a stage of the GEMM that reads H -- so it is copied out
+      // whole; rows past the group hold zeros (their A rows read zeros).
+      if (n0 + wn * 32 < n_out) {
+        bf16_t *blkp = obase + ((size_t)m_tile * (n_out / 32) + (n0 + wn * 32) / 32) * (TILE / 2) + wm * (TILE / 4);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = it * 16 + (lane >> 2);
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 64 + (((lane & 3) ^ ((row >> 2) & 3)) << 4));
-      const int grow = wm * 128 + row;
-      if (grow < rows && gcol < n_out) stg16(obase + (size_t)(m0 + grow) * ostride + gcol, v);
+        for (int it = 0; it < 8; ++it)
+          stg16(blkp + (it * 64 + lane) * 8, *reinterpret_cast<const u32x4 *>(stage + (it * 64 + lane) * 16));
+      }
+    } else {
+      const int gcol = n0 + wn * 32 + (lane & 3) * 8;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 16 + (lane >> 2);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 64 + (((lane & 3) ^ ((row >> 2) & 3)) << 4));
+        const int grow = wm * 128 + row;
+        if (grow < rows && gcol < n_out) stg16(obase + (size_t)(m0 + grow) * ostride + gcol, v);
+      }
     }
   } else {
     const int gcol0 = n0 + wn * 64;
@@ -482,9 +507,39 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   }
 }
 
+// Packed tile layout of a grouped A operand: for row tile m (the rank of a 256-row tile
+// among all groups' row tiles, as the GEMM numbers them) and K step kt, a 16 KB block at
+// (m * K / 32 + kt) * 16 KB holding the tile's 256 rows x 32 values as the GEMM's LDS stage
+// does -- 64-byte rows, 16-byte chunk c of row r at c ^ ((r >> 2) & 3) -- rows past the
+// group zero.  The GEMM then loads each stage as one contiguous 16 KB block instead of 256
+// rows of 64 bytes.  One block per (tile, step); rows gathered through row_index if given.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t *__restrict__ src,
+                                                        const int32_t *__restrict__ row_index,
+                                                        const int32_t *__restrict__ offsets, int G, int K,
+                                                        bf16_t *__restrict__ out) {
+  const int steps = K / 32;
+  const int m_lin = blockIdx.x / steps, kt = blockIdx.x - m_lin * steps;
+  int g, first, count;
+  find_row_block<BG_BM>(offsets, G, m_lin, g, first, count);
+  if (g < 0) return;
+  const int m0 = offsets[g] + (m_lin - first) * BG_BM, row_end = offsets[g + 1];
+  bf16_t *blk = out + ((size_t)m_lin * steps + kt) * (BG_BM * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q >> 2, c = q & 3;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (m0 + r < row_end) {
+      const int64_t sr = row_index ? (int64_t)row_index[m0 + r] : (int64_t)(m0 + r);
+      v = ldg16(src + sr * K + kt * 32 + c * 8);
+    }
+    stg16(blk + r * 32 + ((c ^ ((r >> 2) & 3)) << 3), v);
+  }
+}
+
 }  // namespace
 
-template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false>
+template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false, bool APK = false, bool OPK = false>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
@@ -494,7 +549,7 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
   const int64_t split_stride = rows_total_max * a.n_out;
   const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN>), dim3((unsigned)grid), dim3(512), 0,
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK>), dim3((unsigned)grid), dim3(512), 0,
                      s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr);
@@ -509,12 +564,34 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
 
 // Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  if (a.a_packed || a.out_packed) {  // the packed tile layout (pack_rows): SwiGLU in, plain down
+    if (a.w_kn || a.out_f32) return hipErrorInvalidValue;
+    if (a.swiglu) return a.a_packed ? launch_big<true, bf16_t, false, true, true>(a, rows_total_max, s)
+                                    : hipErrorInvalidValue;
+    return (a.a_packed && !a.out_packed) ? launch_big<false, bf16_t, false, true, false>(a, rows_total_max, s)
+                                         : hipErrorInvalidValue;
+  }
   if (a.w_kn) {  // K-major weights: bf16 output, no SwiGLU
     if (a.swiglu || a.out_f32) return hipErrorInvalidValue;
     return launch_big<false, bf16_t, true>(a, rows_total_max, s);
   }
   if (a.swiglu) return launch_big<true>(a, rows_total_max, s);
   return a.out_f32 ? launch_big<false, float>(a, rows_total_max, s) : launch_big<false>(a, rows_total_max, s);
+}
+
+int64_t packed_rows_bytes(int64_t rows_max, int G, int K) {
+  return ((rows_max + BG_BM - 1) / BG_BM + G) * BG_BM * (int64_t)K * 2;
+}
+
+hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int32_t *offsets, int G, int64_t rows_max,
+                            int K, void *out, hipStream_t s) {
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t grid = ((rows_max + BG_BM - 1) / BG_BM + G) * (K / 32);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(src), row_index,
+                     offsets, G, K, static_cast<bf16_t *>(out));
+  return hipGetLastError();
 }
 
 // Weight gradients with the second operand K-major: out[g][m][n] = sum over k < K_g of

@@ -329,6 +329,7 @@ hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s) {
+  if (a.a_packed || a.out_packed) return hipErrorInvalidValue;  // a layout of the large-tile kernel
   if (a.w_kn) return (a.swiglu || a.out_f32) ? hipErrorInvalidValue : launch_stream_kn(a, s);
   if (a.swiglu) return launch_stream_bm<true>(a, s);
   return a.out_f32 ? launch_stream_bm<false, float>(a, s) : launch_stream_bm<false>(a, s);

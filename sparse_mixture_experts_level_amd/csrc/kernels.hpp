@@ -78,8 +78,20 @@ struct GroupedGemmArgs {
   // Weights stored K-major: group g's matrix is [K, n_out] (row stride n_out) instead of
   // [n_out, K] -- the layout the backward pass multiplies by (dy W_d, dGU W_gu).  No SwiGLU.
   bool w_kn = false;
+  // Large-tile regime only: A in the packed tile layout (launch_pack_rows; a_rows then
+  // bounds the packed buffer in bytes, row_index unused), and/or the SwiGLU output written
+  // in that layout for a following large-tile GEMM over the same groups (out sized
+  // packed_rows_bytes(rows_max, num_groups, n_out)).
+  bool a_packed = false;
+  bool out_packed = false;
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
+// Packed tile layout of grouped rows for the large-tile GEMM's A operand: per 256-row tile
+// of a group (numbered over all groups in order) and 32-wide K step, a 16 KB block laid out
+// as the GEMM's LDS stage; rows gathered through row_index when given.
+int64_t packed_rows_bytes(int64_t rows_max, int G, int K);
+hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int32_t *offsets, int G, int64_t rows_max,
+                            int K, void *out, hipStream_t s);
 // Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group)
 // rather than the streaming one; either reads weights in both layouts (w_kn).
 bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_max);
