@@ -290,7 +290,10 @@ moe_status moe_router_aux_loss(const moe_desc *desc, const float *logits, const 
  * desc->fill_order and desc->overflow (moe_dispatch_permute or moe_dispatch_reroute).
  *   x [T, d] dtype, smaller than 2 GiB; logit_offset [E] float or NULL; out [T, d] dtype
  *   routing: NULL, or a struct whose non-NULL fields receive the routing tables
- *   ws: at least moe_workspace_size(desc) bytes */
+ *   ws: at least moe_workspace_size(desc) bytes
+ * Only kernel launches on `stream` (no host synchronisation, allocation or memset): the
+ * call can be captured into a HIP graph.  Deterministic: equal inputs give bitwise equal
+ * outputs and routing tables. */
 moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const void *x,
                        const float *logit_offset, void *out, moe_routing *routing, void *ws,
                        size_t ws_bytes, hipStream_t stream);
@@ -322,7 +325,8 @@ size_t moe_backward_workspace_size(const moe_desc *desc);
  *   dx         [T, d] dtype, written
  *   grads      written in full (see moe_grads)
  *   ws         at least moe_backward_workspace_size(desc) bytes
- * Accumulation in float; every sum in a fixed order (bit-reproducible). */
+ * Accumulation in float; every sum in a fixed order (bit-reproducible).  Only kernel
+ * launches on `stream` (capturable into a HIP graph). */
 moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const void *x, const moe_routing *routing,
                         const void *dy, void *dx, moe_grads *grads, void *ws, size_t ws_bytes, hipStream_t stream);
 
