@@ -121,11 +121,6 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-__device__ __forceinline__ float silu_grad_f32(float z) {
-  const float s = 1.0f / (1.0f + __expf(-z));
-  return s * (1.0f + z * (1.0f - s));
-}
-
 // One wavefront per row r of the expert-sorted layout.  Finds the row's assignment
 // (t, j), takes its gate g (1 without gates), and from gu = [G | U] (float: silu' is
 // steep enough that a bf16 G would cost percent-level gradient error) and dh' computes
@@ -196,26 +191,80 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict
 
 // Gradient of the renormalised gates with respect to the logits, one wavefront per token:
 // dl[t][ids_j] = g_j (dg_j - sum_j' g_j' dg_j'), zero elsewhere; written as float [T, E]
-// and as bf16 [T, Epad] (zero padded).
+// and as bf16 [T, Epad] (zero padded).  dg_j = dL/dg_j is dgate[t][j], or, with dpart,
+// the sum of the nb block dot products dH' . H of the assignment's row (0 when dropped),
+// added lane-strided and then in a fixed butterfly: the same value in every lane.
 __global__ __launch_bounds__(256) void gates_bwd_kernel(const int32_t *__restrict__ ids,
                                                         const float *__restrict__ gates,
-                                                        const float *__restrict__ dgate, int T, int E, int k,
+                                                        const float *__restrict__ dgate,
+                                                        const float *__restrict__ dpart, int nb,
+                                                        const int32_t *__restrict__ serving,
+                                                        const int32_t *__restrict__ slot,
+                                                        const int32_t *__restrict__ offsets, int T, int E, int k,
                                                         int Epad, float *__restrict__ dl,
                                                         bf16_t *__restrict__ dl16) {
+  constexpr int QMAX = (MOE_MAX_EXPERTS_DEV + 63) / 64;  // experts per lane
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // each lane keeps g_j and dg_j of the selected experts among its own (lane + 64 q)
+  float my_g[QMAX], my_dg[QMAX];
+  bool my_sel[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    my_g[q] = 0.0f;
+    my_dg[q] = 0.0f;
+    my_sel[q] = false;
+  }
   float s = 0.0f;
-  for (int j = 0; j < k; ++j) s += gates[(size_t)t * k + j] * dgate[(size_t)t * k + j];  // same order in every lane
-  for (int e = lane; e < Epad; e += 64) {
-    float v = 0.0f;
-    for (int j = 0; j < k; ++j)
-      if (ids[(size_t)t * k + j] == e) {
-        const float g = gates[(size_t)t * k + j];
-        v = g * (dgate[(size_t)t * k + j] - s);
+  for (int j = 0; j < k; ++j) {
+    const size_t tj = (size_t)t * k + j;
+    float dg;
+    if (dpart) {
+      const int sl = slot[tj];
+      dg = 0.0f;
+      if (sl >= 0) {
+        const float *p = dpart + ((size_t)offsets[serving[tj]] + sl) * nb;
+        for (int b = lane; b < nb; b += 64) dg += p[b];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) dg += __shfl_xor(dg, o, 64);
       }
+    } else {
+      dg = dgate[tj];
+    }
+    const float g = gates[tj];
+    s += g * dg;  // same order in every lane
+    const int e = ids[tj];
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < QMAX; ++q)
+        if (q == (e >> 6)) {
+          my_g[q] = g;
+          my_dg[q] = dg;
+          my_sel[q] = true;
+        }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int e = lane + 64 * q;
+    if (e >= Epad) break;
+    const float v = my_sel[q] ? my_g[q] * (my_dg[q] - s) : 0.0f;
     if (e < E) dl[(size_t)t * E + e] = v;
     dl16[(size_t)t * Epad + e] = f32_to_bf16(v);
+  }
+}
+
+// g of every kept row: row offsets[e] + slot of assignment i (expert e = serving[i])
+// takes gates[i]; each kept row has exactly one assignment.
+__global__ __launch_bounds__(256) void row_gate_kernel(const int32_t *__restrict__ serving,
+                                                       const int32_t *__restrict__ slot,
+                                                       const int32_t *__restrict__ offsets,
+                                                       const float *__restrict__ gates, int64_t n,
+                                                       float *__restrict__ row_gate) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int sl = slot[i];
+    if (sl >= 0) row_gate[offsets[serving[i]] + sl] = gates[i];
   }
 }
 
@@ -581,10 +630,21 @@ hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, cons
   return hipGetLastError();
 }
 
-hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, int T, int E, int k, int Epad,
-                            float *dl, void *dl16, hipStream_t s) {
-  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, ids, gates, dgate, T, E, k,
-                     Epad, dl, static_cast<bf16_t *>(dl16));
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, const float *dpart, int nb,
+                            const int32_t *serving, const int32_t *slot, const int32_t *offsets, int T, int E, int k,
+                            int Epad, float *dl, void *dl16, hipStream_t s) {
+  if (Epad > MOE_MAX_EXPERTS_DEV + 63) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, ids, gates, dgate, dpart, nb,
+                     serving, slot, offsets, T, E, k, Epad, dl, static_cast<bf16_t *>(dl16));
+  return hipGetLastError();
+}
+
+hipError_t launch_row_gate(const int32_t *serving, const int32_t *slot, const int32_t *offsets, const float *gates,
+                           int64_t n, float *row_gate, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(row_gate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, serving, slot, offsets, gates, n,
+                     row_gate);
   return hipGetLastError();
 }
 

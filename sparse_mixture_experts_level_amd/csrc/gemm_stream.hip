@@ -75,13 +75,14 @@ __device__ __forceinline__ u32x4 wt_frag(const uint8_t *tile, int s, int wave, i
 // Loads are issued unconditionally through buffer resources: token rows past the
 // block's end and weight subtiles past n_out get an out-of-range offset and read as
 // zeros without a memory access, which keeps the count of loads per step static.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT, bool WT>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT, bool WT, bool GB>
 __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t ares, const uint32_t *boff,
                                              const uint32_t *aoff, uint8_t *sA0, uint8_t *sA1, uint8_t *sA2,
                                              uint8_t *sA3, uint8_t *const *sW, int nk, int rows, int m0, int ncol0,
-                                             int nvalid, int n_out, OutT *__restrict__ out) {
+                                             int nvalid, int n_out, OutT *__restrict__ out, const SwigluBwdOut &gb) {
   static_assert(S == 3 || S == 4, "three or four stages");
   static_assert(!WT || (NSUB == 1 && NW == 4 && !SWIGLU), "K-major weights: one 64-column tile of four waves");
+  static_assert(!GB || (SWIGLU && sizeof(OutT) == 2), "SwiGLU backward: gate and up blocks, bf16 gradients");
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;
   constexpr int MS = NA * NW / 2 < BM / 16 ? NA * NW / 2 : BM / 16;  // 16-row subtiles the block can fill
   constexpr int LOADS = NA + 2 * (WT ? 1 : NB);            // loads per thread and chunk
@@ -176,6 +177,70 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
   __syncthreads();
 
   // epilogue: C layout of the 16x16 MFMA -- column (lane & 15), rows 4*(lane>>4)+j
+  if constexpr (GB) {
+    // SwiGLU backward from the float G, U of each (row, column) and dH' (bf16): with g
+    // the row's gate, dG = g dH' U silu'(G), dU = g dH' silu(G), g H, and the dot dH' . H
+    // of the row's 16 columns (the wave's subtile), summed over the 16 lanes in a fixed
+    // butterfly order.  Staged through the freed A stages, one wave-private region of
+    // BM rows x 32 bytes (the wave's 16 columns) per stage: dH' comes in, and dG, dU and
+    // g H go out, as 16-byte row pieces (lane: row lane / 2 + 32 it, half lane % 2).
+    // Region 0 holds dH' and then g H (each element read and then overwritten by the
+    // same lane), region 1 dG, region 2 dU; a wave's LDS accesses complete in order.
+    static_assert(NSUB == 1 && S >= 3, "one 16-column subtile per wave, three stages");
+    if (nvalid > 0) {  // wave-uniform; every wave reaches the barrier below
+      uint8_t *rg0 = sA0 + wave * BM * 32, *rg1 = sA1 + wave * BM * 32, *rg2 = sA2 + wave * BM * 32;
+      const int half = lane & 1, col = lane & 15;
+      constexpr int PIECES = (MS * 16 + 31) / 32;  // 16-byte row-piece rounds
+#pragma unroll
+      for (int it = 0; it < PIECES; ++it) {
+        const int q = it * 32 + (lane >> 1);
+        if (q < rows)
+          *reinterpret_cast<u32x4 *>(rg0 + q * 32 + half * 16) =
+              ldg16(gb.dhp + (size_t)(m0 + q) * n_out + ncol0 + half * 8);
+      }
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = i * 16 + (lane >> 4) * 4 + j;
+          const bool ok = r < rows;
+          bf16_t *e0 = reinterpret_cast<bf16_t *>(rg0 + r * 32 + col * 2);
+          const float z = acc[i][0][j], u = acc[i][1][j], d = bf16_to_f32(*e0);
+          const float g = gb.row_gate ? (ok ? gb.row_gate[m0 + r] : 0.0f) : 1.0f;
+          const float sg = sigmoid_fast(z);
+          const float sz = z * sg;                         // silu(z)
+          const float H = sz * u;
+          float dot = d * H;
+          const float dh = g * d;
+          const float dsilu = sg * (1.0f + z * (1.0f - sg));  // silu'(z)
+          *reinterpret_cast<bf16_t *>(rg1 + r * 32 + col * 2) = f32_to_bf16(dh * u * dsilu);
+          *reinterpret_cast<bf16_t *>(rg2 + r * 32 + col * 2) = f32_to_bf16(dh * sz);
+          *e0 = f32_to_bf16(g * H);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o, 64);
+          if (gb.dpart && ok && col == 0) gb.dpart[(size_t)(m0 + r) * (n_out / 16) + ncol0 / 16] = dot;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < PIECES; ++it) {
+        const int q = it * 32 + (lane >> 1);
+        if (q < rows) {
+          const size_t row = (size_t)(m0 + q);
+          const int c = ncol0 + half * 8;
+          stg16(out + row * 2 * n_out + c, *reinterpret_cast<const u32x4 *>(rg1 + q * 32 + half * 16));
+          stg16(out + row * 2 * n_out + n_out + c, *reinterpret_cast<const u32x4 *>(rg2 + q * 32 + half * 16));
+          stg16(gb.hg + row * n_out + c, *reinterpret_cast<const u32x4 *>(rg0 + q * 32 + half * 16));
+        }
+      }
+    }
+    // the next row block refills the stages: every wave is done with its region
+    __syncthreads();
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
 #pragma unroll
@@ -202,14 +267,14 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 // deals consecutive blocks to the 8 XCDs round-robin, which spreads every expert --
 // including the few heavily loaded ones -- over all XCDs.  NW waves per workgroup
 // share the staged A rows: wider workgroups load each token row fewer times.
-template <int BM, int NSUB, bool SWIGLU, int S, int NW, typename OutT, bool WT = false>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW, typename OutT, bool WT = false, bool GB = false>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_kernel(const bf16_t *__restrict__ A,
                                                                      const int32_t *__restrict__ row_index,
                                                                      int64_t a_rows,
                                                                      const int32_t *__restrict__ offsets,
                                                                      const bf16_t *__restrict__ W, int64_t wstride,
                                                                      int n_out, int K, OutT *__restrict__ out,
-                                                                     int n_tiles) {
+                                                                     int n_tiles, const SwigluBwdOut gb) {
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;  // 16-row weight subtiles per wave
   constexpr int NT = 64 * NW;                     // threads
   constexpr int A_PER_T = (BM * 8 + NT - 1) / NT;  // 16-byte A pieces per thread and chunk
@@ -278,8 +343,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
 #define SG_BLOCK(N)                                                                                              \
   if constexpr (N <= A_PER_T) {                                                                                  \
     if (na == N) {                                                                                               \
-      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT, WT>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, sW, nk, rows, m0, \
-                                                     ncol0, nvalid, n_out, out);                                  \
+      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT, WT, GB>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, sW, nk, rows, \
+                                                         m0, ncol0, nvalid, n_out, out, gb);                      \
       continue;                                                                                                  \
     }                                                                                                            \
   }
@@ -291,15 +356,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   }
 }
 
-template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4, typename OutT = bf16_t, bool WT = false>
+template <int BM, int NSUB, bool SWIGLU, int S, int NW = 4, typename OutT = bf16_t, bool WT = false, bool GB = false>
 hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
   const int cols_per_tile = 16 * NW * NSUB;
   const int n_tiles = (a.n_out + cols_per_tile - 1) / cols_per_tile;
   const int64_t grid = (int64_t)a.num_groups * n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT, WT>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+  const SwigluBwdOut gb{static_cast<const bf16_t *>(a.bwd_dhp), a.bwd_row_gate, static_cast<bf16_t *>(a.bwd_hg),
+                        a.bwd_dpart};
+  hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT, WT, GB>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                      static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles);
+                     n_tiles, gb);
   return hipGetLastError();
 }
 
@@ -314,16 +381,16 @@ hipError_t launch_stream_kn(const GroupedGemmArgs &a, hipStream_t s) {
   return launch_stream<128, 1, false, 3, 4, bf16_t, true>(a, s);
 }
 
-template <bool SWIGLU, typename OutT = bf16_t>
+template <bool SWIGLU, typename OutT = bf16_t, bool GB = false>
 hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
   // three stages for gate_up (two weight subtiles per wave keep enough bytes in flight),
   // four for down (one subtile per wave: a deeper pipeline instead)
   constexpr int S = SWIGLU ? 3 : 4;
   const int r = a.group_rows_max;
-  if (r <= 16) return launch_stream<16, 1, SWIGLU, S, 4, OutT>(a, s);
-  if (r <= 32) return launch_stream<32, 1, SWIGLU, S, 4, OutT>(a, s);
-  if (r <= 64) return launch_stream<64, 1, SWIGLU, S, 4, OutT>(a, s);
-  return launch_stream<128, 1, SWIGLU, S, 4, OutT>(a, s);
+  if (r <= 16) return launch_stream<16, 1, SWIGLU, S, 4, OutT, false, GB>(a, s);
+  if (r <= 32) return launch_stream<32, 1, SWIGLU, S, 4, OutT, false, GB>(a, s);
+  if (r <= 64) return launch_stream<64, 1, SWIGLU, S, 4, OutT, false, GB>(a, s);
+  return launch_stream<128, 1, SWIGLU, S, 4, OutT, false, GB>(a, s);
 }
 
 }  // namespace
@@ -331,6 +398,7 @@ hipError_t launch_stream_bm(const GroupedGemmArgs &a, hipStream_t s) {
 hipError_t launch_grouped_gemm_stream_bf16(const GroupedGemmArgs &a, hipStream_t s) {
   if (a.a_packed || a.out_packed) return hipErrorInvalidValue;  // a layout of the large-tile kernel
   if (a.w_kn) return (a.swiglu || a.out_f32) ? hipErrorInvalidValue : launch_stream_kn(a, s);
+  if (a.bwd_dhp) return a.swiglu && !a.out_f32 ? launch_stream_bm<true, bf16_t, true>(a, s) : hipErrorInvalidValue;
   if (a.swiglu) return launch_stream_bm<true>(a, s);
   return a.out_f32 ? launch_stream_bm<false, float>(a, s) : launch_stream_bm<false>(a, s);
 }
@@ -345,7 +413,7 @@ bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_ma
 
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s) {
   if (grouped_gemm_big_regime(a.rows_max, a.num_groups, a.group_rows_max))
-    return launch_grouped_gemm_big_bf16(a, a.rows_max, s);
+    return a.bwd_dhp ? hipErrorInvalidValue : launch_grouped_gemm_big_bf16(a, a.rows_max, s);
   return launch_grouped_gemm_stream_bf16(a, s);
 }
 

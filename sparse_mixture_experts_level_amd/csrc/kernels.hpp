@@ -84,6 +84,23 @@ struct GroupedGemmArgs {
   // packed_rows_bytes(rows_max, num_groups, n_out)).
   bool a_packed = false;
   bool out_packed = false;
+  // SwiGLU backward epilogue (streaming regime, with swiglu, bf16): instead of H, the
+  // kernel forms from the float G, U of each row and bwd_dhp = dH' (bf16 [rows, n_out],
+  // rows in group order) out = [dG | dU] (bf16 [rows, 2 n_out]), bwd_hg = g H (bf16
+  // [rows, n_out]) and, when bwd_dpart is set, the dot products dH' . H of each row over
+  // each 16-column block (float [rows, n_out / 16]); g = bwd_row_gate[row], or 1 when NULL.
+  const void *bwd_dhp = nullptr;
+  const float *bwd_row_gate = nullptr;
+  void *bwd_hg = nullptr;
+  float *bwd_dpart = nullptr;
+};
+
+// Device-side form of the SwiGLU backward outputs (kernel argument).
+struct SwigluBwdOut {
+  const uint16_t *dhp;  // bf16
+  const float *row_gate;
+  uint16_t *hg;        // bf16
+  float *dpart;
 };
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 // Packed tile layout of grouped rows for the large-tile GEMM's A operand: per 256-row tile
@@ -129,8 +146,14 @@ hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, cons
                              const int32_t *row_token, const int32_t *serving, const int32_t *slot,
                              const int32_t *offsets, const float *gates, int k, void *dgu, void *hg, float *dgate,
                              hipStream_t s);
-hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, int T, int E, int k, int Epad,
-                            float *dl, void *dl16, hipStream_t s);
+// dl (float [T, E]) and dl16 (bf16 [T, Epad]) from the gate gradients dg: dgate [T, k], or
+// with dpart the sums of the nb block partials [rows, nb] of each kept assignment's row.
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, const float *dpart, int nb,
+                            const int32_t *serving, const int32_t *slot, const int32_t *offsets, int T, int E, int k,
+                            int Epad, float *dl, void *dl16, hipStream_t s);
+// row_gate[offsets[serving[i]] + slot[i]] = gates[i] for every kept assignment i < n.
+hipError_t launch_row_gate(const int32_t *serving, const int32_t *slot, const int32_t *offsets, const float *gates,
+                           int64_t n, float *row_gate, hipStream_t s);
 hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
                             int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
 // out[g][m][n] = sum over rows r in [off[g], off[g+1]) of A[r][m] B[r][n] from row-major
