@@ -626,7 +626,7 @@ namespace {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdLayout {
-  size_t gu, dhp, dgu, hg, dxr, poff, dyT, dguT, xT, dgate, row_gate, dpart, dl, dl16, dlT, xTT, wr_part, dxrt, tpoff,
+  size_t gu, dhp, dgu, hg, dxr, poff, dyT, dguT, xT, dgate, row_gate, dpart, dl, dl16, dlT, wr_part, dxrt, tpoff,
       sh_off, gus, dhs, dgus, hs, dxs, dyTT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
   bool long_k, shared_long;
@@ -670,8 +670,7 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dl = take(T * E * 4);
   L.dl16 = take(T * L.Epad * s);
   L.dlT = take(L.Epad * L.Tpad * s);
-  L.xTT = take(d * L.Tpad * s);
-  const int64_t wr_split = moe::wgrad_ksplit((int)E, (int)d, L.Tpad);
+  const int64_t wr_split = moe::wgrad_big_f32_splits((int)E, (int)d, L.Tpad);
   L.wr_part = take(wr_split > 1 ? wr_split * E * d * 4 : 0);
   L.dxrt = take(T * d * s);
   L.tpoff = take(2 * 4);
@@ -865,11 +864,9 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dl16), 0, T, (int)L.Epad, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
                                          W(L.dlT), L.Tpad, 0, stream),
               "dl transpose"));
-  MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.xTT), L.Tpad, 0,
-                                         stream),
-              "x transpose"));
-  MOE_TRY(hcall(moe::launch_wgrad_ksplit(W(L.dlT), L.Tpad, W(L.xTT), L.Tpad, tpoff, E, d, L.Tpad, at<float>(ws, L.wr_part),
-                                        static_cast<float *>(grads->dw_router), stream),
+  // dW_r = dl^T x over the tokens: dl transposed (small), x read K-major as it is
+  MOE_TRY(hcall(moe::launch_wgrad_big_kn_f32(W(L.dlT), L.Tpad, tpoff, x, T, sh_off, E, d, L.Tpad,
+                                            at<float>(ws, L.wr_part), static_cast<float *>(grads->dw_router), stream),
               "dW_router"));
   {
     // dl W_r: W_r [E, d] is K-major for this product; the contraction runs over Epad, rows

@@ -302,111 +302,6 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const bf16_t *__restrict
   }
 }
 
-// Weight gradient of the router, float: out[m][n] = sum over k < K of AT[m][k] * BT[n][k]
-// (K = poff[1] - poff[0], a multiple of 32, padding columns zero) with AT [M, lda] and BT
-// [N, ldb] K-contiguous (transposed dl and x).  128 x 128 output tile per workgroup, 4 waves
-// of 64 x 64 (2 x 2 blocks of the 32x32x16 MFMA), operand fragments straight from memory
-// into registers, two 32-wide chunks in flight.  With ksplit > 1 block b computes K slice
-// b / tiles into its own [M, N] slice of out (a reduction adds the slices in order).  The
-// BT fragment is the MFMA's first operand, so a lane's accumulator holds four consecutive
-// output columns; the tile is staged through LDS and written as 16-byte runs.  Rows past
-// M read zeros and are not stored; N must be a multiple of 8.
-__global__ __launch_bounds__(256) void wgrad_f32_kernel(const bf16_t *__restrict__ AT, int64_t lda,
-                                                    const bf16_t *__restrict__ BT, int64_t ldb,
-                                                    const int32_t *__restrict__ poff, int M, int N, int m_tiles,
-                                                    int n_tiles, void *__restrict__ out, int ksplit) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][64 * 64 * 4];
-  const int per_g = m_tiles * n_tiles;
-  // Tiles in launch order, dealt round-robin to the XCDs: groups' row counts are skewed,
-  // and contiguous ranges per XCD would leave the heavy groups on a few XCDs.
-  // With ksplit > 1 (one group, float output) block b computes K slice b / per_g of the
-  // tile b % per_g into its own [M, N] slice of out; a reduction adds the slices.
-  int tile = blockIdx.x, ks = 0;
-  if (ksplit > 1) {
-    ks = tile / per_g;
-    tile -= ks * per_g;
-  }
-  const int g = tile / per_g;
-  const int rem = tile - g * per_g;
-  const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int m0 = mt * 128 + (wave >> 1) * 64, n0 = nt * 128 + (wave & 1) * 64;
-  const int kb = poff[g], ke = poff[g + 1];
-  const int nk_all = (ke - kb) / 32, per = (nk_all + ksplit - 1) / ksplit;
-  const int k_lo = min(nk_all, ks * per), nk = min(nk_all, k_lo + per) - k_lo;  // in 32-wide chunks
-  const rsrc_t ares = make_rsrc(AT, (uint32_t)min<int64_t>((int64_t)M * lda * 2, 0x7fffffffLL));
-  const rsrc_t bres = make_rsrc(BT, (uint32_t)min<int64_t>((int64_t)N * ldb * 2, 0x7fffffffLL));
-  // 32x32x16 operand fragment: lane holds row (lane & 31), k = 8 * (lane >> 5) .. + 7.
-  // Group g's operands are the contiguous blocks [M, K_g] at AT + kb * M and [N, K_g] at
-  // BT + kb * N (row stride K_g).
-  const int64_t kg = ke - kb;
-  uint32_t ao[2], bo[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + i * 32 + lr, n = n0 + i * 32 + lr;
-    ao[i] = m < M ? (uint32_t)(((int64_t)kb * M + (int64_t)m * kg + k_lo * 32) * 2) + (uint32_t)lh * 16u : kOob;
-    bo[i] = n < N ? (uint32_t)(((int64_t)kb * N + (int64_t)n * kg + k_lo * 32) * 2) + (uint32_t)lh * 16u : kOob;
-  }
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  // two 32-wide chunks in flight: the next chunk's loads overlap this chunk's MFMAs
-  u32x4 fa[2][2][2], fb[2][2][2];  // [stage][block][16-wide half of the chunk]
-  auto issue = [&](int st, int c) {
-    const uint32_t kc = (uint32_t)c * 64u;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        fa[st][i][h] = buf_ld16(ares, ao[i] != kOob ? ao[i] + kc + h * 32u : kOob);
-        fb[st][i][h] = buf_ld16(bres, bo[i] != kOob ? bo[i] + kc + h * 32u : kOob);
-      }
-  };
-  if (nk > 0) issue(0, 0);
-  for (int c0 = 0; c0 < nk; c0 += 2) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int c = c0 + st;
-      if (c >= nk) break;
-      if (c + 1 < nk) issue(st ^ 1, c + 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[st][j][h], fa[st][i][h], acc[i][j]);
-    }
-  }
-  // acc[i][j] element r: row m0 + i * 32 + (lane & 31), column n0 + j * 32 + 8 * (r / 4) +
-  // 4 * (lane / 32) + r % 4.  Each wave stages its 64 x 64 in its own LDS region.
-  uint8_t *stage = stage_all[wave];
-  const size_t obase = (size_t)(g + ks) * M * N;  // ks > 0 only for one group
-  // 256-byte rows; 16-byte chunk c (4 columns) of row r at c ^ (r & 15)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = i * 32 + lr;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = j * 8 + q * 2 + lh;
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        *reinterpret_cast<f32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4)) = v;
-      }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  const int c = lane & 15, n = n0 + c * 4;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 4 + (lane >> 4), m = m0 + row;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + row * 256 + ((c ^ (row & 15)) << 4));
-    if (m < M && n < N) stg16(static_cast<float *>(out) + obase + (size_t)m * N + n, v);
-  }
-}
-
 // The weight-gradient product straight from row-major activations, for short row
 // ranges (write bound): for group g with rows off[g] .. off[g+1] - 1,
 //   out[g][m][n] = sum over those rows r of A[r][m] * B[r][n]   (bf16 out),
@@ -568,30 +463,8 @@ __global__ __launch_bounds__(256) void ksplit_sum_kernel(const float *__restrict
 
 }  // namespace
 
-int wgrad_ksplit(int M, int N, int64_t K) {
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t chunks = K / 32;
-  if (tiles >= 256 || chunks < 16) return 1;
-  return (int)std::min<int64_t>({64, std::max(1, 512 / tiles), chunks / 8});
-}
-
-hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int M,
-                               int N, int64_t K, float *part, float *out, hipStream_t s) {
-  if (N % 8) return hipErrorInvalidValue;
-  const int S = wgrad_ksplit(M, N, K);
-  const int m_tiles = (M + 127) / 128, n_tiles = (N + 127) / 128;
-  if (S == 1) {
-    hipLaunchKernelGGL(wgrad_f32_kernel, dim3((unsigned)(m_tiles * n_tiles)), dim3(256), 0, s,
-                       static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
-                       n_tiles, static_cast<void *>(out), 1);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(wgrad_f32_kernel, dim3((unsigned)(m_tiles * n_tiles * S)), dim3(256), 0, s,
-                     static_cast<const bf16_t *>(AT), lda, static_cast<const bf16_t *>(BT), ldb, koff, M, N, m_tiles,
-                     n_tiles, static_cast<void *>(part), S);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)M * N;
+hipError_t launch_ksplit_sum(const float *part, int S, int64_t n, float *out, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
   const int64_t blocks = std::min<int64_t>((n / 4 + 255) / 256, 2048);
   hipLaunchKernelGGL(ksplit_sum_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, part, S, n, out);
   return hipGetLastError();

@@ -225,11 +225,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     obase = out;
     ostride = n_out;
   } else {
+    // With split_out (one group, float), K is the number of K slices: slice ks writes its
+    // float partial sums to split_out + ks * split_stride, and a reduction adds them.
     const int m_tiles = (M + BG_BM - 1) / BG_BM;
     const int per_g = m_tiles * n_tiles;
-    const int real_blocks = G * per_g;
+    const int ksplit = split_out ? max(1, K) : 1;
+    const int real_blocks = G * per_g * ksplit;
     if ((int)blockIdx.x >= real_blocks) return;
-    const int lin = xcd_remap(blockIdx.x, real_blocks);
+    const int lin0 = xcd_remap(blockIdx.x, real_blocks);
+    ks = lin0 / (G * per_g);
+    const int lin = lin0 - ks * (G * per_g);
     const int g = lin / per_g, local = lin - g * per_g;
     int mt, nt;
     if (M <= n_out) {  // the B operand larger: its tile outermost
@@ -250,7 +255,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     // offsets_b[g] .. offsets_b[g+1] - 1 (unpadded; k-rows past them read zeros).
     // Instruction blk of W brings k-rows 2 blk and 2 blk + 1 of the step (512 bytes
     // each), chunk p of a row at slot p ^ (4 (row & 3)), as the forward mode's W.
-    nk = (int)(kg / BK);
+    const int steps = (int)(kg / BK), sps = (steps + ksplit - 1) / ksplit;
+    kbase = ks * sps;
+    nk = max(0, min(sps, steps - kbase));
+    partial = ksplit > 1;
     const int kbb = offsets_b[g];
     kvalid = offsets_b[g + 1] - kbb;
     ares = make_rsrc(A, (uint32_t)(M * lda * 2));
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     for (int i = 0; i < IPW; ++i) {
       const int blk = wave * IPW + i;
       bool okb = ok;
-      if constexpr (BKN && WG) okb = ok && kt * BK + krow[i] < kvalid;  // k-rows past the group: zeros
+      if constexpr (BKN && WG) okb = ok && (kbase + kt) * BK + krow[i] < kvalid;  // k-rows past the group: zeros
       buf_ld16_lds(ares, (ok && agoff[i] != kOob) ? agoff[i] + kca : kOob, la + blk * 1024);
       buf_ld16_lds(wres, (okb && bgoff[i] != kOob) ? bgoff[i] + kcb : kOob, lb + blk * 1024);
     }
@@ -610,6 +618,36 @@ hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff,
                      static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
                      M, nullptr, (int64_t)0, off_b);
   return hipGetLastError();
+}
+
+// Number of K slices of the float weight-gradient form with one group (M x N output,
+// K rows): enough blocks to fill the GPU, at least 8 steps of 32 per slice.
+int wgrad_big_f32_splits(int M, int N, int64_t K) {
+  const int tiles = ((M + BG_BM - 1) / BG_BM) * ((N + BG_BN - 1) / BG_BN);
+  const int64_t steps = K / 32;
+  if (tiles >= 256 || steps < 16) return 1;
+  return (int)std::min<int64_t>({64, std::max(1, 256 / tiles), steps / 8});
+}
+
+// out[m][n] = sum over k < K of AT[m][k] B[k][n] in float, one group: AT [M, K] with row
+// stride K = poff[1] - poff[0] (a multiple of 32, zero padding), B [b_rows, N] row-major
+// with rows off_b[0] .. off_b[1] - 1 (k past them: zero).  Cut along K into
+// wgrad_big_f32_splits() slices whose float partials (part, slices * M * N floats) are
+// added in slice order.  N a multiple of 8.
+hipError_t launch_wgrad_big_kn_f32(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
+                                   const int32_t *off_b, int M, int N, int64_t K, float *part, float *out,
+                                   hipStream_t s) {
+  if (N % 8) return hipErrorInvalidValue;
+  const int S = wgrad_big_f32_splits(M, N, K);
+  const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
+  const int64_t grid = (int64_t)m_tiles * n_tiles * S;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float, true, true>), dim3((unsigned)grid), dim3(512), 0, s,
+                     static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, 1, static_cast<const bf16_t *>(B),
+                     (int64_t)0, N, S, out, n_tiles, lda, b_rows, M, S > 1 ? part : nullptr, (int64_t)M * N, off_b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_ksplit_sum(part, S, (int64_t)M * N, out, s);
 }
 
 }  // namespace moe

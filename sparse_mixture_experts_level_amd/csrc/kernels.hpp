@@ -161,14 +161,17 @@ hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32
 // ranges, no transposes.  M, N multiples of 8; operands below 2 GiB.
 hipError_t launch_wgrad_kn(const void *A, int64_t a_rows, const void *B, int64_t b_rows, const int32_t *off, int G,
                            int M, int N, void *out, hipStream_t s);
-// out[m][n] = sum_{k < K} AT[m][k] BT[n][k] for one group (koff = {0, K}), AT [M, lda] and BT
-// [N, ldb] K-contiguous, K a multiple of 32, float output, split along K into
-// wgrad_ksplit(M, N, K) slices
-// when the output has few tiles: slice partials in part (that many * M * N floats), added
-// in order into out.
-int wgrad_ksplit(int M, int N, int64_t K);
-hipError_t launch_wgrad_ksplit(const void *AT, int64_t lda, const void *BT, int64_t ldb, const int32_t *koff, int M,
-                               int N, int64_t K, float *part, float *out, hipStream_t s);
+// out[i] = sum over s < S of part[s * n + i], in slice order (float, n a multiple of 4).
+hipError_t launch_ksplit_sum(const float *part, int S, int64_t n, float *out, hipStream_t s);
+// out[m][n] = sum over k < K of AT[m][k] B[k][n] in float for one group: AT [M, K] with row
+// stride K = poff[1] - poff[0] (a multiple of 32), B [b_rows, N] row-major with rows off_b[0]
+// .. off_b[1] - 1; the large-tile weight-gradient form cut along K into
+// wgrad_big_f32_splits(M, N, K) slices, their partials in part (that many * M * N floats)
+// added in order.  N a multiple of 8.
+int wgrad_big_f32_splits(int M, int N, int64_t K);
+hipError_t launch_wgrad_big_kn_f32(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
+                                   const int32_t *off_b, int M, int N, int64_t K, float *part, float *out,
+                                   hipStream_t s);
 // out[g][m][n] = sum over k < K_g of AT_g[m][k] B[off_b[g] + k][n]: AT group-major transposed
 // (as for launch_wgrad_big, K_g = poff[g+1] - poff[g]), B [b_rows, N] row-major (K-major,
 // unpadded; k past the group's rows reads zero); 256 x 256 tiles.
