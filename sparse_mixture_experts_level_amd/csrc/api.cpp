@@ -626,18 +626,15 @@ namespace {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdLayout {
-  size_t gu, dhp, dgu, hg, dxr, poff, dyT, dguT, xT, dgate, row_gate, dpart, dl, dl16, dlT, wr_part, dxrt, tpoff,
-      sh_off, gus, dhs, dgus, hs, dxs, dyTT, dgusT, total;
+  size_t dhp, dgu, hg, dxr, poff, dyT, dguT, xT, row_gate, dpart, dl, dl16, dlT, wr_part, dxrt, tpoff, sh_off, dhs,
+      dgus, hs, dxs, dyTT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
   bool long_k, shared_long;
-  // streaming regime: the G|U recompute forms the SwiGLU backward in its epilogue (no
-  // float G|U buffer, gate gradients as per-16-column partial dot products)
-  bool fused, shared_fused;
 };
 
 BwdLayout bwd_layout(const moe_desc &D) {
   BwdLayout L{};
-  const int64_t T = D.num_tokens, E = D.num_experts, k = D.top_k, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
+  const int64_t T = D.num_tokens, E = D.num_experts, d = D.d_model, f = D.d_ff, fs = D.d_ff_shared;
   const int64_t R = max_rows(D);
   L.Rpad = round_up(R + 32 * E, 8);  // each group padded to a multiple of 32 rows
   L.Tpad = round_up(T, 32);
@@ -649,9 +646,6 @@ BwdLayout bwd_layout(const moe_desc &D) {
     return at;
   };
   const int64_t s = 2;
-  L.fused = !moe::grouped_gemm_big_regime(R, (int)E, std::max(1, group_rows_bound(D)));
-  L.shared_fused = fs > 0 && !moe::grouped_gemm_big_regime(T, 1, (int)T);
-  L.gu = take(L.fused ? 0 : R * 2 * f * 4);  // float
   L.dhp = take(R * f * s);
   L.dgu = take(R * 2 * f * s);
   L.hg = take(R * f * s);
@@ -664,9 +658,8 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dyT = take(L.long_k ? d * L.Rpad * s : R * d * s);  // transposed, or gathered rows
   L.dguT = take(L.long_k ? 2 * f * L.Rpad * s : 0);
   L.xT = take(R * d * s);                                // gathered rows
-  L.dgate = take(L.fused ? 0 : T * k * 4);
-  L.row_gate = take(L.fused ? R * 4 : 0);
-  L.dpart = take(L.fused ? R * (f / 16) * 4 : 0);
+  L.row_gate = take(R * 4);
+  L.dpart = take(R * (f / 16) * 4);  // gate gradients: dH' . H per row and 16-column block
   L.dl = take(T * E * 4);
   L.dl16 = take(T * L.Epad * s);
   L.dlT = take(L.Epad * L.Tpad * s);
@@ -675,7 +668,6 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.dxrt = take(T * d * s);
   L.tpoff = take(2 * 4);
   L.sh_off = take(2 * 4);
-  L.gus = take(fs && !L.shared_fused ? T * 2 * fs * 4 : 0);  // float
   L.dhs = take(fs ? T * fs * s : 0);
   L.dgus = take(fs ? T * 2 * fs * s : 0);
   L.hs = take(fs ? T * fs * s : 0);
@@ -786,39 +778,24 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   MOE_TRY(hcall(moe::launch_fill_i32(sh_off, 2, 0, T, stream), "offsets"));
 
   // ---- routed experts
-  float *dgate = L.fused ? nullptr : at<float>(ws, L.dgate);
   if (R > 0) {
     if (L.long_k) MOE_TRY(hcall(moe::launch_pad_offsets(offsets, E, poff, stream), "padded offsets"));
     // dH' = dy W_d: W_d [d, f] per expert is K-major for this product
-    auto a = gemm_args(E, R, grb, dy, row_token, T, offsets, weights->w_down, (int64_t)d * f, f, d, W(L.dhp));
-    a.w_kn = true;
-    MOE_TRY(gemm(a, "dH' grouped GEMM"));
-    if (L.fused) {
-      // G | U of every kept row recomputed from x, and the SwiGLU backward formed from
-      // them in the same kernel: dG | dU, g H and the gate gradients' block partials
-      MOE_TRY(hcall(moe::launch_row_gate(serving, slot, offsets, gates, (int64_t)T * k, at<float>(ws, L.row_gate),
-                                         stream),
-                    "row gates"));
-      auto r = gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, f, d, W(L.dgu));
-      r.swiglu = true;
-      r.bwd_dhp = W(L.dhp);
-      r.bwd_row_gate = at<float>(ws, L.row_gate);
-      r.bwd_hg = W(L.hg);
-      r.bwd_dpart = at<float>(ws, L.dpart);
-      MOE_TRY(gemm(r, "gate_up recompute + SwiGLU backward"));
-    } else {
-      // G | U of every kept row, recomputed from x (float), then the SwiGLU backward
-      MOE_TRY(gemm(gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, 2 * f, d,
-                             W(L.gu), true),
-                   "gate_up recompute"));
-    }
-  }
-  if (!L.fused) MOE_TRY(hcall(moe::launch_fill_u32(dgate, (int64_t)T * k, 0u, stream), "zero gate gradients"));
-  if (R > 0) {
-    if (!L.fused)
-      MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gu), W(L.dhp), R, rows_dev, f, row_token, serving, slot, offsets,
-                                         gates, k, W(L.dgu), W(L.hg), dgate, stream),
-                    "SwiGLU backward"));
+    auto h = gemm_args(E, R, grb, dy, row_token, T, offsets, weights->w_down, (int64_t)d * f, f, d, W(L.dhp));
+    h.w_kn = true;
+    MOE_TRY(gemm(h, "dH' grouped GEMM"));
+    // G | U of every kept row recomputed from x, and the SwiGLU backward formed from them
+    // in the same kernel: dG | dU, g H and the gate gradients' block partials
+    MOE_TRY(hcall(moe::launch_row_gate(serving, slot, offsets, gates, (int64_t)T * k, at<float>(ws, L.row_gate),
+                                       stream),
+                  "row gates"));
+    auto r = gemm_args(E, R, grb, x, row_token, T, offsets, weights->w_gate_up, (int64_t)2 * f * d, f, d, W(L.dgu));
+    r.swiglu = true;
+    r.bwd_dhp = W(L.dhp);
+    r.bwd_row_gate = at<float>(ws, L.row_gate);
+    r.bwd_hg = W(L.hg);
+    r.bwd_dpart = at<float>(ws, L.dpart);
+    MOE_TRY(gemm(r, "gate_up recompute + SwiGLU backward"));
     // dx rows = [dG dU] W_gu (W_gu [2f, d] per expert is K-major for this product)
     auto a = gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, weights->w_gate_up, (int64_t)2 * f * d, d, 2 * f,
                        W(L.dxr));
@@ -858,8 +835,8 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   }
 
   // ---- router: dl from the gate gradients; dW_r = dl^T x, dx += dl W_r
-  MOE_TRY(hcall(moe::launch_gates_bwd(ids, gates, dgate, L.fused ? at<float>(ws, L.dpart) : nullptr, f / 16, serving,
-                                      slot, offsets, T, E, k, (int)L.Epad, at<float>(ws, L.dl), W(L.dl16), stream),
+  MOE_TRY(hcall(moe::launch_gates_bwd(ids, gates, at<float>(ws, L.dpart), f / 16, serving, slot, offsets, T, E, k,
+                                      (int)L.Epad, at<float>(ws, L.dl), W(L.dl16), stream),
               "gate backward"));
   MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dl16), 0, T, (int)L.Epad, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
                                          W(L.dlT), L.Tpad, 0, stream),
@@ -885,7 +862,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
       a.w_kn = true;  // W_sd [d, f_s] is K-major for dy W_sd
       MOE_TRY(gemm(a, "shared dH'"));
     }
-    if (L.shared_fused) {
+    {
       // recompute and SwiGLU backward in one kernel (g = 1, no gate gradient)
       auto r = gemm_args(1, T, T, x, nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, fs, d,
                          W(L.dgus));
@@ -893,13 +870,6 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
       r.bwd_dhp = W(L.dhs);
       r.bwd_hg = W(L.hs);
       MOE_TRY(gemm(r, "shared gate_up recompute + SwiGLU backward"));
-    } else {
-      MOE_TRY(gemm(gemm_args(1, T, T, x, nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, 2 * fs,
-                             d, W(L.gus), true),
-                   "shared gate_up recompute"));
-      MOE_TRY(hcall(moe::launch_swiglu_bwd(W(L.gus), W(L.dhs), T, nullptr, fs, nullptr, nullptr, nullptr, nullptr,
-                                         nullptr, 1, W(L.dgus), W(L.hs), nullptr, stream),
-                    "shared SwiGLU backward"));
     }
     {
       auto a = gemm_args(1, T, T, W(L.dgus), nullptr, 0, sh_off, weights->w_shared_gate_up, (int64_t)2 * fs * d, d,

@@ -121,82 +121,13 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-// One wavefront per row r of the expert-sorted layout.  Finds the row's assignment
-// (t, j), takes its gate g (1 without gates), and from gu = [G | U] (float: silu' is
-// steep enough that a bf16 G would cost percent-level gradient error) and dh' computes
-// dgu = [dG | dU], hg = g * H and dgate[t][j] = dh' . H (float, fixed lane order).
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict__ gu, const bf16_t *__restrict__ dhp,
-                                                         int64_t rows, const int32_t *__restrict__ rows_dev, int f,
-                                                         const int32_t *__restrict__ row_token,
-                                                         const int32_t *__restrict__ serving,
-                                                         const int32_t *__restrict__ slot,
-                                                         const int32_t *__restrict__ offsets,
-                                                         const float *__restrict__ gates, int k,
-                                                         bf16_t *__restrict__ dgu, bf16_t *__restrict__ hg,
-                                                         float *__restrict__ dgate) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nrows = rows_dev ? min<int64_t>(rows, (int64_t)*rows_dev) : rows;
-  if (r >= nrows) return;
-  float g = 1.0f;
-  int jt = -1;
-  int64_t t = r;
-  if (gates) {
-    t = row_token[r];
-    for (int j = 0; j < k; ++j) {
-      const int sl = slot[t * k + j];
-      if (sl >= 0 && (int64_t)offsets[serving[t * k + j]] + sl == r) jt = j;
-    }
-    g = jt >= 0 ? gates[t * k + jt] : 0.0f;
-  }
-  const float *G = gu + (size_t)r * 2 * f, *U = G + f;
-  const bf16_t *D = dhp + (size_t)r * f;
-  bf16_t *dG = dgu + (size_t)r * 2 * f, *dU = dG + f;
-  bf16_t *HG = hg + (size_t)r * f;
-  float dot = 0.0f;
-  for (int c = lane * 8; c < f; c += 64 * 8) {
-    const u32x4 dv = ldg16(D + c);
-    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(G + c), g1 = *reinterpret_cast<const f32x4 *>(G + c + 4);
-    const f32x4 u0 = *reinterpret_cast<const f32x4 *>(U + c), u1 = *reinterpret_cast<const f32x4 *>(U + c + 4);
-    u32x4 og, ou, oh;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float z[2], u[2], d[2], rg[2], ru[2], rh[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = 2 * q + h;
-        z[h] = e < 4 ? g0[e] : g1[e - 4];
-        u[h] = e < 4 ? u0[e] : u1[e - 4];
-        d[h] = bf16_to_f32(bf16_t(dv[q] >> (16 * h)));
-        const float sz = silu_f32(z[h]);
-        const float H = sz * u[h];
-        dot += d[h] * H;
-        const float dh = g * d[h];
-        rg[h] = dh * u[h] * silu_grad_f32(z[h]);
-        ru[h] = dh * sz;
-        rh[h] = g * H;
-      }
-      og[q] = pack_bf16x2(rg[0], rg[1]);
-      ou[q] = pack_bf16x2(ru[0], ru[1]);
-      oh[q] = pack_bf16x2(rh[0], rh[1]);
-    }
-    stg16(dG + c, og);
-    stg16(dU + c, ou);
-    stg16(HG + c, oh);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
-  if (dgate && lane == 0 && jt >= 0) dgate[t * k + jt] = dot;
-}
-
 // Gradient of the renormalised gates with respect to the logits, one wavefront per token:
 // dl[t][ids_j] = g_j (dg_j - sum_j' g_j' dg_j'), zero elsewhere; written as float [T, E]
-// and as bf16 [T, Epad] (zero padded).  dg_j = dL/dg_j is dgate[t][j], or, with dpart,
-// the sum of the nb block dot products dH' . H of the assignment's row (0 when dropped),
-// added lane-strided and then in a fixed butterfly: the same value in every lane.
+// and as bf16 [T, Epad] (zero padded).  dg_j = dL/dg_j is the sum of the nb block dot
+// products dH' . H of the assignment's row in dpart (0 when dropped), added lane-strided
+// and then in a fixed butterfly: the same value in every lane.
 __global__ __launch_bounds__(256) void gates_bwd_kernel(const int32_t *__restrict__ ids,
                                                         const float *__restrict__ gates,
-                                                        const float *__restrict__ dgate,
                                                         const float *__restrict__ dpart, int nb,
                                                         const int32_t *__restrict__ serving,
                                                         const int32_t *__restrict__ slot,
@@ -219,18 +150,13 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const int32_t *__restric
   float s = 0.0f;
   for (int j = 0; j < k; ++j) {
     const size_t tj = (size_t)t * k + j;
-    float dg;
-    if (dpart) {
-      const int sl = slot[tj];
-      dg = 0.0f;
-      if (sl >= 0) {
-        const float *p = dpart + ((size_t)offsets[serving[tj]] + sl) * nb;
-        for (int b = lane; b < nb; b += 64) dg += p[b];
+    const int sl = slot[tj];
+    float dg = 0.0f;
+    if (sl >= 0) {
+      const float *p = dpart + ((size_t)offsets[serving[tj]] + sl) * nb;
+      for (int b = lane; b < nb; b += 64) dg += p[b];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) dg += __shfl_xor(dg, o, 64);
-      }
-    } else {
-      dg = dgate[tj];
+      for (int o = 1; o < 64; o <<= 1) dg += __shfl_xor(dg, o, 64);
     }
     const float g = gates[tj];
     s += g * dg;  // same order in every lane
@@ -492,23 +418,12 @@ hipError_t launch_fill_u32(void *p, int64_t n_words, uint32_t v, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, const int32_t *rows_dev, int f,
-                             const int32_t *row_token, const int32_t *serving, const int32_t *slot,
-                             const int32_t *offsets, const float *gates, int k, void *dgu, void *hg, float *dgate,
-                             hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                     static_cast<const float *>(gu), static_cast<const bf16_t *>(dhp), rows, rows_dev, f, row_token,
-                     serving, slot, offsets, gates, k, static_cast<bf16_t *>(dgu), static_cast<bf16_t *>(hg), dgate);
-  return hipGetLastError();
-}
-
-hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, const float *dpart, int nb,
-                            const int32_t *serving, const int32_t *slot, const int32_t *offsets, int T, int E, int k,
-                            int Epad, float *dl, void *dl16, hipStream_t s) {
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dpart, int nb, const int32_t *serving,
+                            const int32_t *slot, const int32_t *offsets, int T, int E, int k, int Epad, float *dl,
+                            void *dl16, hipStream_t s) {
   if (Epad > MOE_MAX_EXPERTS_DEV + 63) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, ids, gates, dgate, dpart, nb,
-                     serving, slot, offsets, T, E, k, Epad, dl, static_cast<bf16_t *>(dl16));
+  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, ids, gates, dpart, nb, serving,
+                     slot, offsets, T, E, k, Epad, dl, static_cast<bf16_t *>(dl16));
   return hipGetLastError();
 }
 

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // rows past offsets_b[g+1] read zeros); every group M x n_out, written at out + g * M * n_out.
 // APK: A is in the packed tile layout (pack_rows_kernel); OPK: the SwiGLU output is
 // written in that layout, for a following large-tile GEMM over the same groups.
-template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false, bool APK = false, bool OPK = false>
+template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false, bool APK = false, bool OPK = false,
+          bool GB = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
                                                                          int64_t lda, int64_t ldb, int M,
                                                                          float *__restrict__ split_out,
                                                                          int64_t split_stride,
-                                                                         const int32_t *__restrict__ offsets_b) {
+                                                                         const int32_t *__restrict__ offsets_b,
+                                                                         const SwigluBwdOut gb) {
   // Eight waves (two per SIMD) in a 2 x 4 arrangement, each 128 rows x 64 weight rows.
   constexpr int WN_W = 4;                        // waves along the weight rows
   constexpr int NBUF = 4;                        // LDS stages
@@ -121,6 +123,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   static_assert(!BKN || !SWIGLU, "K-major operands: plain store");
   static_assert(!(APK || OPK) || !WG, "packed operands: the forward form");
   static_assert(!OPK || SWIGLU, "packed output: the SwiGLU projection");
+  static_assert(!GB || (SWIGLU && !WG && !APK && !OPK && sizeof(OutT) == 2),
+                "SwiGLU backward: the forward form's gate and up blocks, bf16 gradients");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
@@ -418,6 +422,106 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   constexpr int PER = TILE / 16384;  // 16 KB regions per stage array
   uint8_t *stage = (wave < 4 ? bufA((wave & 3) / PER) : bufB((wave & 3) / PER)) + ((wave & 3) % PER) * 16384;
   const int lr = lane & 31, lh = lane >> 5;
+  if constexpr (GB) {
+    // SwiGLU backward from the float G (acc[i][0]) and U (acc[i][1]) of each (row,
+    // column): lane l holds row wm * 128 + i * 32 + (l & 31) and, per q = 0..3, the four
+    // consecutive columns n0 + wn * 32 + 8 q + 4 (l / 32) .. + 3.  With g the row's gate:
+    // dG = g dH' U silu'(G), dU = g dH' silu(G), g H, and the dot dH' . H over each
+    // 16-column block (q = 0, 1 and q = 2, 3), added over the lane's eight values in order
+    // and then with lane l ^ 32's.  The wave's 128 rows x 32 columns move through its
+    // 16 KB of LDS as two 8 KB halves laid out as the forward's H stage (64-byte rows,
+    // 16-byte chunk c of row r at c ^ ((r >> 2) & 3)), in and out as 16-byte runs: dH'
+    // in to half 0; dU back into half 0 (each 8 bytes read and then overwritten by the
+    // same lane) and dG into half 1; both out; then g H, formed again from the registers,
+    // into half 0 and out.  A wave's LDS accesses complete in order.
+    const int cw = n0 + wn * 32;  // the wave's first column
+    uint8_t *h0 = stage, *h1 = stage + 8192;
+    auto lds_at = [&](int row, int q) { return row * 64 + ((q ^ ((row >> 2) & 3)) << 4) + lh * 8; };
+    // 16-byte run it of the wave's block: row it * 16 + lane / 4, chunk lane % 4
+    auto run_row = [&](int it) { return it * 16 + (lane >> 2); };
+    auto run_lds = [&](int it) {
+      const int row = run_row(it), c = lane & 3;
+      return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+    };
+    if (cw < n_out) {  // wave-uniform: whole 32-column blocks (n_out a multiple of 32)
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rl = wm * 128 + run_row(it);
+        if (rl < rows)
+          *reinterpret_cast<u32x4 *>(h0 + run_lds(it)) =
+              ldg16(gb.dhp + (size_t)(m0 + rl) * n_out + cw + (lane & 3) * 8);
+      }
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      float gr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = wm * 128 + i * 32 + lr;
+        const bool ok = rl < rows;
+        gr[i] = gb.row_gate ? (ok ? gb.row_gate[m0 + rl] : 0.0f) : 1.0f;
+        float dot[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int at = lds_at(i * 32 + lr, q);
+          const uint2 dv = *reinterpret_cast<const uint2 *>(h0 + at);
+          float rg[4], ru[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[i][0][4 * q + e], u = acc[i][1][4 * q + e];
+            const float d = bf16_to_f32(bf16_t((e < 2 ? dv.x : dv.y) >> (16 * (e & 1))));
+            const float sg = sigmoid_fast(z);
+            const float sz = z * sg;  // silu(z)
+            dot[q >> 1] += d * (sz * u);
+            const float dh = gr[i] * d;
+            rg[e] = dh * u * (sg * (1.0f + z * (1.0f - sg)));  // silu'(z)
+            ru[e] = dh * sz;
+          }
+          *reinterpret_cast<uint2 *>(h1 + at) = uint2{pack_bf16x2(rg[0], rg[1]), pack_bf16x2(rg[2], rg[3])};
+          *reinterpret_cast<uint2 *>(h0 + at) = uint2{pack_bf16x2(ru[0], ru[1]), pack_bf16x2(ru[2], ru[3])};
+        }
+        // lane l's blocks hold columns 8 q + 4 (l / 32): lane l and l ^ 32 together cover them
+        const float d0 = dot[0] + __shfl_xor(dot[0], 32, 64), d1 = dot[1] + __shfl_xor(dot[1], 32, 64);
+        if (gb.dpart && ok && lh == 0)
+          *reinterpret_cast<float2 *>(gb.dpart + (size_t)(m0 + rl) * (n_out / 16) + cw / 16) = float2{d0, d1};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rl = wm * 128 + run_row(it);
+        if (rl < rows) {
+          bf16_t *o = out + (size_t)(m0 + rl) * 2 * n_out + cw + (lane & 3) * 8;
+          stg16(o, *reinterpret_cast<const u32x4 *>(h1 + run_lds(it)));
+          stg16(o + n_out, *reinterpret_cast<const u32x4 *>(h0 + run_lds(it)));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // half 0 read out before g H overwrites it
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float rh[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[i][0][4 * q + e], u = acc[i][1][4 * q + e];
+            rh[e] = gr[i] * (z * sigmoid_fast(z) * u);
+          }
+          *reinterpret_cast<uint2 *>(h0 + lds_at(i * 32 + lr, q)) =
+              uint2{pack_bf16x2(rh[0], rh[1]), pack_bf16x2(rh[2], rh[3])};
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rl = wm * 128 + run_row(it);
+        if (rl < rows)
+          stg16(gb.hg + (size_t)(m0 + rl) * n_out + cw + (lane & 3) * 8,
+                *reinterpret_cast<const u32x4 *>(h0 + run_lds(it)));
+      }
+    }
+    return;
+  }
   if constexpr (SWIGLU) {
     static_assert(sizeof(OutT) == 2 && NI == 2, "SwiGLU: bf16 output, one gate and one up block per wave");
     // 128 rows x 32 columns of H, 64-byte rows; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
@@ -547,7 +651,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t *__restrict
 
 }  // namespace
 
-template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false, bool APK = false, bool OPK = false>
+template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false, bool APK = false, bool OPK = false, bool GB = false>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
@@ -555,12 +659,14 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
   // K splits only for a plain bf16 store with a workspace for the partials
   float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
+  const SwigluBwdOut gb{static_cast<const bf16_t *>(a.bwd_dhp), a.bwd_row_gate, static_cast<bf16_t *>(a.bwd_hg),
+                        a.bwd_dpart};
   const int64_t split_stride = rows_total_max * a.n_out;
   const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK>), dim3((unsigned)grid), dim3(512), 0,
-                     s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK, GB>), dim3((unsigned)grid), dim3(512),
+                     0, s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr);
+                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr, gb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t blocks = std::min<int64_t>((rows_total_max * a.n_out / 8 + 255) / 256, 4096);
@@ -572,6 +678,10 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
 
 // Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
 hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  if (a.bwd_dhp) {  // the SwiGLU backward epilogue: plain rows in, bf16 gradients out
+    if (!a.swiglu || a.out_f32 || a.w_kn || a.a_packed || a.out_packed || a.n_out % 32) return hipErrorInvalidValue;
+    return launch_big<true, bf16_t, false, false, false, true>(a, rows_total_max, s);
+  }
   if (a.a_packed || a.out_packed) {  // the packed tile layout (pack_rows): SwiGLU in, plain down
     if (a.w_kn || a.out_f32) return hipErrorInvalidValue;
     if (a.swiglu) return a.a_packed ? launch_big<true, bf16_t, false, true, true>(a, rows_total_max, s)
@@ -616,7 +726,7 @@ hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff,
   hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true>), dim3((unsigned)grid),
                      dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G,
                      static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
-                     M, nullptr, (int64_t)0, off_b);
+                     M, nullptr, (int64_t)0, off_b, SwigluBwdOut{});
   return hipGetLastError();
 }
 
@@ -644,7 +754,8 @@ hipError_t launch_wgrad_big_kn_f32(const void *AT, int64_t lda, const int32_t *p
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float, true, true>), dim3((unsigned)grid), dim3(512), 0, s,
                      static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, 1, static_cast<const bf16_t *>(B),
-                     (int64_t)0, N, S, out, n_tiles, lda, b_rows, M, S > 1 ? part : nullptr, (int64_t)M * N, off_b);
+                     (int64_t)0, N, S, out, n_tiles, lda, b_rows, M, S > 1 ? part : nullptr, (int64_t)M * N, off_b,
+                     SwigluBwdOut{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_ksplit_sum(part, S, (int64_t)M * N, out, s);

@@ -413,7 +413,7 @@ bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_ma
 
 hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s) {
   if (grouped_gemm_big_regime(a.rows_max, a.num_groups, a.group_rows_max))
-    return a.bwd_dhp ? hipErrorInvalidValue : launch_grouped_gemm_big_bf16(a, a.rows_max, s);
+    return launch_grouped_gemm_big_bf16(a, a.rows_max, s);
   return launch_grouped_gemm_stream_bf16(a, s);
 }
 

@@ -84,7 +84,7 @@ struct GroupedGemmArgs {
   // packed_rows_bytes(rows_max, num_groups, n_out)).
   bool a_packed = false;
   bool out_packed = false;
-  // SwiGLU backward epilogue (streaming regime, with swiglu, bf16): instead of H, the
+  // SwiGLU backward epilogue (with swiglu, bf16, plain row layout): instead of H, the
   // kernel forms from the float G, U of each row and bwd_dhp = dH' (bf16 [rows, n_out],
   // rows in group order) out = [dG | dU] (bf16 [rows, 2 n_out]), bwd_hg = g H (bf16
   // [rows, n_out]) and, when bwd_dpart is set, the dot products dH' . H of each row over
@@ -141,16 +141,11 @@ hipError_t launch_transpose_bf16(const void *in, int64_t in_stride_b, int64_t ro
 // poff[g] = sum over g' < g of ceil32(off[g'+1] - off[g']), poff[G] = total
 hipError_t launch_pad_offsets(const int32_t *off, int G, int32_t *poff, hipStream_t s);
 hipError_t launch_fill_u32(void *p, int64_t n_words, uint32_t v, hipStream_t s);
-// per row: dgu = [dG | dU], hg = g * H, dgate[t][j] = dh' . H (gates NULL: g = 1, rows are tokens)
-hipError_t launch_swiglu_bwd(const void *gu, const void *dhp, int64_t rows, const int32_t *rows_dev, int f,
-                             const int32_t *row_token, const int32_t *serving, const int32_t *slot,
-                             const int32_t *offsets, const float *gates, int k, void *dgu, void *hg, float *dgate,
-                             hipStream_t s);
-// dl (float [T, E]) and dl16 (bf16 [T, Epad]) from the gate gradients dg: dgate [T, k], or
-// with dpart the sums of the nb block partials [rows, nb] of each kept assignment's row.
-hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dgate, const float *dpart, int nb,
-                            const int32_t *serving, const int32_t *slot, const int32_t *offsets, int T, int E, int k,
-                            int Epad, float *dl, void *dl16, hipStream_t s);
+// dl (float [T, E]) and dl16 (bf16 [T, Epad]) from the gate gradients: dg of each kept
+// assignment is the sum of the nb block partials [rows, nb] of its row in dpart.
+hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float *dpart, int nb, const int32_t *serving,
+                            const int32_t *slot, const int32_t *offsets, int T, int E, int k, int Epad, float *dl,
+                            void *dl16, hipStream_t s);
 // row_gate[offsets[serving[i]] + slot[i]] = gates[i] for every kept assignment i < n.
 hipError_t launch_row_gate(const int32_t *serving, const int32_t *slot, const int32_t *offsets, const float *gates,
                            int64_t n, float *row_gate, hipStream_t s);
