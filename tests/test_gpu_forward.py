@@ -196,6 +196,20 @@ def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards)
     assert row_rel_err(to_np(total), to_np(full).astype(np.float64)) <= 2e-2
 
 
+@pytest.mark.parametrize("T,d,E,k,f,cf", [
+    (4096, 128, 8, 2, 64, 1.0),
+    (4100, 256, 16, 4, 64, None),   # a ragged last workgroup of tokens
+    (4608, 64, 5, 2, 64, 1.25),     # d = 64: three of the four waves get no chunk; experts past 5 read zeros
+    (4096, 2880, 16, 4, 64, 1.0),   # 45 chunks of d split unevenly over the waves
+])
+def test_fused_router_many_tokens(T, d, E, k, f, cf):
+    """At most 16 experts and >= 4096 tokens: router linear and top-k run as one kernel."""
+    w = wl.Workload("fused_router", T, d, E, k, f, cf, "bf16", offset="boost4")
+    say(f"fused router T={T} d={d} E={E} k={k}")
+    inp = wl.make_inputs(w, seed=11, device=DEV)
+    _run_and_check(inp, sample=np.arange(0, T, 37))
+
+
 @pytest.mark.parametrize("T,d,E,k,f,cf,order,overflow", [
     (300, 256, 8, 2, 192, 1.0, "rank", "drop"),
     (300, 256, 8, 2, 192, 1.0, "token", "reroute"),
@@ -203,6 +217,8 @@ def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards)
     (513, 128, 16, 4, 128, 0.5, "token", "reroute"),   # every expert full after pass 1
     (257, 64, 4, 1, 64, 0.75, "token", "reroute"),
     (48, 128, 16, 2, 64, 0.5, "rank", "drop"),          # small batch
+    (4100, 192, 12, 4, 64, 1.0, "token", "reroute"),    # router linear and top-k in one kernel
+    (4096, 128, 64, 1, 64, 0.5, "rank", "reroute"),
 ])
 def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
     """moe_forward with the rank-major fill and/or redirection of overflow vs the oracle."""
