@@ -630,6 +630,9 @@ struct BwdLayout {
       dgus, hs, dxs, dyTT, dgusT, total;
   int64_t Rpad, Tpad, Epad;
   bool long_k, shared_long;
+  // many rows per expert: dW_gu is formed as its transpose x^T [dG dU] when x (d columns)
+  // is the smaller operand to transpose than [dG dU] (2f columns)
+  bool x_first;
 };
 
 BwdLayout bwd_layout(const moe_desc &D) {
@@ -655,9 +658,10 @@ BwdLayout bwd_layout(const moe_desc &D) {
   // gathered to [R, d]); when experts hold many rows the first operand is transposed instead
   // (padded groups), since the matrix cores then need the LDS read path for themselves
   L.long_k = R / E >= 256 && d >= 256 && f >= 256;
+  L.x_first = L.long_k && d < 2 * f;
   L.dyT = take(L.long_k ? d * L.Rpad * s : R * d * s);  // transposed, or gathered rows
-  L.dguT = take(L.long_k ? 2 * f * L.Rpad * s : 0);
-  L.xT = take(R * d * s);                                // gathered rows
+  L.dguT = take(L.long_k && !L.x_first ? 2 * f * L.Rpad * s : 0);
+  L.xT = take(L.x_first ? d * L.Rpad * s : R * d * s);  // transposed, or gathered rows
   L.row_gate = take(R * 4);
   L.dpart = take(R * (f / 16) * 4);  // gate gradients: dH' . H per row and 16-column block
   L.dl = take(T * E * 4);
@@ -809,16 +813,27 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
       MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.dyT), L.Rpad,
                                              0, stream),
                   "dy transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad,
-                                             W(L.dguT), L.Rpad, 0, stream),
-                  "dGU transpose"));
-      MOE_TRY(hcall(moe::launch_gather_rows(x, row_token, rows_dev, R, d, 2, W(L.xT), stream), "x gather"));
       MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyT), L.Rpad, poff, W(L.hg), R, offsets, E, d, f, grads->dw_down,
                                            stream),
                   "dW_down"));
-      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dguT), L.Rpad, poff, W(L.xT), R, offsets, E, 2 * f, d,
-                                           grads->dw_gate_up, stream),
-                  "dW_gate_up"));
+      if (L.x_first) {
+        // dW_gu^T = x^T [dG dU]: x transposed like dy, [dG dU] read K-major as written,
+        // the product stored transposed
+        MOE_TRY(hcall(moe::launch_transpose_bf16(x, 0, R, d, 1, row_token, offsets, poff, E, L.Rpad, W(L.xT),
+                                               L.Rpad, 0, stream),
+                      "x transpose"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.xT), L.Rpad, poff, W(L.dgu), R, offsets, E, d, 2 * f,
+                                             grads->dw_gate_up, stream, true),
+                      "dW_gate_up"));
+      } else {
+        MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgu), 0, R, 2 * f, 1, nullptr, offsets, poff, E, L.Rpad,
+                                               W(L.dguT), L.Rpad, 0, stream),
+                      "dGU transpose"));
+        MOE_TRY(hcall(moe::launch_gather_rows(x, row_token, rows_dev, R, d, 2, W(L.xT), stream), "x gather"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dguT), L.Rpad, poff, W(L.xT), R, offsets, E, 2 * f, d,
+                                             grads->dw_gate_up, stream),
+                      "dW_gate_up"));
+      }
     } else {
       // few rows per expert (write bound): both operands K-major straight from the
       // row-major activations (dy and x rows gathered into expert order), no transposes

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // APK: A is in the packed tile layout (pack_rows_kernel); OPK: the SwiGLU output is
 // written in that layout, for a following large-tile GEMM over the same groups.
 template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false, bool APK = false, bool OPK = false,
-          bool GB = false>
+          bool GB = false, bool TO = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
@@ -125,6 +125,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   static_assert(!OPK || SWIGLU, "packed output: the SwiGLU projection");
   static_assert(!GB || (SWIGLU && !WG && !APK && !OPK && sizeof(OutT) == 2),
                 "SwiGLU backward: the forward form's gate and up blocks, bf16 gradients");
+  static_assert(!TO || (WG && sizeof(OutT) == 2), "transposed output: the weight-gradient form, bf16");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
@@ -381,7 +382,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(bfr[kk][j], af[kk][i], acc[i][j]);
+          for (int j = 0; j < NI; ++j) {
+            if constexpr (TO)  // A first: a lane's accumulator holds four consecutive rows
+              acc[i][j] = mfma32(af[kk][i], bfr[kk][j], acc[i][j]);
+            else
+              acc[i][j] = mfma32(bfr[kk][j], af[kk][i], acc[i][j]);
+          }
       __builtin_amdgcn_s_setprio(0);
     };
     auto bar = [&]() {
@@ -591,6 +597,33 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next pass writes
       }
+    } else if constexpr (TO) {
+      // Transposed bf16 store, out[n][m] with row stride M: with A the MFMA's first operand,
+      // block (i, j) holds in lane l column j * 32 + (l & 31) and the four consecutive rows
+      // i * 32 + 8 (r / 4) + 4 (l / 32) .. + 3.  The wave's 128 x 64 goes to LDS as 64
+      // column-rows of 128 values (256 bytes; 16-byte chunk c of column-row n at c ^ (n & 15))
+      // and leaves as 16-byte runs along the rows.
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = j * 32 + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2 *>(stage + n * 256 + (((4 * i + q) ^ (n & 15)) << 4) + lh * 8) = v;
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int c = lane & 15, grow = wm * 128 + c * 8;  // eight rows per 16-byte run
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int n = it * 4 + (lane >> 4), gn = gcol0 + n;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + n * 256 + ((c ^ (n & 15)) << 4));
+        if (grow < rows && gn < n_out) stg16(obase + (size_t)gn * M + m0 + grow, v);
+      }
     } else if constexpr (sizeof(OutT) == 2) {
       // bf16: 128 rows x 64 columns, 128-byte rows; chunk c of row r at c ^ ((r >> 1) & 7)
 #pragma unroll
@@ -716,17 +749,23 @@ hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int
 // AT_g[m][k] B[off_b[g] + k][n], AT_g = AT + poff[g] * M with row stride K_g = poff[g+1] -
 // poff[g] (group-major transposed, zero padded to multiples of 32), B [b_rows, N] row-major
 // with group g's rows off_b[g] .. off_b[g+1] - 1 (k past them: zero).  M and N multiples of
-// 8; an empty group writes zeros.
+// 8; an empty group writes zeros.  With `transposed`, out[g] is stored as [N, M] (out[g][n][m]).
 hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
-                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s) {
+                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s, bool transposed) {
   if (N % 8 || M % 8) return hipErrorInvalidValue;
   const int m_tiles = (M + BG_BM - 1) / BG_BM, n_tiles = (N + BG_BN - 1) / BG_BN;
   const int64_t grid = (int64_t)G * m_tiles * n_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true>), dim3((unsigned)grid),
-                     dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G,
-                     static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows,
-                     M, nullptr, (int64_t)0, off_b, SwigluBwdOut{});
+  if (transposed)
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true, false, false, false, true>),
+                       dim3((unsigned)grid), dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff,
+                       G, static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
+                       b_rows, M, nullptr, (int64_t)0, off_b, SwigluBwdOut{});
+  else
+    hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true>), dim3((unsigned)grid), dim3(512), 0, s,
+                       static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G, static_cast<const bf16_t *>(B),
+                       (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows, M, nullptr, (int64_t)0,
+                       off_b, SwigluBwdOut{});
   return hipGetLastError();
 }
 

@@ -168,8 +168,10 @@ hipError_t launch_wgrad_big_kn_f32(const void *AT, int64_t lda, const int32_t *p
                                    const int32_t *off_b, int M, int N, int64_t K, float *part, float *out,
                                    hipStream_t s);
 // out[g][m][n] = sum over k < K_g of AT_g[m][k] B[off_b[g] + k][n]: AT group-major transposed
-// (as for launch_wgrad_big, K_g = poff[g+1] - poff[g]), B [b_rows, N] row-major (K-major,
-// unpadded; k past the group's rows reads zero); 256 x 256 tiles.
+// (group g's [M, K_g] block at poff[g] * M, K_g = poff[g+1] - poff[g] a multiple of 32, zero
+// padding), B [b_rows, N] row-major (K-major, unpadded; k past the group's rows reads zero);
+// 256 x 256 tiles.  With `transposed` each out[g] is stored as [N, M] (out[g][n][m]).
 hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff, const void *B, int64_t b_rows,
-                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s);
+                               const int32_t *off_b, int G, int M, int N, void *out, hipStream_t s,
+                               bool transposed = false);
 }  // namespace moe

@@ -82,6 +82,7 @@ def _compare(w, ref, dx, grads):
     (200, 128, 32, 8, 64, 1.0, 128, "boost4"),
     (64, 64, 8, 2, 64, 0.1, 0, None),          # most assignments dropped, idle experts
     (1024, 256, 4, 2, 320, None, 0, None),     # hundreds of rows per expert: the large-tile kernels
+    (1024, 768, 4, 2, 256, None, 0, None),     # ... with d >= 2 f: [dG dU] transposed instead of x
     (600, 256, 6, 2, 128, None, 256, "boost4"),  # shared expert on the large-tile kernels, ragged tiles
 ])
 def test_backward_small_layers(T, d, E, k, f, cf, fs, offset):
