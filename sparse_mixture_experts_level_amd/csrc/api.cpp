@@ -677,8 +677,10 @@ BwdLayout bwd_layout(const moe_desc &D) {
   L.hs = take(fs ? T * fs * s : 0);
   L.dxs = take(fs ? T * d * s : 0);
   L.shared_long = T >= 256 && d >= 256 && fs >= 256;
-  L.dyTT = take(fs && L.shared_long ? d * L.Tpad * s : 0);
-  L.dgusT = take(fs && L.shared_long ? 2 * fs * L.Tpad * s : 0);
+  // shared weight gradients with many rows: the smaller of each product's two operands is
+  // transposed (dy or g H for dW_sd, [dG dU] or x for dW_sgu)
+  L.dyTT = take(fs && L.shared_long ? std::min(d, fs) * L.Tpad * s : 0);
+  L.dgusT = take(fs && L.shared_long ? std::min(2 * fs, d) * L.Tpad * s : 0);
   L.total = o;
   return L;
 }
@@ -893,18 +895,34 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
       MOE_TRY(gemm(a, "shared dx"));
     }
     if (L.shared_long) {
-      MOE_TRY(hcall(moe::launch_transpose_bf16(dy, 0, T, d, 1, nullptr, nullptr, nullptr, 0, L.Tpad, W(L.dyTT),
-                                             L.Tpad, 0, stream),
-                  "dy transpose"));
-      MOE_TRY(hcall(moe::launch_transpose_bf16(W(L.dgus), 0, T, 2 * fs, 1, nullptr, nullptr, nullptr, 0, L.Tpad,
-                                             W(L.dgusT), L.Tpad, 0, stream),
-                  "shared dGU transpose"));
-      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyTT), L.Tpad, tpoff, W(L.hs), T, sh_off, 1, d, fs,
-                                           grads->dw_shared_down, stream),
-                  "dW_shared_down"));
-      MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dgusT), L.Tpad, tpoff, x, T, sh_off, 1, 2 * fs, d,
-                                           grads->dw_shared_gate_up, stream),
-                  "dW_shared_gate_up"));
+      // each product transposes its smaller operand; the other form is stored transposed
+      auto tr = [&](const void *src, int cols, void *dst, const char *what) {
+        return hcall(moe::launch_transpose_bf16(src, 0, T, cols, 1, nullptr, nullptr, nullptr, 0, L.Tpad, dst, L.Tpad,
+                                                0, stream),
+                     what);
+      };
+      if (fs < d) {  // dW_sd^T = (g H)^T dy
+        MOE_TRY(tr(W(L.hs), fs, W(L.dyTT), "shared H transpose"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyTT), L.Tpad, tpoff, dy, T, sh_off, 1, fs, d,
+                                             grads->dw_shared_down, stream, true),
+                      "dW_shared_down"));
+      } else {
+        MOE_TRY(tr(dy, d, W(L.dyTT), "dy transpose"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dyTT), L.Tpad, tpoff, W(L.hs), T, sh_off, 1, d, fs,
+                                             grads->dw_shared_down, stream),
+                      "dW_shared_down"));
+      }
+      if (d < 2 * fs) {  // dW_sgu^T = x^T [dG dU]
+        MOE_TRY(tr(x, d, W(L.dgusT), "x transpose"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dgusT), L.Tpad, tpoff, W(L.dgus), T, sh_off, 1, d, 2 * fs,
+                                             grads->dw_shared_gate_up, stream, true),
+                      "dW_shared_gate_up"));
+      } else {
+        MOE_TRY(tr(W(L.dgus), 2 * fs, W(L.dgusT), "shared dGU transpose"));
+        MOE_TRY(hcall(moe::launch_wgrad_big_kn(W(L.dgusT), L.Tpad, tpoff, x, T, sh_off, 1, 2 * fs, d,
+                                             grads->dw_shared_gate_up, stream),
+                      "dW_shared_gate_up"));
+      }
     } else {
       MOE_TRY(hcall(moe::launch_wgrad_kn(dy, T, W(L.hs), T, sh_off, 1, d, fs, grads->dw_shared_down, stream),
                   "dW_shared_down"));

@@ -84,6 +84,7 @@ def _compare(w, ref, dx, grads):
     (1024, 256, 4, 2, 320, None, 0, None),     # hundreds of rows per expert: the large-tile kernels
     (1024, 768, 4, 2, 256, None, 0, None),     # ... with d >= 2 f: [dG dU] transposed instead of x
     (600, 256, 6, 2, 128, None, 256, "boost4"),  # shared expert on the large-tile kernels, ragged tiles
+    (600, 512, 6, 2, 128, None, 256, None),      # ... with f_s < d and d >= 2 f_s: the other transposes
 ])
 def test_backward_small_layers(T, d, E, k, f, cf, fs, offset):
     w = wl.Workload("bwd", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset=offset)
