@@ -933,7 +933,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   }
 
   // ---- dx: the expert rows of each token, the router term and the shared expert's
-  MOE_TRY(hcall(moe::launch_dx_gather(W(L.dxr), serving, slot, offsets, T, d, k, W(L.dxrt), dxs, dx, stream), "dx"));
+  MOE_TRY(hcall(moe::launch_dx_gather(W(L.dxr), R, serving, slot, offsets, T, d, k, W(L.dxrt), dxs, dx, stream), "dx"));
   return ok();
 }
 

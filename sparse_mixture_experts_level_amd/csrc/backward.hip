@@ -228,6 +228,56 @@ __global__ __launch_bounds__(256) void dx_gather_kernel(const bf16_t *__restrict
   }
 }
 
+// The same sum for k <= KB with every load unconditional: the token's kept rows are
+// resolved once, then each 16-byte column step issues all KB + 2 loads at once -- dropped
+// assignments (j < k), j >= k and absent terms read zeros through range-checked buffer
+// loads -- and adds them in the same order (zeros change nothing).
+template <int KB>
+__global__ __launch_bounds__(256) void dx_gather_wide_kernel(const bf16_t *__restrict__ dxr, int64_t rows,
+                                                             const int32_t *__restrict__ serving,
+                                                             const int32_t *__restrict__ slot,
+                                                             const int32_t *__restrict__ offsets, int T, int d, int k,
+                                                             const bf16_t *__restrict__ extra,
+                                                             const bf16_t *__restrict__ extra2,
+                                                             bf16_t *__restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint32_t dbytes = (uint32_t)d * 2u;
+  const rsrc_t rres = make_rsrc(dxr, (uint32_t)(rows * dbytes));
+  const rsrc_t eres = make_rsrc(extra, extra ? (uint32_t)T * dbytes : 0u);
+  const rsrc_t e2res = make_rsrc(extra2, extra2 ? (uint32_t)T * dbytes : 0u);
+  uint32_t roff[KB];
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    roff[j] = kOob;
+    if (j < k) {
+      const int sl = slot[(size_t)t * k + j];
+      if (sl >= 0) roff[j] = (uint32_t)(offsets[serving[(size_t)t * k + j]] + sl) * dbytes;
+    }
+  }
+  const uint32_t toff = (uint32_t)t * dbytes;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    u32x4 v[KB + 2];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) v[j] = buf_ld16(rres, roff[j] + (uint32_t)c * 2u);
+    v[KB] = buf_ld16(eres, toff + (uint32_t)c * 2u);
+    v[KB + 1] = buf_ld16(e2res, toff + (uint32_t)c * 2u);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KB + 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(bf16_t(v[j][q]));
+        acc[2 * q + 1] += bf16_to_f32(bf16_t(v[j][q] >> 16));
+      }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    stg16(dx + (size_t)t * d + c, o);
+  }
+}
+
 // The weight-gradient product straight from row-major activations, for short row
 // ranges (write bound): for group g with rows off[g] .. off[g+1] - 1,
 //   out[g][m][n] = sum over those rows r of A[r][m] * B[r][n]   (bf16 out),
@@ -436,8 +486,25 @@ hipError_t launch_row_gate(const int32_t *serving, const int32_t *slot, const in
   return hipGetLastError();
 }
 
-hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
-                            int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s) {
+hipError_t launch_dx_gather(const void *dxr, int64_t rows, const int32_t *serving, const int32_t *slot,
+                            const int32_t *offsets, int T, int d, int k, const void *extra, const void *extra2, void *dx,
+                            hipStream_t s) {
+  const bool wide = k <= 8 && (rows + 1) * d * 2 < ((int64_t)1 << 31) && ((int64_t)T + 1) * d * 2 < ((int64_t)1 << 31);
+  if (wide) {
+    const bf16_t *r = static_cast<const bf16_t *>(dxr), *e = static_cast<const bf16_t *>(extra),
+                 *e2 = static_cast<const bf16_t *>(extra2);
+    bf16_t *o = static_cast<bf16_t *>(dx);
+    const dim3 grid((unsigned)((T + 3) / 4));
+    if (k <= 1)
+      hipLaunchKernelGGL(dx_gather_wide_kernel<1>, grid, dim3(256), 0, s, r, rows, serving, slot, offsets, T, d, k, e, e2, o);
+    else if (k <= 2)
+      hipLaunchKernelGGL(dx_gather_wide_kernel<2>, grid, dim3(256), 0, s, r, rows, serving, slot, offsets, T, d, k, e, e2, o);
+    else if (k <= 4)
+      hipLaunchKernelGGL(dx_gather_wide_kernel<4>, grid, dim3(256), 0, s, r, rows, serving, slot, offsets, T, d, k, e, e2, o);
+    else
+      hipLaunchKernelGGL(dx_gather_wide_kernel<8>, grid, dim3(256), 0, s, r, rows, serving, slot, offsets, T, d, k, e, e2, o);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dx_gather_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
                      static_cast<const bf16_t *>(dxr), serving, slot, offsets, T, d, k,
                      static_cast<const bf16_t *>(extra), static_cast<const bf16_t *>(extra2), static_cast<bf16_t *>(dx));

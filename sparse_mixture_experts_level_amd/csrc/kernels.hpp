@@ -149,8 +149,11 @@ hipError_t launch_gates_bwd(const int32_t *ids, const float *gates, const float 
 // row_gate[offsets[serving[i]] + slot[i]] = gates[i] for every kept assignment i < n.
 hipError_t launch_row_gate(const int32_t *serving, const int32_t *slot, const int32_t *offsets, const float *gates,
                            int64_t n, float *row_gate, hipStream_t s);
-hipError_t launch_dx_gather(const void *dxr, const int32_t *serving, const int32_t *slot, const int32_t *offsets,
-                            int T, int d, int k, const void *extra, const void *extra2, void *dx, hipStream_t s);
+// dx[t] = sum over kept j of dxr[row(t, j)], then extra[t] and extra2[t] when given (float,
+// in that order); dxr holds `rows` rows.
+hipError_t launch_dx_gather(const void *dxr, int64_t rows, const int32_t *serving, const int32_t *slot,
+                            const int32_t *offsets, int T, int d, int k, const void *extra, const void *extra2, void *dx,
+                            hipStream_t s);
 // out[g][m][n] = sum over rows r in [off[g], off[g+1]) of A[r][m] B[r][n] from row-major
 // (K-major) A [a_rows, M] and B [b_rows, N], bf16 out; 128 x 128 tiles for short row
 // ranges, no transposes.  M, N multiples of 8; operands below 2 GiB.
