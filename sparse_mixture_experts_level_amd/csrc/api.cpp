@@ -118,8 +118,8 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, x_packed, hidden, y_perm,
-      sh_hidden, sh_out, sh_offsets, router_part, down_split, total;
+  size_t logits, ids, gates, counts, offsets, slot, row_token, spare, assigned, hist, x_packed, hidden, hidden_tail,
+      y_perm, sh_hidden, sh_out, sh_offsets, router_part, down_split, total;
 };
 
 // Whether the routed experts may take the large-tile regime (an expert can hold 256 rows)
@@ -160,6 +160,9 @@ Layout layout(const moe_desc &D) {
   const bool pack = packable(D);
   L.x_packed = take(pack ? (size_t)moe::packed_rows_bytes((int64_t)R, (int)E, (int)d) : 0);
   L.hidden = take(std::max(R * f * s, pack ? (size_t)moe::packed_rows_bytes((int64_t)R, (int)E, (int)f) : (size_t)0));
+  // H of the groups' tail rows (streaming kernel, row-major at the rows' own positions)
+  // when H itself is packed
+  L.hidden_tail = take(pack ? R * f * s : 0);
   L.y_perm = take(R * d * s);
   L.sh_hidden = take(fs ? T * fs * s : 0);
   L.sh_out = take(fs ? T * d * s : 0);
@@ -211,20 +214,33 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
-                           int64_t x_row_count = 0, float *split_ws = nullptr, void *x_packed = nullptr) {
-  if (x_packed && dtype == MOE_DTYPE_BF16 && moe::grouped_gemm_big_regime(rows_max, G, group_rows_max)) {
+                           int64_t x_row_count = 0, float *split_ws = nullptr, void *x_packed = nullptr,
+                           void *hidden_tail = nullptr) {
+  if (x_packed && hidden_tail && dtype == MOE_DTYPE_BF16 &&
+      moe::grouped_gemm_big_regime(rows_max, G, group_rows_max)) {
     // Large-tile regime: the gathered rows of x are first copied into the packed tile
     // layout, so that every stage of the gate_up projection loads one contiguous 16 KB
-    // block; the projection writes H in the same layout for the down projection.
+    // block; the projection writes H in the same layout for the down projection.  The
+    // groups' tail rows (left to the streaming kernel) use x and a row-major H instead.
+    // one tail choice for both projections and the packing: they number the same tiles
+    const int tail = moe::big_tails(G, std::min(d, f));
     const int64_t xb = moe::packed_rows_bytes(rows_max, G, d), hb = moe::packed_rows_bytes(rows_max, G, f);
-    MOE_TRY_HIP(moe::launch_pack_rows(x_rows, row_index, offsets, G, rows_max, d, x_packed, s), "pack x rows");
+    MOE_TRY_HIP(moe::launch_pack_rows(x_rows, row_index, offsets, G, rows_max, d, x_packed, s, tail), "pack x rows");
     moe::GroupedGemmArgs gu = projection_args(G, rows_max, group_rows_max, d, f, x_packed, offsets, w_gate_up, hidden,
                                               true, nullptr, xb);
     gu.a_packed = gu.out_packed = true;
+    gu.tail = tail;
+    gu.tail_A = x_rows;
+    gu.tail_row_index = row_index;
+    gu.tail_a_rows = row_index ? x_row_count : rows_max;
+    gu.tail_out = hidden_tail;
     MOE_TRY(run_projection(gu, dtype, s, "gate_up grouped GEMM"));
     moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows,
                                                 false, nullptr, hb);
     down.a_packed = true;
+    down.tail = tail;
+    down.tail_A = hidden_tail;
+    down.tail_a_rows = rows_max;
     down.split_ws = split_ws;
     MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
     return MOE_OK;
@@ -578,7 +594,8 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
     MOE_TRY(run_grouped_ffn(e_end - e_begin, rmax, std::max(1, group_rows_bound(D)), d, f, D.dtype, x,
                             offsets + e_begin, weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden),
                             stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr,
-                            packable(D) ? at<void>(ws, L.x_packed) : nullptr));
+                            packable(D) ? at<void>(ws, L.x_packed) : nullptr,
+                            packable(D) ? at<void>(ws, L.hidden_tail) : nullptr));
   }
   const void *shared = nullptr;
   if (fs > 0 && add_shared) {

@@ -77,14 +77,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-// Groups cut into blocks of BM rows: group g holds ceil(rows_g / BM) blocks, rows_g =
-// offsets[g+1] - offsets[g], numbered group after group.  One wavefront scans the
-// offsets; the results are equal in every lane.
+// Groups cut into blocks of BM rows: group g holds row_blocks<BM>(rows_g, tail) blocks,
+// rows_g = offsets[g+1] - offsets[g], numbered group after group -- ceil(rows_g / BM), but
+// with tail > 0 a last partial block of at most `tail` rows is left out (those rows are
+// another kernel's).  One wavefront scans the offsets; the results are equal in every lane.
+template <int BM>
+__host__ __device__ __forceinline__ int row_blocks(int rows, int tail) { return rows / BM + (rows % BM > tail ? 1 : 0); }
+
 // Block index m_lin -> its group (-1 past the last block), the group's first block and
 // its block count.
 template <int BM>
 __device__ __forceinline__ void find_row_block(const int32_t *offsets, int G, int m_lin, int &g_out, int &first,
-                                               int &count) {
+                                               int &count, int tail = 0) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   g_out = -1;
@@ -93,7 +97,7 @@ __device__ __forceinline__ void find_row_block(const int32_t *offsets, int G, in
   for (int g0 = 0; g0 < G; g0 += 64) {
     const int g = g0 + lane;
     int mt = 0;
-    if (g < G) mt = (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+    if (g < G) mt = row_blocks<BM>(offsets[g + 1] - offsets[g], tail);
     int incl = mt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -114,10 +118,10 @@ __device__ __forceinline__ void find_row_block(const int32_t *offsets, int G, in
 
 // Total row blocks over all groups, sum_g ceil(rows_g / BM).
 template <int BM>
-__device__ __forceinline__ int total_row_blocks(const int32_t *offsets, int G) {
+__device__ __forceinline__ int total_row_blocks(const int32_t *offsets, int G, int tail = 0) {
   const int lane = threadIdx.x & 63;
   int sum = 0;
-  for (int g = lane; g < G; g += 64) sum += (offsets[g + 1] - offsets[g] + BM - 1) / BM;
+  for (int g = lane; g < G; g += 64) sum += row_blocks<BM>(offsets[g + 1] - offsets[g], tail);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   return sum;

@@ -26,7 +26,7 @@ namespace moe {
 
 namespace {
 
-constexpr int BG_BM = 256, BG_BN = 256;
+constexpr int BG_BM = kBigTileRows, BG_BN = 256;
 
 // Pipeline: K advances in steps of 32.  Operand tiles go from HBM straight into LDS
 // (buffer loads with an LDS destination, no registers), into four stages that are
@@ -63,8 +63,8 @@ __host__ __device__ __forceinline__ int big_ksplit(int tiles, int steps) {
 __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__restrict__ part, int64_t stride,
                                                                const int32_t *__restrict__ offsets, int G,
                                                                int n_tiles, int steps, int n_out,
-                                                               bf16_t *__restrict__ out) {
-  const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+                                                               bf16_t *__restrict__ out, int tail) {
+  const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G, tail)) * n_tiles;
   const int ks = big_ksplit(tiles, steps);
   if (ks == 1) return;
   const int64_t rows = offsets[G];
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
                                                                          float *__restrict__ split_out,
                                                                          int64_t split_stride,
                                                                          const int32_t *__restrict__ offsets_b,
-                                                                         const SwigluBwdOut gb) {
+                                                                         const SwigluBwdOut gb, int tail) {
   // Eight waves (two per SIMD) in a 2 x 4 arrangement, each 128 rows x 64 weight rows.
   constexpr int WN_W = 4;                        // waves along the weight rows
   constexpr int NBUF = 4;                        // LDS stages
@@ -153,7 +153,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     // loose).
     // With split_out, few tiles are cut along K as well (big_ksplit()): split ks writes
     // its float partial sums to split_out + ks * split_stride, and a reduction adds them.
-    const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G)) * n_tiles;
+    // Tiles of at most `tail` rows (a group's last partial tile) are left to a streaming
+    // launch: they do not exist here.
+    const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G, tail)) * n_tiles;
     const int ksplit = split_out ? big_ksplit(tiles, K / BK) : 1;
     const int real_blocks = tiles * ksplit;
     if ((int)blockIdx.x >= real_blocks) return;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     int g, mt_first, mt_count;
     // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
     // (mt_first + mt_count) * n_tiles).  Within a group the order is chosen below.
-    find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count);
+    find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count, tail);
     // the scan's results are equal in every lane: keep them (and all that derives from
     // them, like the buffer resources) in scalar registers
     g = __builtin_amdgcn_readfirstlane(g);
@@ -661,11 +663,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
 __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t *__restrict__ src,
                                                         const int32_t *__restrict__ row_index,
                                                         const int32_t *__restrict__ offsets, int G, int K,
-                                                        bf16_t *__restrict__ out) {
+                                                        bf16_t *__restrict__ out, int tail) {
   const int steps = K / 32;
   const int m_lin = blockIdx.x / steps, kt = blockIdx.x - m_lin * steps;
   int g, first, count;
-  find_row_block<BG_BM>(offsets, G, m_lin, g, first, count);
+  find_row_block<BG_BM>(offsets, G, m_lin, g, first, count, tail);
   if (g < 0) return;
   const int m0 = offsets[g] + (m_lin - first) * BG_BM, row_end = offsets[g + 1];
   bf16_t *blk = out + ((size_t)m_lin * steps + kt) * (BG_BM * 32);
@@ -699,18 +701,20 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
   hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK, GB>), dim3((unsigned)grid), dim3(512),
                      0, s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr, gb);
+                     n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr, gb, a.tail);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t blocks = std::min<int64_t>((rows_total_max * a.n_out / 8 + 255) / 256, 4096);
   hipLaunchKernelGGL(big_split_reduce_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, split,
                      split_stride, a.offsets, a.num_groups, n_tiles, a.K / 32, a.n_out,
-                     static_cast<bf16_t *>(a.out));
+                     static_cast<bf16_t *>(a.out), a.tail);
   return hipGetLastError();
 }
 
 // Upper bound of the total row tiles: sum_g ceil(rows_g / 256) <= ceil(rows / 256) + G.
-hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+namespace {
+
+hipError_t launch_big_tiles(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.bwd_dhp) {  // the SwiGLU backward epilogue: plain rows in, bf16 gradients out
     if (!a.swiglu || a.out_f32 || a.w_kn || a.a_packed || a.out_packed || a.n_out % 32) return hipErrorInvalidValue;
     return launch_big<true, bf16_t, false, false, false, true>(a, rows_total_max, s);
@@ -730,18 +734,47 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a, int64_t rows_t
   return a.out_f32 ? launch_big<false, float>(a, rows_total_max, s) : launch_big<false>(a, rows_total_max, s);
 }
 
+}  // namespace
+
+// The 256-row tiles, then, when tails are on (a.tail, or big_tails() for -1), the groups'
+// last partial tiles of at most kBigTailRows rows on the streaming kernel: after the K-split
+// reduction, which writes every row.
+hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a0, int64_t rows_total_max, hipStream_t s) {
+  GroupedGemmArgs a = a0;
+  if (a.tail < 0) a.tail = big_tails(a.num_groups, a.n_out);
+  if (a.tail != 0 && a.tail != kBigTailRows) return hipErrorInvalidValue;
+  if (a.tail && ((a.a_packed && !a.tail_A) || (a.out_packed && !a.tail_out))) return hipErrorInvalidValue;
+  hipError_t e = launch_big_tiles(a, rows_total_max, s);
+  if (e != hipSuccess || !a.tail) return e;
+  GroupedGemmArgs t = a;
+  t.tails_only = true;
+  t.group_rows_max = std::min(a.group_rows_max, kBigTailRows);
+  t.split_ws = nullptr;
+  if (a.a_packed) {
+    t.A = a.tail_A;
+    t.row_index = a.tail_row_index;
+    t.a_rows = a.tail_a_rows;
+    t.a_packed = false;
+  }
+  if (a.out_packed) {
+    t.out = a.tail_out;
+    t.out_packed = false;
+  }
+  return launch_grouped_gemm_stream_bf16(t, s);
+}
+
 int64_t packed_rows_bytes(int64_t rows_max, int G, int K) {
   return ((rows_max + BG_BM - 1) / BG_BM + G) * BG_BM * (int64_t)K * 2;
 }
 
 hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int32_t *offsets, int G, int64_t rows_max,
-                            int K, void *out, hipStream_t s) {
+                            int K, void *out, hipStream_t s, int tail) {
   if (K % 32) return hipErrorInvalidValue;
   const int64_t grid = ((rows_max + BG_BM - 1) / BG_BM + G) * (K / 32);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(src), row_index,
-                     offsets, G, K, static_cast<bf16_t *>(out));
+                     offsets, G, K, static_cast<bf16_t *>(out), tail);
   return hipGetLastError();
 }
 
@@ -760,12 +793,12 @@ hipError_t launch_wgrad_big_kn(const void *AT, int64_t lda, const int32_t *poff,
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true, false, false, false, true>),
                        dim3((unsigned)grid), dim3(512), 0, s, static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff,
                        G, static_cast<const bf16_t *>(B), (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda,
-                       b_rows, M, nullptr, (int64_t)0, off_b, SwigluBwdOut{});
+                       b_rows, M, nullptr, (int64_t)0, off_b, SwigluBwdOut{}, 0);
   else
     hipLaunchKernelGGL((grouped_gemm_big_kernel<false, bf16_t, true, true>), dim3((unsigned)grid), dim3(512), 0, s,
                        static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, G, static_cast<const bf16_t *>(B),
                        (int64_t)0, N, 0, static_cast<bf16_t *>(out), n_tiles, lda, b_rows, M, nullptr, (int64_t)0,
-                       off_b, SwigluBwdOut{});
+                       off_b, SwigluBwdOut{}, 0);
   return hipGetLastError();
 }
 
@@ -794,7 +827,7 @@ hipError_t launch_wgrad_big_kn_f32(const void *AT, int64_t lda, const int32_t *p
   hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float, true, true>), dim3((unsigned)grid), dim3(512), 0, s,
                      static_cast<const bf16_t *>(AT), nullptr, (int64_t)0, poff, 1, static_cast<const bf16_t *>(B),
                      (int64_t)0, N, S, out, n_tiles, lda, b_rows, M, S > 1 ? part : nullptr, (int64_t)M * N, off_b,
-                     SwigluBwdOut{});
+                     SwigluBwdOut{}, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_ksplit_sum(part, S, (int64_t)M * N, out, s);

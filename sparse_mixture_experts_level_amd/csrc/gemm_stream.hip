@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
                                                                      const int32_t *__restrict__ offsets,
                                                                      const bf16_t *__restrict__ W, int64_t wstride,
                                                                      int n_out, int K, OutT *__restrict__ out,
-                                                                     int n_tiles, const SwigluBwdOut gb) {
+                                                                     int n_tiles, const SwigluBwdOut gb, int tail) {
   constexpr int NB = SWIGLU ? 2 * NSUB : NSUB;  // 16-row weight subtiles per wave
   constexpr int NT = 64 * NW;                     // threads
   constexpr int A_PER_T = (BM * 8 + NT - 1) / NT;  // 16-byte A pieces per thread and chunk
@@ -290,7 +290,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
 
   const int tile = blockIdx.x;
   const int g = tile / n_tiles, nt = tile - g * n_tiles;
-  const int row_begin = offsets[g], row_end = offsets[g + 1];
+  int row_begin = offsets[g];
+  const int row_end = offsets[g + 1];
+  if (tail > 0) {  // only the rows past the group's last full large tile, when at most `tail`
+    const int rem = (row_end - row_begin) % kBigTileRows;
+    if (rem > tail) return;
+    row_begin = row_end - rem;
+  }
   if (row_begin >= row_end) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -366,7 +372,7 @@ hipError_t launch_stream(const GroupedGemmArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((grouped_gemm_stream_kernel<BM, NSUB, SWIGLU, S, NW, OutT, WT, GB>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
                      static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets,
                      static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
-                     n_tiles, gb);
+                     n_tiles, gb, a.tails_only ? a.tail : 0);
   return hipGetLastError();
 }
 

@@ -93,7 +93,26 @@ struct GroupedGemmArgs {
   const float *bwd_row_gate = nullptr;
   void *bwd_hg = nullptr;
   float *bwd_dpart = nullptr;
+  // Tails, large-tile regime: with tail = kBigTailRows a group's last partial 256-row tile
+  // of at most that many rows is left to a streaming launch over the same groups
+  // (re-reading that group's weights then costs less than a nearly empty tile); 0: every
+  // row in large tiles; -1: chosen by the launch (big_tails()).  With a packed A or output
+  // the tail launch reads tail_A instead (row-major; rows through tail_row_index when
+  // given, tail_a_rows rows) and writes tail_out (row-major, rows in group order).
+  int tail = -1;
+  const void *tail_A = nullptr;
+  const int32_t *tail_row_index = nullptr;
+  int64_t tail_a_rows = 0;
+  void *tail_out = nullptr;
+  // Streaming kernel: compute only each group's tail rows (set by the large-tile launch).
+  bool tails_only = false;
 };
+
+// Large-tile row tiles and the tail rows left to the streaming kernel.
+constexpr int kBigTileRows = 256, kBigTailRows = 128;
+// The tail threshold for a large-tile launch over G groups with n_out output columns: the
+// streaming tail launch (one workgroup per group and 64 columns) must fill the GPU.
+inline int big_tails(int G, int n_out) { return (int64_t)G * ((n_out + 63) / 64) >= 512 ? kBigTailRows : 0; }
 
 // Device-side form of the SwiGLU backward outputs (kernel argument).
 struct SwigluBwdOut {
@@ -108,7 +127,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 // as the GEMM's LDS stage; rows gathered through row_index when given.
 int64_t packed_rows_bytes(int64_t rows_max, int G, int K);
 hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int32_t *offsets, int G, int64_t rows_max,
-                            int K, void *out, hipStream_t s);
+                            int K, void *out, hipStream_t s, int tail = 0);
 // Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group)
 // rather than the streaming one; either reads weights in both layouts (w_kn).
 bool grouped_gemm_big_regime(int64_t rows_max, int num_groups, int group_rows_max);
