@@ -196,6 +196,17 @@ def test_expert_parallel_shards_sum_to_the_layer(T, d, E, k, f, cf, fs, nshards)
     assert row_rel_err(to_np(total), to_np(full).astype(np.float64)) <= 2e-2
 
 
+def test_large_tile_tails_in_the_packed_forward():
+    """~300 rows per expert, d = f = 4096, 8 experts: both packed large-tile projections leave
+    their groups' last tiles of <= 128 rows to streaming launches (row-major x and H)."""
+    w = wl.Workload("tails", 2400, 4096, 8, 1, 4096, None, "bf16", offset="boost4")
+    say("packed forward with streamed tails T=2400 d=f=4096 E=8")
+    inp = wl.make_inputs(w, seed=5, device=DEV)
+    res = _run_and_check(inp, sample=np.arange(0, 2400, 29))
+    rows = np.diff(to_np(res["layer"].routing["expert_offsets"]).astype(np.int64))
+    assert np.any((rows % 256 > 0) & (rows % 256 <= 128)), rows  # some group has a streamed tail
+
+
 @pytest.mark.parametrize("T,d,E,k,f,cf", [
     (4096, 128, 8, 2, 64, 1.0),
     (4100, 256, 16, 4, 64, None),   # a ragged last workgroup of tokens

@@ -253,6 +253,9 @@ def test_grouped_gemm_bf16_wide():
     ([600, 0, 300, 1000], 256, 192),  # ragged row tiles, an empty group, a column tail (192 = 1.5 x 128)
     ([2000], 512, 384),
     ([257, 511, 1, 256], 320, 256),   # K = 320 (five 64-wide steps)
+    # eight groups x 4096 columns: gate_up leaves last tiles of <= 128 rows to a streaming
+    # launch (44, 88 and 8 rows; a 40-row group entirely), keeps 188- and 130-row ones
+    ([300, 600, 40, 520, 700, 256, 130, 0], 256, 4096),
 ])
 def test_grouped_gemm_bf16_large_groups(sizes, d, f):
     """Average group of >= 256 rows: the 256 x 256 MFMA tile kernel."""
