@@ -88,6 +88,9 @@ def _to_dev(inp):
     (64, 128, 256, 8, 64, 1.0, 64, "boost4"),  # T k = 512 and E = 256, the largest such batch, drops
     (1, 64, 8, 2, 64, None, 0, None),        # a single token
     (37, 192, 20, 3, 64, 0.5, 0, "boost4"),  # ragged tiles, drops
+    # top-1 without a shared expert
+    (300, 256, 16, 1, 192, 1.0, 0, "boost4"),
+    (37, 192, 20, 1, 64, 0.5, 0, "boost4"),
 ])
 def test_small_bf16_layers_all_tokens(T, d, E, k, f, cf, fs, offset):
     w = wl.Workload("small", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset=offset)
@@ -112,6 +115,14 @@ def test_zero_capacity_gives_zero_or_shared_output():
     desc0 = ops.make_desc(100, 128, 64, 8, 2, 0, 0, torch.bfloat16)
     ops.moe_forward(desc0, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, None, out,
                     ops.workspace(ops.moe_workspace_size(desc0)))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    # top-1 without a shared expert: every token dropped
+    w1 = wl.make_inputs(wl.Workload("zero_cap1", 100, 128, 8, 1, 64, None, "bf16"), seed=2, device=DEV)
+    desc1 = ops.make_desc(100, 128, 64, 8, 1, 0, 0, torch.bfloat16)
+    out.fill_(5.0)
+    ops.moe_forward(desc1, w1.w_router, w1.w_gate_up, w1.w_down, w1.x, None, out,
+                    ops.workspace(ops.moe_workspace_size(desc1)))
     torch.cuda.synchronize()
     assert torch.all(out == 0)
 
@@ -230,6 +241,7 @@ def test_fused_router_many_tokens(T, d, E, k, f, cf):
     (48, 128, 16, 2, 64, 0.5, "rank", "drop"),          # small batch
     (4100, 192, 12, 4, 64, 1.0, "token", "reroute"),    # router linear and top-k in one kernel
     (4096, 128, 64, 1, 64, 0.5, "rank", "reroute"),
+    (300, 256, 8, 1, 192, 0.75, "rank", "drop"),        # top-1, rank-major fill (the same order for k = 1)
 ])
 def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
     """moe_forward with the rank-major fill and/or redirection of overflow vs the oracle."""
@@ -263,7 +275,8 @@ def test_forward_dispatch_variants(T, d, E, k, f, cf, order, overflow):
     assert row_rel_err(to_np(layer.out), ref["out"]) <= 2e-2
 
 
-@pytest.mark.parametrize("T,d,E,k,f,cf,fs", [(300, 256, 8, 2, 192, 1.25, 64), (16, 256, 32, 4, 128, None, 0)])
+@pytest.mark.parametrize("T,d,E,k,f,cf,fs", [(300, 256, 8, 2, 192, 1.25, 64), (16, 256, 32, 4, 128, None, 0),
+                                              (300, 256, 16, 1, 192, 1.0, 0)])
 def test_forward_replays_from_a_captured_graph(T, d, E, k, f, cf, fs):
     """moe_forward allocates, synchronises and clears nothing on the host side, so a caller
     can capture it into a HIP graph: every replay (with eager work and synchronisation in
