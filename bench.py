@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward pass (moe_backward, routing from one forward) instead of the "
                         "forward")
+    p.add_argument("--tiled", choices=("auto", "on", "off"), default="auto",
+                   help="tile-major copies of the routed weights, prepared once before timing (auto: when the "
+                        "routed experts take the large-tile regime)")
     p.add_argument("--ep-shards", type=int, default=1, metavar="N",
                    help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
                         "contiguous ranges, every range timed on this GPU, the slowest one reported")
@@ -56,6 +59,10 @@ def source_hash(paths) -> str:
         with open(os.path.join(ROOT, p), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+WEIGHT_LAYOUT = {False: "row-major",
+                 True: "row-major plus tile-major copies of the routed weights, prepared once before timing"}
 
 
 def main():
@@ -75,8 +82,13 @@ def main():
     w = wl.get_workload(args.workload)
     inp = wl.make_inputs(w, seed=args.seed, device=dev)
     cap = ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor)
-    layer = ops.MoELayer(inp, cap, device=dev)
     T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
+    # The library's regime rule: groups averaging >= 256 rows (R_max / E) that can reach 256
+    # rows (min(T, C)) run on the large-tile kernel, which reads tile-major copies when given.
+    desc = ops.make_desc(T, d, f, E, k, cap, fs, w.torch_dtype)
+    large_tiles = ops.moe_max_rows(desc) // E >= 256 and (T if cap is None else min(T, cap)) >= 256
+    args.use_tiles = w.dtype == "bf16" and (args.tiled == "on" or (args.tiled == "auto" and large_tiles))
+    layer = ops.MoELayer(inp, cap, device=dev, tiled=args.use_tiles)
     s_bytes = 2 if w.dtype == "bf16" else 4
     if args.ep_shards > 1:
         return ep_share_bench(args, w, inp, cap, layer, s_bytes)
@@ -241,7 +253,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "num_tokens": T, "d_model": d,
                    "num_experts": E, "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap,
-                   "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R)},
+                   "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R),
+                   "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
         "roofline": roofline,
         "layer_roofline": layer_roofline,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
@@ -280,11 +293,15 @@ def ep_share_bench(args, w, inp, cap, layer, s_bytes):
     torch.cuda.synchronize()
     kept = np.diff(layer.routing["expert_offsets"].cpu().numpy().astype(np.int64))
 
+    # each rank's tile-major copies of its own experts, prepared once
+    tiles = [ops.tiled_weights(layer.desc, inp.w_gate_up[r * per:(r + 1) * per], inp.w_down[r * per:(r + 1) * per])
+             if args.use_tiles else None for r in range(N)]
+
     def share(r):
         b, e = r * per, (r + 1) * per
         ops.moe_forward_expert_shard(layer.desc, inp.w_router, inp.w_gate_up[b:e], inp.w_down[b:e], b, e, r == 0,
                                      inp.x, inp.logit_offset, part, layer.ws, w_shared_gate_up=inp.w_shared_gate_up,
-                                     w_shared_down=inp.w_shared_down)
+                                     w_shared_down=inp.w_shared_down, tiled=tiles[r])
 
     ranks = []
     for r in range(N):
@@ -321,7 +338,8 @@ def ep_share_bench(args, w, inp, cap, layer, s_bytes):
         "data": "synthetic",
         "config": {"workload": f"{w.name}, one rank's share of {N}-way expert parallelism (slowest rank)",
                    "num_tokens": T, "d_model": d, "num_experts": E, "top_k": w.top_k, "d_ff": f, "d_ff_shared": fs,
-                   "capacity": cap, "ep_shards": N, "experts_per_rank": per},
+                   "capacity": cap, "ep_shards": N, "experts_per_rank": per,
+                   "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
         "ranks": ranks,
         "roofline": None,
         "cpu_baseline": None,
@@ -359,7 +377,7 @@ def backward_bench(args, w, inp, cap, layer, s_bytes):
 
     def step():
         ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx, grads, ws,
-                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down)
+                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down, tiled=layer.tiled)
 
     for _ in range(args.warmup):
         step()
@@ -390,7 +408,7 @@ def backward_bench(args, w, inp, cap, layer, s_bytes):
         "data": "synthetic",
         "config": {"workload": f"{w.name}, backward pass", "num_tokens": T, "d_model": d, "num_experts": E,
                    "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap, "kept_rows": R,
-                   "experts_touched": E_t},
+                   "experts_touched": E_t, "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
         "layer_roofline": {"algorithmic_flop": flop, "algorithmic_bytes": nbytes, "roofline_ms": round(rt * 1e3, 4),
                            "frac_of_roofline": round(rt * 1e3 / ms, 4)},
         "roofline": None,

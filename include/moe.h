@@ -104,6 +104,15 @@ typedef struct moe_weights {
   const void *w_down;           /* [E, d, f] */
   const void *w_shared_gate_up; /* [2 f_s, d] or NULL when d_ff_shared == 0 */
   const void *w_shared_down;    /* [d, f_s]   or NULL when d_ff_shared == 0 */
+  /* Optional, bf16 only, both or neither: w_gate_up and w_down also in the tile-major
+   * layout that moe_tile_expert_weights writes (NULL: not given).  The large-tile regime of
+   * the routed experts' grouped GEMMs then reads these copies -- one contiguous 16 KB
+   * block per weight tile and K step instead of 256 rows of 64 bytes; w_gate_up and
+   * w_down stay required (the streaming kernel reads them).  The caller keeps the two
+   * forms equal.  Read by moe_forward, moe_forward_expert_shard (the range's experts) and
+   * moe_backward (the recomputed gate_up projection). */
+  const void *w_gate_up_tiled;
+  const void *w_down_tiled;
 } moe_weights;
 
 /* Optional routing outputs of moe_forward (device pointers; any may be NULL,
@@ -329,6 +338,28 @@ size_t moe_backward_workspace_size(const moe_desc *desc);
  * launches on `stream` (capturable into a HIP graph). */
 moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const void *x, const moe_routing *routing,
                         const void *dy, void *dx, moe_grads *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the tile-major copy of num_experts experts' gate_up (which = 0) or down
+ * (which = 1) weights for desc's shapes: per expert, ceil(f / 128) gate_up tiles (128 gate
+ * rows and their 128 up rows each) or ceil(d / 256) down tiles (256 rows each), times K/32
+ * steps (K = d for gate_up, f for down), times 16 KB.  0 for an invalid descriptor, a
+ * dtype other than bf16, num_experts < 1 or another `which`.  Host only. */
+size_t moe_tiled_weights_bytes(const moe_desc *desc, int32_t num_experts, int32_t which);
+
+/* Writes the tile-major copies of num_experts experts' routed weights: a one-time
+ * preparation of the runtime layout at weight-loading time ([HF-MoE] "Рефакторинг
+ * загрузки весов": checkpoint weights are converted once, on load, into the layout the
+ * runtime computes with).  Tile nt, K step kt of expert e is the 16 KB block
+ * (e * tiles + nt) * K/32 + kt: the tile's 256 weight rows by 32 values, 64 bytes per row,
+ * 16-byte chunk c of row r stored at chunk position c ^ ((r >> 2) & 3), rows past the
+ * matrix zero.  gate_up tile nt holds gate rows 128 nt .. 128 nt + 127 followed by the
+ * matching up rows (f apart); down tile nt holds rows 256 nt .. 256 nt + 255.  Inputs as in
+ * moe_weights ([num_experts, 2f, d] and [num_experts, d, f]); outputs sized by
+ * moe_tiled_weights_bytes, 16-byte aligned, not overlapping the inputs.  bf16 only
+ * (MOE_ERR_UNSUPPORTED otherwise).  Only kernel launches on `stream`. */
+moe_status moe_tile_expert_weights(const moe_desc *desc, int32_t num_experts, const void *w_gate_up,
+                                   const void *w_down, void *w_gate_up_tiled, void *w_down_tiled,
+                                   hipStream_t stream);
 
 /* One rank's share of expert parallelism ([HF-MoE] "Параллелизм экспертов
  * (Expert Parallelism)": each device holds a contiguous subset of the experts,

@@ -55,6 +55,16 @@ moe_status check_ptr(const void *p, const char *name) {
 
 moe_status check_opt_ptr(const void *p, const char *name) { return p ? check_ptr(p, name) : MOE_OK; }
 
+// The optional tile-major copies of the routed weights: both or neither, bf16 only.
+moe_status check_tiled(const moe_weights &w, int32_t dtype) {
+  if (!w.w_gate_up_tiled && !w.w_down_tiled) return MOE_OK;
+  if (!w.w_gate_up_tiled || !w.w_down_tiled)
+    return fail(MOE_ERR_INVALID, "w_gate_up_tiled and w_down_tiled: give both or neither");
+  if (dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tile-major weights are bf16 only");
+  MOE_TRY(check_ptr(w.w_gate_up_tiled, "w_gate_up_tiled"));
+  return check_ptr(w.w_down_tiled, "w_down_tiled");
+}
+
 size_t elem_bytes(int32_t dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
 moe_status check_dtype_dims(int32_t dtype, int64_t d, int64_t f, int64_t fs) {
@@ -215,7 +225,8 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
                            int64_t x_row_count = 0, float *split_ws = nullptr, void *x_packed = nullptr,
-                           void *hidden_tail = nullptr) {
+                           void *hidden_tail = nullptr, const void *w_gate_up_tiled = nullptr,
+                           const void *w_down_tiled = nullptr) {
   if (x_packed && hidden_tail && dtype == MOE_DTYPE_BF16 &&
       moe::grouped_gemm_big_regime(rows_max, G, group_rows_max)) {
     // Large-tile regime: the gathered rows of x are first copied into the packed tile
@@ -234,6 +245,7 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     gu.tail_row_index = row_index;
     gu.tail_a_rows = row_index ? x_row_count : rows_max;
     gu.tail_out = hidden_tail;
+    gu.W_packed = w_gate_up_tiled;
     MOE_TRY(run_projection(gu, dtype, s, "gate_up grouped GEMM"));
     moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows,
                                                 false, nullptr, hb);
@@ -242,6 +254,7 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     down.tail_A = hidden_tail;
     down.tail_a_rows = rows_max;
     down.split_ws = split_ws;
+    down.W_packed = w_down_tiled;
     MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
     return MOE_OK;
   }
@@ -520,6 +533,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
   if (any_local) {
     MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
     MOE_TRY(check_ptr(weights->w_down, "w_down"));
+    MOE_TRY(check_tiled(*weights, D.dtype));
   }
   MOE_TRY(check_opt_ptr(logit_offset, "logit_offset"));
   if (D.d_ff_shared > 0 && add_shared) {
@@ -595,7 +609,8 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
                             offsets + e_begin, weights->w_gate_up, weights->w_down, y_perm, at<void>(ws, L.hidden),
                             stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr,
                             packable(D) ? at<void>(ws, L.x_packed) : nullptr,
-                            packable(D) ? at<void>(ws, L.hidden_tail) : nullptr));
+                            packable(D) ? at<void>(ws, L.hidden_tail) : nullptr, weights->w_gate_up_tiled,
+                            weights->w_down_tiled));
   }
   const void *shared = nullptr;
   if (fs > 0 && add_shared) {
@@ -620,6 +635,35 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
   MOE_TRY(check_desc(desc));
   return forward_range(*desc, weights, x, logit_offset, out, routing, ws, ws_bytes, stream, 0, desc->num_experts,
                        true);
+}
+
+size_t moe_tiled_weights_bytes(const moe_desc *desc, int32_t num_experts, int32_t which) {
+  if (check_desc(desc) != MOE_OK || desc->dtype != MOE_DTYPE_BF16 || num_experts < 1 || (which != 0 && which != 1))
+    return 0;
+  const moe_desc &D = *desc;
+  return which == 0 ? (size_t)moe::packed_weights_bytes(num_experts, D.d_ff, D.d_model, true)
+                    : (size_t)moe::packed_weights_bytes(num_experts, D.d_model, D.d_ff, false);
+}
+
+moe_status moe_tile_expert_weights(const moe_desc *desc, int32_t num_experts, const void *w_gate_up,
+                                   const void *w_down, void *w_gate_up_tiled, void *w_down_tiled,
+                                   hipStream_t stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_desc &D = *desc;
+  if (D.dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "tile-major weights are bf16 only");
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID, "num_experts %d outside [1, %d]", num_experts, MOE_MAX_EXPERTS);
+  MOE_TRY(check_ptr(w_gate_up, "w_gate_up"));
+  MOE_TRY(check_ptr(w_down, "w_down"));
+  MOE_TRY(check_ptr(w_gate_up_tiled, "w_gate_up_tiled"));
+  MOE_TRY(check_ptr(w_down_tiled, "w_down_tiled"));
+  const int d = D.d_model, f = D.d_ff;
+  MOE_TRY_HIP(moe::launch_pack_weights(w_gate_up, num_experts, (int64_t)2 * f * d, f, d, true, w_gate_up_tiled,
+                                       stream),
+              "tile gate_up weights");
+  MOE_TRY_HIP(moe::launch_pack_weights(w_down, num_experts, (int64_t)d * f, d, f, false, w_down_tiled, stream),
+              "tile down weights");
+  return ok();
 }
 
 moe_status moe_forward_expert_shard(const moe_desc *desc, const moe_weights *weights, int32_t expert_begin,
@@ -762,6 +806,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
   MOE_TRY(check_ptr(weights->w_router, "w_router"));
   MOE_TRY(check_ptr(weights->w_gate_up, "w_gate_up"));
   MOE_TRY(check_ptr(weights->w_down, "w_down"));
+  MOE_TRY(check_tiled(*weights, D.dtype));
   MOE_TRY(check_ptr(routing->topk_ids, "routing.topk_ids"));
   MOE_TRY(check_ptr(routing->topk_gates, "routing.topk_gates"));
   MOE_TRY(check_ptr(routing->expert_offsets, "routing.expert_offsets"));
@@ -818,6 +863,7 @@ moe_status moe_backward(const moe_desc *desc, const moe_weights *weights, const 
     r.bwd_row_gate = at<float>(ws, L.row_gate);
     r.bwd_hg = W(L.hg);
     r.bwd_dpart = at<float>(ws, L.dpart);
+    r.W_packed = weights->w_gate_up_tiled;  // read by the large-tile regime
     MOE_TRY(gemm(r, "gate_up recompute + SwiGLU backward"));
     // dx rows = [dG dU] W_gu (W_gu [2f, d] per expert is K-major for this product)
     auto a = gemm_args(E, R, grb, W(L.dgu), nullptr, 0, offsets, weights->w_gate_up, (int64_t)2 * f * d, d, 2 * f,

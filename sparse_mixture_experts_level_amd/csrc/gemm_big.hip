@@ -94,9 +94,11 @@ __global__ __launch_bounds__(256) void big_split_reduce_kernel(const float *__re
 // activations, zero padded; lda bounds the buffer), and W [ldb rows, n_out] K-major (BKN;
 // rows past offsets_b[g+1] read zeros); every group M x n_out, written at out + g * M * n_out.
 // APK: A is in the packed tile layout (pack_rows_kernel); OPK: the SwiGLU output is
-// written in that layout, for a following large-tile GEMM over the same groups.
+// written in that layout, for a following large-tile GEMM over the same groups.  BPK: the
+// weights are in their packed tile layout (pack_weights_kernel; wstride is the packed
+// group's size in elements).
 template <bool SWIGLU, typename OutT = bf16_t, bool WG = false, bool BKN = false, bool APK = false, bool OPK = false,
-          bool GB = false, bool TO = false>
+          bool GB = false, bool TO = false, bool BPK = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *__restrict__ A,
                                                                          const int32_t *__restrict__ row_index,
                                                                          int64_t a_rows,
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   static_assert(!GB || (SWIGLU && !WG && !APK && !OPK && sizeof(OutT) == 2),
                 "SwiGLU backward: the forward form's gate and up blocks, bf16 gradients");
   static_assert(!TO || (WG && sizeof(OutT) == 2), "transposed output: the weight-gradient form, bf16");
+  static_assert(!BPK || (!WG && !BKN), "packed weights: the forward form's row-major weights");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
   auto bufA = [&](int b) -> uint8_t * { return b == 0 ? sA0 : b == 1 ? sA1 : b == 2 ? sA2 : sA3; };
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   // This lane's global offsets (k = 0) for its IPW instructions per operand.
   uint32_t agoff[IPW], bgoff[IPW];
   int krow[IPW];  // WG with K-major operands: this lane's k-row within a step, per instruction
-  int m0, rows, n0, nk, ks = 0, kbase = 0, kvalid = 0, m_tile = 0;
+  int m0, rows, n0, nk, ks = 0, kbase = 0, kvalid = 0, m_tile = 0, n_tile = 0;
   bool partial = false;
   rsrc_t ares, wres;
   OutT *obase;
@@ -189,6 +192,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     rows = min(BG_BM, row_end - m0);
     m_tile = mt_first + mt;  // rank of this row tile among all groups' row tiles
     n0 = nt * (SWIGLU ? BG_BN / 2 : BG_BN);  // first output column of the tile
+    n_tile = nt;
     const uint32_t kbytes = (uint32_t)K * 2u;
     // A rows: contiguous from m0, or gathered from the unpermuted activations by row_index
     if constexpr (APK)  // the tiles' K steps are 16 KB blocks, a_rows bounds the buffer in bytes
@@ -207,7 +211,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
         agoff[i] = r < rows ? (uint32_t)row_index[m0 + r] * kbytes + (uint32_t)c * 16u : kOob;
       else
         agoff[i] = (uint32_t)r * kbytes + (uint32_t)c * 16u;
-      if constexpr (BKN) {
+      if constexpr (BPK) {
+        // packed weights: a stage image, like the packed A
+        bgoff[i] = (uint32_t)blk * 1024u + (uint32_t)lane * 16u;
+      } else if constexpr (BKN) {
         // K-major weights [K, n_out]: instruction blk brings k-rows 2 blk and 2 blk + 1 of
         // the step, 512 bytes (256 columns) each; lane p of a row stores the row's chunk
         // p ^ (4 (row & 3)) at slot p
@@ -287,8 +294,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
   auto issue = [&](int kt, int b) {  // loads of step kt into stage b; steps past K read zeros
     const bool ok = kt < nk;
     const uint32_t kc = (uint32_t)(kbase + kt) * (BK * 2);
-    // K-major operands advance BK rows per step
-    const uint32_t kcb = BKN ? (uint32_t)(kbase + kt) * (uint32_t)BK * (uint32_t)n_out * 2u : kc;
+    // K-major operands advance BK rows per step; packed weights: block (n_tile, step)
+    const uint32_t kcb = BKN ? (uint32_t)(kbase + kt) * (uint32_t)BK * (uint32_t)n_out * 2u
+                       : BPK ? ((uint32_t)n_tile * (uint32_t)(K / BK) + (uint32_t)(kbase + kt)) * (uint32_t)TILE
+                             : kc;
     // packed A: block (m_tile, step) of the tile-major layout
     const uint32_t kca = APK ? ((uint32_t)m_tile * (uint32_t)(K / BK) + (uint32_t)(kbase + kt)) * (uint32_t)TILE : kc;
     uint8_t *la = bufA(b), *lb = bufB(b);
@@ -684,13 +693,52 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t *__restrict
   }
 }
 
+// Packed tile layout of grouped row-major weights ([n_rows, K] per group, group stride
+// wstride elements) for the forward form's B operand: for group g, weight tile nt and K
+// step kt, a 16 KB block at ((g * n_tiles + nt) * K / 32 + kt) * 16 KB holding the tile's
+// 256 weight rows x 32 values as the GEMM's LDS stage does (the layout of pack_rows).
+// The tile's rows are those the GEMM assigns it: with SwiGLU, gate rows nt * 128 .. + 127
+// then the matching up rows (n_out apart); otherwise rows nt * 256 .. + 255; rows past
+// n_out zero.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16_t *__restrict__ W, int64_t wstride, int n_out,
+                                                           int K, int n_tiles, int swiglu,
+                                                           bf16_t *__restrict__ out) {
+  const int steps = K / 32;
+  const int64_t b = blockIdx.x;
+  const int64_t gt = b / steps;
+  const int kt = (int)(b - gt * steps);
+  const int g = (int)(gt / n_tiles), nt = (int)(gt - (int64_t)g * n_tiles);
+  bf16_t *blk = out + b * (BG_BN * 32);
+  const bf16_t *wg = W + (size_t)g * wstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q >> 2, c = q & 3;
+    int wr;  // weight row held in tile row r, -1 past n_out
+    if (swiglu) {
+      const int col = nt * (BG_BN / 2) + (r & 127);
+      wr = col < n_out ? (r < 128 ? col : n_out + col) : -1;
+    } else {
+      wr = nt * BG_BN + r < n_out ? nt * BG_BN + r : -1;
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (wr >= 0) v = ldg16(wg + (int64_t)wr * K + kt * 32 + c * 8);
+    stg16(blk + r * 32 + ((c ^ ((r >> 2) & 3)) << 3), v);
+  }
+}
+
 }  // namespace
 
-template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false, bool APK = false, bool OPK = false, bool GB = false>
+template <bool SWIGLU, typename OutT = bf16_t, bool BKN = false, bool APK = false, bool OPK = false, bool GB = false,
+          bool BPK = false>
 hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
   if (a.n_out % 8) return hipErrorInvalidValue;  // the epilogue stores runs of 8 columns
   const int cols = SWIGLU ? BG_BN / 2 : BG_BN;
   const int n_tiles = (a.n_out + cols - 1) / cols;
+  // packed weights: the group stride of their layout
+  const void *W = BPK ? a.W_packed : a.W;
+  const int64_t wstride = BPK ? packed_weights_bytes(1, a.n_out, a.K, SWIGLU) / 2 : a.w_group_stride;
+  if (BPK && (a.K % 32 || wstride * 2 >= ((int64_t)1 << 32))) return hipErrorInvalidValue;
   const int64_t m_tiles = (rows_total_max + BG_BM - 1) / BG_BM + a.num_groups;
   // K splits only for a plain bf16 store with a workspace for the partials
   float *split = (!SWIGLU && sizeof(OutT) == 2 && a.split_ws && a.row_index == nullptr) ? a.split_ws : nullptr;
@@ -698,9 +746,9 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
                         a.bwd_dpart};
   const int64_t split_stride = rows_total_max * a.n_out;
   const int64_t grid = m_tiles * n_tiles * (split ? 4 : 1);
-  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK, GB>), dim3((unsigned)grid), dim3(512),
-                     0, s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
-                     static_cast<const bf16_t *>(a.W), a.w_group_stride, a.n_out, a.K, static_cast<OutT *>(a.out),
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<SWIGLU, OutT, false, BKN, APK, OPK, GB, false, BPK>), dim3((unsigned)grid),
+                     dim3(512), 0, s, static_cast<const bf16_t *>(a.A), a.row_index, a.a_rows, a.offsets, a.num_groups,
+                     static_cast<const bf16_t *>(W), wstride, a.n_out, a.K, static_cast<OutT *>(a.out),
                      n_tiles, (int64_t)0, (int64_t)0, 0, split, split_stride, nullptr, gb, a.tail);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
@@ -715,17 +763,25 @@ hipError_t launch_big(const GroupedGemmArgs &a, int64_t rows_total_max, hipStrea
 namespace {
 
 hipError_t launch_big_tiles(const GroupedGemmArgs &a, int64_t rows_total_max, hipStream_t s) {
+  const bool bp = a.W_packed != nullptr;
+  if (bp && a.w_kn) return hipErrorInvalidValue;  // packed weights: the row-major forward form
   if (a.bwd_dhp) {  // the SwiGLU backward epilogue: plain rows in, bf16 gradients out
     if (!a.swiglu || a.out_f32 || a.w_kn || a.a_packed || a.out_packed || a.n_out % 32) return hipErrorInvalidValue;
-    return launch_big<true, bf16_t, false, false, false, true>(a, rows_total_max, s);
+    return bp ? launch_big<true, bf16_t, false, false, false, true, true>(a, rows_total_max, s)
+              : launch_big<true, bf16_t, false, false, false, true>(a, rows_total_max, s);
   }
   if (a.a_packed || a.out_packed) {  // the packed tile layout (pack_rows): SwiGLU in, plain down
     if (a.w_kn || a.out_f32) return hipErrorInvalidValue;
-    if (a.swiglu) return a.a_packed ? launch_big<true, bf16_t, false, true, true>(a, rows_total_max, s)
-                                    : hipErrorInvalidValue;
-    return (a.a_packed && !a.out_packed) ? launch_big<false, bf16_t, false, true, false>(a, rows_total_max, s)
-                                         : hipErrorInvalidValue;
+    if (a.swiglu) {
+      if (!a.a_packed) return hipErrorInvalidValue;
+      return bp ? launch_big<true, bf16_t, false, true, true, false, true>(a, rows_total_max, s)
+                : launch_big<true, bf16_t, false, true, true>(a, rows_total_max, s);
+    }
+    if (!a.a_packed || a.out_packed) return hipErrorInvalidValue;
+    return bp ? launch_big<false, bf16_t, false, true, false, false, true>(a, rows_total_max, s)
+              : launch_big<false, bf16_t, false, true, false>(a, rows_total_max, s);
   }
+  if (bp) return hipErrorInvalidValue;  // packed weights: with the packed activations or the SwiGLU backward
   if (a.w_kn) {  // K-major weights: bf16 output, no SwiGLU
     if (a.swiglu || a.out_f32) return hipErrorInvalidValue;
     return launch_big<false, bf16_t, true>(a, rows_total_max, s);
@@ -761,6 +817,23 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a0, int64_t rows_
     t.out_packed = false;
   }
   return launch_grouped_gemm_stream_bf16(t, s);
+}
+
+int64_t packed_weights_bytes(int G, int n_out, int K, bool swiglu) {
+  const int cols = swiglu ? BG_BN / 2 : BG_BN;
+  return (int64_t)G * ((n_out + cols - 1) / cols) * (K / 32) * (BG_BN * 32 * 2);
+}
+
+hipError_t launch_pack_weights(const void *W, int G, int64_t wstride, int n_out, int K, bool swiglu, void *out,
+                               hipStream_t s) {
+  if (K % 32 || n_out < 1 || G < 1) return hipErrorInvalidValue;
+  const int cols = swiglu ? BG_BN / 2 : BG_BN;
+  const int n_tiles = (n_out + cols - 1) / cols;
+  const int64_t grid = (int64_t)G * n_tiles * (K / 32);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t *>(W), wstride,
+                     n_out, K, n_tiles, swiglu ? 1 : 0, static_cast<bf16_t *>(out));
+  return hipGetLastError();
 }
 
 int64_t packed_rows_bytes(int64_t rows_max, int G, int K) {

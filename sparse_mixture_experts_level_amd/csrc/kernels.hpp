@@ -106,6 +106,10 @@ struct GroupedGemmArgs {
   void *tail_out = nullptr;
   // Streaming kernel: compute only each group's tail rows (set by the large-tile launch).
   bool tails_only = false;
+  // The same weights in the packed tile layout (launch_pack_weights), or NULL: the
+  // large-tile kernel then reads them with the packed activations or the SwiGLU backward
+  // epilogue; the streaming kernel (tails included) reads W.
+  const void *W_packed = nullptr;
 };
 
 // Large-tile row tiles and the tail rows left to the streaming kernel.
@@ -126,6 +130,13 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemmArgs &a, hipStream_t s);
 // of a group (numbered over all groups in order) and 32-wide K step, a 16 KB block laid out
 // as the GEMM's LDS stage; rows gathered through row_index when given.
 int64_t packed_rows_bytes(int64_t rows_max, int G, int K);
+// Packed tile layout of G groups' row-major weights ([rows, K] each, group stride wstride
+// elements) for the large-tile kernel's B operand: per group, weight tile (256 rows: with
+// SwiGLU 128 gate rows and the matching up rows, n_out apart) and 32-wide K step, one 16 KB
+// block laid out as the kernel's LDS stage; rows past n_out zero.  K a multiple of 32.
+int64_t packed_weights_bytes(int G, int n_out, int K, bool swiglu);
+hipError_t launch_pack_weights(const void *W, int G, int64_t wstride, int n_out, int K, bool swiglu, void *out,
+                               hipStream_t s);
 hipError_t launch_pack_rows(const void *src, const int32_t *row_index, const int32_t *offsets, int G, int64_t rows_max,
                             int K, void *out, hipStream_t s, int tail = 0);
 // Whether launch_grouped_gemm_bf16 takes the large-tile kernel (many rows per group)

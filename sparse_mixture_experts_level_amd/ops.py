@@ -30,7 +30,7 @@ SYMBOLS = [
     "moe_status_string", "moe_last_error", "moe_router_logits", "moe_router_topk",
     "moe_dispatch_permute", "moe_dispatch_reroute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
     "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
-    "moe_backward_workspace_size", "moe_backward",
+    "moe_backward_workspace_size", "moe_backward", "moe_tiled_weights_bytes", "moe_tile_expert_weights",
 ]
 
 
@@ -49,7 +49,8 @@ class MoeDesc(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("w_shared_gate_up", ctypes.c_void_p), ("w_shared_down", ctypes.c_void_p)]
+                ("w_shared_gate_up", ctypes.c_void_p), ("w_shared_down", ctypes.c_void_p),
+                ("w_gate_up_tiled", ctypes.c_void_p), ("w_down_tiled", ctypes.c_void_p)]
 
 
 class MoeGrads(ctypes.Structure):
@@ -108,6 +109,9 @@ def lib() -> ctypes.CDLL:
     L.moe_backward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, ctypes.POINTER(MoeRouting), vp, vp,
                                ctypes.POINTER(MoeGrads), vp, sz, vp]
     L.moe_backward.restype = st
+    L.moe_tiled_weights_bytes.argtypes, L.moe_tiled_weights_bytes.restype = [dp, i32, i32], sz
+    L.moe_tile_expert_weights.argtypes = [dp, i32, vp, vp, vp, vp, vp]
+    L.moe_tile_expert_weights.restype = st
     _lib = L
     return L
 
@@ -253,9 +257,37 @@ def moe_router_aux_loss(desc, logits, expert_counts, alpha, loss, ws, stream=Non
            "moe_router_aux_loss")
 
 
+def moe_tiled_weights_bytes(desc, num_experts: int, which: int) -> int:
+    return int(lib().moe_tiled_weights_bytes(ctypes.byref(desc), int(num_experts), int(which)))
+
+
+def moe_tile_expert_weights(desc, num_experts, w_gate_up, w_down, w_gate_up_tiled, w_down_tiled,
+                            stream=None) -> None:
+    _check(lib().moe_tile_expert_weights(ctypes.byref(desc), int(num_experts), _ptr(w_gate_up), _ptr(w_down),
+                                         _ptr(w_gate_up_tiled), _ptr(w_down_tiled), _stream(stream)),
+           "moe_tile_expert_weights")
+
+
+def tiled_weights(desc, w_gate_up, w_down, stream=None):
+    """The tile-major copies of w_gate_up [n, 2f, d] and w_down [n, d, f] (bf16, n experts),
+    allocated here as uint8 tensors and written by moe_tile_expert_weights."""
+    n = w_gate_up.shape[0]
+    gu = torch.empty(moe_tiled_weights_bytes(desc, n, 0), dtype=torch.uint8, device=w_gate_up.device)
+    dn = torch.empty(moe_tiled_weights_bytes(desc, n, 1), dtype=torch.uint8, device=w_down.device)
+    moe_tile_expert_weights(desc, n, w_gate_up, w_down, gu, dn, stream=stream)
+    return gu, dn
+
+
+def _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled):
+    gu_t, dn_t = tiled if tiled is not None else (None, None)
+    return MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down),
+                      _ptr(gu_t), _ptr(dn_t))
+
+
 def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, routing: Optional[dict] = None,
-                w_shared_gate_up=None, w_shared_down=None, stream=None) -> None:
-    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down))
+                w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None) -> None:
+    """tiled: optional (w_gate_up_tiled, w_down_tiled) from tiled_weights()."""
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled)
     R = None
     if routing is not None:
         R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
@@ -266,9 +298,8 @@ def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, rou
 
 def moe_forward_expert_shard(desc, w_router, w_gate_up_local, w_down_local, expert_begin, expert_end, add_shared, x,
                              logit_offset, out_partial, ws, routing: Optional[dict] = None, w_shared_gate_up=None,
-                             w_shared_down=None, stream=None) -> None:
-    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up_local), _ptr(w_down_local), _ptr(w_shared_gate_up),
-                   _ptr(w_shared_down))
+                             w_shared_down=None, stream=None, tiled=None) -> None:
+    W = _weights(w_router, w_gate_up_local, w_down_local, w_shared_gate_up, w_shared_down, tiled)
     R = None
     if routing is not None:
         R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
@@ -284,8 +315,8 @@ def moe_backward_workspace_size(desc: MoeDesc) -> int:
 
 
 def moe_backward(desc, w_router, w_gate_up, w_down, x, routing: dict, dy, dx, grads: dict, ws,
-                 w_shared_gate_up=None, w_shared_down=None, stream=None) -> None:
-    W = MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down))
+                 w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None) -> None:
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled)
     R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
     G = MoeGrads(*(_ptr(grads.get(n)) for n, _ in MoeGrads._fields_))
     _check(lib().moe_backward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), ctypes.byref(R), _ptr(dy), _ptr(dx),
@@ -299,7 +330,7 @@ class MoELayer:
 
     Convenience only: allocation happens here, once, never inside a forward call."""
 
-    def __init__(self, inputs, capacity, device="cuda", fill_order="token", overflow="drop"):
+    def __init__(self, inputs, capacity, device="cuda", fill_order="token", overflow="drop", tiled=False):
         w = inputs.workload
         self.inputs = inputs
         self.desc = make_desc(w.num_tokens, w.d_model, w.d_ff, w.num_experts, w.top_k, capacity,
@@ -319,10 +350,12 @@ class MoELayer:
             "row_token": torch.empty((max(R, 1),), **i32),
             "assigned_ids": torch.empty((T, k), **i32),
         }
+        # the routed weights' tile-major copies, prepared once (bf16)
+        self.tiled = tiled_weights(self.desc, inputs.w_gate_up, inputs.w_down) if tiled else None
 
     def forward(self, with_routing=True, stream=None):
         i = self.inputs
         moe_forward(self.desc, i.w_router, i.w_gate_up, i.w_down, i.x, i.logit_offset, self.out, self.ws,
                     routing=self.routing if with_routing else None, w_shared_gate_up=i.w_shared_gate_up,
-                    w_shared_down=i.w_shared_down, stream=stream)
+                    w_shared_down=i.w_shared_down, stream=stream, tiled=self.tiled)
         return self.out

@@ -156,3 +156,37 @@ def test_dispatch_variants_are_checked():
     assert st == ops.MOE_ERR_WORKSPACE
     # the redirection tables enlarge the layer's workspace
     assert ops.moe_workspace_size(d) > ops.moe_workspace_size(_desc())
+
+
+def test_tiled_weights_sizes_and_argument_checks():
+    """moe_tiled_weights_bytes is the tile count times 16 KB; moe_tile_expert_weights and the
+    calls that read tile-major weights reject bad arguments on the host."""
+    d = _desc(d_model=4096, d_ff=14336, num_experts=8, top_k=2, dtype=ops.MOE_DTYPE_BF16)
+    # gate_up: ceil(f / 128) tiles of 128 gate + 128 up rows, d / 32 steps; down: ceil(d / 256), f / 32
+    assert ops.moe_tiled_weights_bytes(d, 8, 0) == 8 * (14336 // 128) * (4096 // 32) * 16384
+    assert ops.moe_tiled_weights_bytes(d, 1, 1) == (4096 // 256) * (14336 // 32) * 16384
+    # for these shapes (2f a multiple of 256, d a multiple of 256) the copies are the size of the weights
+    assert ops.moe_tiled_weights_bytes(d, 8, 0) == 8 * 2 * 14336 * 4096 * 2
+    assert ops.moe_tiled_weights_bytes(d, 8, 1) == 8 * 4096 * 14336 * 2
+    d2 = _desc(d_model=192, d_ff=320, num_experts=4, top_k=1, dtype=ops.MOE_DTYPE_BF16)  # ragged tiles
+    assert ops.moe_tiled_weights_bytes(d2, 4, 0) == 4 * 3 * (192 // 32) * 16384
+    assert ops.moe_tiled_weights_bytes(d2, 4, 1) == 4 * 1 * (320 // 32) * 16384
+    assert ops.moe_tiled_weights_bytes(d2, 0, 0) == 0
+    assert ops.moe_tiled_weights_bytes(d2, 4, 2) == 0
+    assert ops.moe_tiled_weights_bytes(_desc(), 4, 0) == 0  # fp32
+    st = L.moe_tile_expert_weights(ctypes.byref(_desc()), 8, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == ops.MOE_ERR_UNSUPPORTED
+    st = L.moe_tile_expert_weights(ctypes.byref(d), 8, FAKE, FAKE, None, FAKE, None)
+    assert st == ops.MOE_ERR_INVALID and b"w_gate_up_tiled" in L.moe_last_error()
+    st = L.moe_tile_expert_weights(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == ops.MOE_ERR_INVALID
+    # one tile-major matrix without the other
+    W = ops.MoeWeights(FAKE, FAKE, FAKE, None, None, FAKE, None)
+    st = L.moe_forward(ctypes.byref(d), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
+    assert st == ops.MOE_ERR_INVALID and b"both or neither" in L.moe_last_error()
+    W = ops.MoeWeights(FAKE, FAKE, FAKE, None, None, FAKE + 4, FAKE)
+    st = L.moe_forward(ctypes.byref(d), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
+    assert st == ops.MOE_ERR_INVALID and b"aligned" in L.moe_last_error()
+    W = ops.MoeWeights(FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+    st = L.moe_forward(ctypes.byref(_desc()), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
+    assert st == ops.MOE_ERR_UNSUPPORTED  # fp32 layer

@@ -119,6 +119,22 @@ def test_backward_is_deterministic():
         assert torch.equal(grads[n], grads2[n]), n
 
 
+def test_backward_with_tile_major_weights():
+    """~512 rows per expert (large tiles): the gate_up recompute reading the tile-major copy
+    gives the same gradients, bit for bit."""
+    w = wl.Workload("bwd-tiled", 1024, 768, 4, 2, 256, None, "bf16", offset="boost4")
+    say("backward with tile-major weights")
+    inp, cap, layer, dy, dx, grads, ws = _run(w)
+    dx2 = torch.empty_like(dx)
+    grads2 = {n: torch.empty_like(v) for n, v in grads.items()}
+    ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx2, grads2, ws,
+                     tiled=ops.tiled_weights(layer.desc, inp.w_gate_up, inp.w_down))
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    for n in grads:
+        assert torch.equal(grads[n], grads2[n]), n
+
+
 def test_backward_replays_from_a_captured_graph():
     """moe_backward captured into a HIP graph: every replay equals the eager gradients bit
     for bit (the library clears its buffers with kernels, never with memsets)."""

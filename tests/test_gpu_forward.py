@@ -218,6 +218,54 @@ def test_large_tile_tails_in_the_packed_forward():
     assert np.any((rows % 256 > 0) & (rows % 256 <= 128)), rows  # some group has a streamed tail
 
 
+@pytest.mark.parametrize("T,d,E,k,f", [
+    (2400, 4096, 8, 1, 4096),  # both packed projections, with streamed tails
+    (2048, 320, 4, 2, 704),    # ragged weight tiles: 5.5 gate_up tiles of 128, 1.25 down tiles of 256
+])
+def test_tile_major_weights_give_the_same_forward(T, d, E, k, f):
+    """The large-tile regime reading the routed weights' tile-major copies computes exactly
+    what it computes from the row-major weights (same products, same order); the oracle
+    agrees on a sample."""
+    w = wl.Workload("tiled", T, d, E, k, f, None, "bf16", offset="boost4")
+    say(f"tile-major weights T={T} d={d} E={E} k={k} f={f}")
+    inp = wl.make_inputs(w, seed=6, device=DEV)
+    cap = ops.moe_capacity(T, E, None)
+    plain = ops.MoELayer(inp, cap)
+    plain.forward()
+    tiled = ops.MoELayer(inp, cap, tiled=True)
+    tiled.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(plain.out.view(torch.int16), tiled.out.view(torch.int16))
+    x = to_np(inp.x).astype(np.float64)
+    sample = np.arange(0, T, 41)
+    ref = oracle.moe_forward(x, to_np(inp.w_router).astype(np.float64), HostExperts(inp.w_gate_up),
+                             HostExperts(inp.w_down), k, cap, to_np(inp.logit_offset), tokens=sample,
+                             ids=to_np(tiled.routing["topk_ids"]).astype(np.int64))
+    assert row_rel_err(to_np(tiled.out)[sample], ref["out"]) <= tol_for(w.torch_dtype)
+
+
+def test_tile_major_weights_in_expert_shards():
+    """One large expert per rank (the down projection cut along K): each rank's partial from
+    its experts' tile-major copies equals the partial from the row-major weights."""
+    T, d, E, k, f, nshards = 1024, 256, 8, 2, 8192, 8
+    w = wl.Workload("tiled-ep", T, d, E, k, f, None, "bf16", offset="boost4")
+    say("tile-major weights, expert shards")
+    inp = wl.make_inputs(w, seed=7, device=DEV)
+    desc = ops.make_desc(T, d, f, E, k, ops.moe_capacity(T, E, None), 0, torch.bfloat16)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    per = E // nshards
+    for r in range(nshards):
+        b, e = r * per, (r + 1) * per
+        gu, dn = inp.w_gate_up[b:e].contiguous(), inp.w_down[b:e].contiguous()
+        want = torch.empty_like(inp.x)
+        got = torch.empty_like(inp.x)
+        ops.moe_forward_expert_shard(desc, inp.w_router, gu, dn, b, e, True, inp.x, inp.logit_offset, want, ws)
+        ops.moe_forward_expert_shard(desc, inp.w_router, gu, dn, b, e, True, inp.x, inp.logit_offset, got, ws,
+                                     tiled=ops.tiled_weights(desc, gu, dn))
+        torch.cuda.synchronize()
+        assert torch.equal(want.view(torch.int16), got.view(torch.int16)), r
+
+
 @pytest.mark.parametrize("T,d,E,k,f,cf", [
     (4096, 128, 8, 2, 64, 1.0),
     (4100, 256, 16, 4, 64, None),   # a ragged last workgroup of tokens
