@@ -45,8 +45,8 @@ def parse():
                    help="time the layer's backward pass (moe_backward, routing from one forward) instead of the "
                         "forward")
     p.add_argument("--tiled", choices=("auto", "on", "off"), default="auto",
-                   help="tile-major copies of the routed weights, prepared once before timing (auto: when the "
-                        "routed experts take the large-tile regime)")
+                   help="tile-major copies of the routed (shared) expert weights, prepared once before timing "
+                        "(auto: when the routed experts (the shared expert) take the large-tile regime)")
     p.add_argument("--ep-shards", type=int, default=1, metavar="N",
                    help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
                         "contiguous ranges, every range timed on this GPU, the slowest one reported")
@@ -61,8 +61,11 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-WEIGHT_LAYOUT = {False: "row-major",
-                 True: "row-major plus tile-major copies of the routed weights, prepared once before timing"}
+def weight_layout(args):
+    which = [n for n, on in (("routed", args.use_tiles), ("shared", args.use_shared_tiles)) if on]
+    if not which:
+        return "row-major"
+    return f"row-major plus tile-major copies of the {' and '.join(which)} expert weights, prepared once before timing"
 
 
 def main():
@@ -88,7 +91,9 @@ def main():
     desc = ops.make_desc(T, d, f, E, k, cap, fs, w.torch_dtype)
     large_tiles = ops.moe_max_rows(desc) // E >= 256 and (T if cap is None else min(T, cap)) >= 256
     args.use_tiles = w.dtype == "bf16" and (args.tiled == "on" or (args.tiled == "auto" and large_tiles))
-    layer = ops.MoELayer(inp, cap, device=dev, tiled=args.use_tiles)
+    # the shared expert, one group of all T tokens, takes the large-tile regime from 256 tokens
+    args.use_shared_tiles = w.dtype == "bf16" and fs > 0 and (args.tiled == "on" or (args.tiled == "auto" and T >= 256))
+    layer = ops.MoELayer(inp, cap, device=dev, tiled=args.use_tiles, shared_tiled=args.use_shared_tiles)
     s_bytes = 2 if w.dtype == "bf16" else 4
     if args.ep_shards > 1:
         return ep_share_bench(args, w, inp, cap, layer, s_bytes)
@@ -254,7 +259,7 @@ def main():
         "config": {"workload": w.name, "description": w.description, "num_tokens": T, "d_model": d,
                    "num_experts": E, "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap,
                    "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R),
-                   "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
+                   "weight_layout": weight_layout(args)},
         "roofline": roofline,
         "layer_roofline": layer_roofline,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
@@ -301,7 +306,8 @@ def ep_share_bench(args, w, inp, cap, layer, s_bytes):
         b, e = r * per, (r + 1) * per
         ops.moe_forward_expert_shard(layer.desc, inp.w_router, inp.w_gate_up[b:e], inp.w_down[b:e], b, e, r == 0,
                                      inp.x, inp.logit_offset, part, layer.ws, w_shared_gate_up=inp.w_shared_gate_up,
-                                     w_shared_down=inp.w_shared_down, tiled=tiles[r])
+                                     w_shared_down=inp.w_shared_down, tiled=tiles[r],
+                                     shared_tiled=layer.shared_tiled if r == 0 else None)
 
     ranks = []
     for r in range(N):
@@ -339,7 +345,7 @@ def ep_share_bench(args, w, inp, cap, layer, s_bytes):
         "config": {"workload": f"{w.name}, one rank's share of {N}-way expert parallelism (slowest rank)",
                    "num_tokens": T, "d_model": d, "num_experts": E, "top_k": w.top_k, "d_ff": f, "d_ff_shared": fs,
                    "capacity": cap, "ep_shards": N, "experts_per_rank": per,
-                   "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
+                   "weight_layout": weight_layout(args)},
         "ranks": ranks,
         "roofline": None,
         "cpu_baseline": None,
@@ -377,7 +383,8 @@ def backward_bench(args, w, inp, cap, layer, s_bytes):
 
     def step():
         ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx, grads, ws,
-                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down, tiled=layer.tiled)
+                         w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down, tiled=layer.tiled,
+                         shared_tiled=layer.shared_tiled)
 
     for _ in range(args.warmup):
         step()
@@ -408,7 +415,7 @@ def backward_bench(args, w, inp, cap, layer, s_bytes):
         "data": "synthetic",
         "config": {"workload": f"{w.name}, backward pass", "num_tokens": T, "d_model": d, "num_experts": E,
                    "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap, "kept_rows": R,
-                   "experts_touched": E_t, "weight_layout": WEIGHT_LAYOUT[args.use_tiles]},
+                   "experts_touched": E_t, "weight_layout": weight_layout(args)},
         "layer_roofline": {"algorithmic_flop": flop, "algorithmic_bytes": nbytes, "roofline_ms": round(rt * 1e3, 4),
                            "frac_of_roofline": round(rt * 1e3 / ms, 4)},
         "roofline": None,

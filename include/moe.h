@@ -113,6 +113,12 @@ typedef struct moe_weights {
    * moe_backward (the recomputed gate_up projection). */
   const void *w_gate_up_tiled;
   const void *w_down_tiled;
+  /* Optional, bf16 only, both or neither: the shared expert's weights in the same tile-major
+   * layout (moe_tile_expert_weights with a descriptor of one expert, d_ff = d_ff_shared,
+   * top_k = 1).  Read by moe_forward, moe_forward_expert_shard (with add_shared) and
+   * moe_backward when the shared expert takes the large-tile regime (T >= 256). */
+  const void *w_shared_gate_up_tiled;
+  const void *w_shared_down_tiled;
 } moe_weights;
 
 /* Optional routing outputs of moe_forward (device pointers; any may be NULL,

@@ -773,7 +773,10 @@ hipError_t launch_big_tiles(const GroupedGemmArgs &a, int64_t rows_total_max, hi
   if (a.a_packed || a.out_packed) {  // the packed tile layout (pack_rows): SwiGLU in, plain down
     if (a.w_kn || a.out_f32) return hipErrorInvalidValue;
     if (a.swiglu) {
-      if (!a.a_packed) return hipErrorInvalidValue;
+      if (!a.out_packed) return hipErrorInvalidValue;
+      if (!a.a_packed)  // row-major (or gathered) A, packed H
+        return bp ? launch_big<true, bf16_t, false, false, true, false, true>(a, rows_total_max, s)
+                  : launch_big<true, bf16_t, false, false, true>(a, rows_total_max, s);
       return bp ? launch_big<true, bf16_t, false, true, true, false, true>(a, rows_total_max, s)
                 : launch_big<true, bf16_t, false, true, true>(a, rows_total_max, s);
     }

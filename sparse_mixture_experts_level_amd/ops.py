@@ -50,7 +50,8 @@ class MoeDesc(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("w_shared_gate_up", ctypes.c_void_p), ("w_shared_down", ctypes.c_void_p),
-                ("w_gate_up_tiled", ctypes.c_void_p), ("w_down_tiled", ctypes.c_void_p)]
+                ("w_gate_up_tiled", ctypes.c_void_p), ("w_down_tiled", ctypes.c_void_p),
+                ("w_shared_gate_up_tiled", ctypes.c_void_p), ("w_shared_down_tiled", ctypes.c_void_p)]
 
 
 class MoeGrads(ctypes.Structure):
@@ -278,16 +279,25 @@ def tiled_weights(desc, w_gate_up, w_down, stream=None):
     return gu, dn
 
 
-def _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled):
+def tiled_shared_weights(desc, w_shared_gate_up, w_shared_down, stream=None):
+    """The tile-major copies of the shared expert's [2 f_s, d] and [d, f_s] weights: one expert
+    of width d_ff_shared."""
+    one = MoeDesc(**{n: getattr(desc, n) for n, _ in MoeDesc._fields_})
+    one.num_experts, one.top_k, one.d_ff, one.d_ff_shared, one.capacity = 1, 1, desc.d_ff_shared, 0, MOE_NO_CAPACITY
+    return tiled_weights(one, w_shared_gate_up.unsqueeze(0), w_shared_down.unsqueeze(0), stream=stream)
+
+
+def _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled, shared_tiled=None):
     gu_t, dn_t = tiled if tiled is not None else (None, None)
+    sgu_t, sdn_t = shared_tiled if shared_tiled is not None else (None, None)
     return MoeWeights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(w_shared_gate_up), _ptr(w_shared_down),
-                      _ptr(gu_t), _ptr(dn_t))
+                      _ptr(gu_t), _ptr(dn_t), _ptr(sgu_t), _ptr(sdn_t))
 
 
 def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, routing: Optional[dict] = None,
-                w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None) -> None:
-    """tiled: optional (w_gate_up_tiled, w_down_tiled) from tiled_weights()."""
-    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled)
+                w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None, shared_tiled=None) -> None:
+    """tiled / shared_tiled: optional tile-major copies from tiled_weights() / tiled_shared_weights()."""
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled, shared_tiled)
     R = None
     if routing is not None:
         R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
@@ -298,8 +308,8 @@ def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, rou
 
 def moe_forward_expert_shard(desc, w_router, w_gate_up_local, w_down_local, expert_begin, expert_end, add_shared, x,
                              logit_offset, out_partial, ws, routing: Optional[dict] = None, w_shared_gate_up=None,
-                             w_shared_down=None, stream=None, tiled=None) -> None:
-    W = _weights(w_router, w_gate_up_local, w_down_local, w_shared_gate_up, w_shared_down, tiled)
+                             w_shared_down=None, stream=None, tiled=None, shared_tiled=None) -> None:
+    W = _weights(w_router, w_gate_up_local, w_down_local, w_shared_gate_up, w_shared_down, tiled, shared_tiled)
     R = None
     if routing is not None:
         R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
@@ -315,8 +325,8 @@ def moe_backward_workspace_size(desc: MoeDesc) -> int:
 
 
 def moe_backward(desc, w_router, w_gate_up, w_down, x, routing: dict, dy, dx, grads: dict, ws,
-                 w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None) -> None:
-    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled)
+                 w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None, shared_tiled=None) -> None:
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled, shared_tiled)
     R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
     G = MoeGrads(*(_ptr(grads.get(n)) for n, _ in MoeGrads._fields_))
     _check(lib().moe_backward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), ctypes.byref(R), _ptr(dy), _ptr(dx),
@@ -330,7 +340,8 @@ class MoELayer:
 
     Convenience only: allocation happens here, once, never inside a forward call."""
 
-    def __init__(self, inputs, capacity, device="cuda", fill_order="token", overflow="drop", tiled=False):
+    def __init__(self, inputs, capacity, device="cuda", fill_order="token", overflow="drop", tiled=False,
+                 shared_tiled=False):
         w = inputs.workload
         self.inputs = inputs
         self.desc = make_desc(w.num_tokens, w.d_model, w.d_ff, w.num_experts, w.top_k, capacity,
@@ -352,10 +363,12 @@ class MoELayer:
         }
         # the routed weights' tile-major copies, prepared once (bf16)
         self.tiled = tiled_weights(self.desc, inputs.w_gate_up, inputs.w_down) if tiled else None
+        self.shared_tiled = (tiled_shared_weights(self.desc, inputs.w_shared_gate_up, inputs.w_shared_down)
+                             if shared_tiled and w.d_ff_shared else None)
 
     def forward(self, with_routing=True, stream=None):
         i = self.inputs
         moe_forward(self.desc, i.w_router, i.w_gate_up, i.w_down, i.x, i.logit_offset, self.out, self.ws,
                     routing=self.routing if with_routing else None, w_shared_gate_up=i.w_shared_gate_up,
-                    w_shared_down=i.w_shared_down, stream=stream, tiled=self.tiled)
+                    w_shared_down=i.w_shared_down, stream=stream, tiled=self.tiled, shared_tiled=self.shared_tiled)
         return self.out

@@ -190,3 +190,7 @@ def test_tiled_weights_sizes_and_argument_checks():
     W = ops.MoeWeights(FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
     st = L.moe_forward(ctypes.byref(_desc()), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
     assert st == ops.MOE_ERR_UNSUPPORTED  # fp32 layer
+    ds = _desc(d_model=4096, d_ff=14336, num_experts=8, top_k=2, d_ff_shared=1024, dtype=ops.MOE_DTYPE_BF16)
+    W = ops.MoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE)
+    st = L.moe_forward(ctypes.byref(ds), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
+    assert st == ops.MOE_ERR_INVALID and b"w_shared_gate_up_tiled" in L.moe_last_error()

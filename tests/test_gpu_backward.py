@@ -135,6 +135,23 @@ def test_backward_with_tile_major_weights():
         assert torch.equal(grads[n], grads2[n]), n
 
 
+def test_backward_with_tile_major_shared_weights():
+    """400 tokens: the shared expert's recompute takes the large-tile regime; reading its
+    weights' tile-major copy gives the same gradients, bit for bit."""
+    w = wl.Workload("bwd-tiled-shared", 400, 128, 16, 2, 128, 1.25, "bf16", d_ff_shared=320, offset="boost4")
+    say("backward with tile-major shared weights")
+    inp, cap, layer, dy, dx, grads, ws = _run(w)
+    dx2 = torch.empty_like(dx)
+    grads2 = {n: torch.empty_like(v) for n, v in grads.items()}
+    ops.moe_backward(layer.desc, inp.w_router, inp.w_gate_up, inp.w_down, inp.x, layer.routing, dy, dx2, grads2, ws,
+                     w_shared_gate_up=inp.w_shared_gate_up, w_shared_down=inp.w_shared_down,
+                     shared_tiled=ops.tiled_shared_weights(layer.desc, inp.w_shared_gate_up, inp.w_shared_down))
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    for n in grads:
+        assert torch.equal(grads[n], grads2[n]), n
+
+
 def test_backward_replays_from_a_captured_graph():
     """moe_backward captured into a HIP graph: every replay equals the eager gradients bit
     for bit (the library clears its buffers with kernels, never with memsets)."""

@@ -244,6 +244,23 @@ def test_tile_major_weights_give_the_same_forward(T, d, E, k, f):
     assert row_rel_err(to_np(tiled.out)[sample], ref["out"]) <= tol_for(w.torch_dtype)
 
 
+def test_shared_expert_on_packed_rows_and_tile_major_weights():
+    """A shared expert over T >= 256 tokens runs in the large-tile regime on packed x rows; with
+    its weights' tile-major copies the output is the same bit for bit, and the oracle agrees."""
+    T, d, E, k, f, cf, fs = 1100, 256, 8, 2, 128, 1.25, 576  # 1100 rows: four full tiles and 76 rows
+    w = wl.Workload("tiled-shared", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset="boost4")
+    say("shared expert, packed rows and tile-major weights")
+    inp = wl.make_inputs(w, seed=8, device=DEV)
+    cap = ops.moe_capacity(T, E, cf)
+    plain = ops.MoELayer(inp, cap)
+    plain.forward()
+    tiled = ops.MoELayer(inp, cap, shared_tiled=True)
+    tiled.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(plain.out.view(torch.int16), tiled.out.view(torch.int16))
+    _run_and_check(inp, sample=np.arange(0, T, 13))
+
+
 def test_tile_major_weights_in_expert_shards():
     """One large expert per rank (the down projection cut along K): each rank's partial from
     its experts' tile-major copies equals the partial from the row-major weights."""
