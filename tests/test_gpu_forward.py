@@ -21,10 +21,10 @@ ops = pytest.importorskip("sparse_mixture_experts_level_amd.ops")
 DEV = "cuda"
 
 
-def _run_and_check(inp, sample=None, check_logits=True):
+def _run_and_check(inp, sample=None, check_logits=True, tiled=False, shared_tiled=False):
     w = inp.workload
     cap = ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor)
-    layer = ops.MoELayer(inp, cap)
+    layer = ops.MoELayer(inp, cap, tiled=tiled, shared_tiled=shared_tiled)
     layer.forward()
     torch.cuda.synchronize()
     r = {k: to_np(v) for k, v in layer.routing.items()}
@@ -144,20 +144,42 @@ def test_forward_is_deterministic():
 FULL = [("switch_bf16", 48), ("mixtral_bf16", 24), ("gptoss_decode_bf16", None), ("deepseek_v3_bf16", 12)]
 
 
+def _full_sample(w, nsample):
+    if nsample is None:
+        return None
+    rng = np.random.default_rng(0)
+    # the last tokens of the batch are the ones capacity drops first: always include a few
+    return np.unique(np.concatenate([rng.choice(w.num_tokens, nsample - 4, replace=False),
+                                     np.arange(w.num_tokens - 4, w.num_tokens)]))
+
+
 @pytest.mark.parametrize("name,nsample", FULL)
 def test_full_size_workloads(name, nsample):
     w = wl.get_workload(name)
     say(f"full size {w.description}")
     inp = wl.make_inputs(w, seed=0, device=DEV)
-    sample = None
-    if nsample is not None:
-        rng = np.random.default_rng(0)
-        # the last tokens of the batch are the ones capacity drops first: always include a few
-        sample = np.unique(np.concatenate([rng.choice(w.num_tokens, nsample - 4, replace=False),
-                                           np.arange(w.num_tokens - 4, w.num_tokens)]))
+    sample = _full_sample(w, nsample)
     res = _run_and_check(inp, sample=sample)
     say(f"  max row rel err {res['err']:.3e}, near-tie routing differences {res['differ']}, drops {res['drops']}")
     del res
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,nsample,tiled,shared_tiled", [("mixtral_bf16", 24, True, False),
+                                                             ("deepseek_v3_bf16", 12, False, True)])
+def test_full_size_workloads_with_tile_major_weights(name, nsample, tiled, shared_tiled):
+    """The two full-size layers whose experts take the large-tile regime, as bench.py times them:
+    with tile-major copies of those weights (routed / shared).  Checked against the oracle on
+    sampled tokens and bitwise against the same layer on row-major weights."""
+    w = wl.get_workload(name)
+    say(f"full size, tile-major weights: {w.description}")
+    inp = wl.make_inputs(w, seed=0, device=DEV)
+    res = _run_and_check(inp, sample=_full_sample(w, nsample), tiled=tiled, shared_tiled=shared_tiled)
+    plain = ops.MoELayer(inp, ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor))
+    plain.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(plain.out.view(torch.int16), res["layer"].out.view(torch.int16))
+    del res, plain
     torch.cuda.empty_cache()
 
 
