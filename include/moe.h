@@ -97,7 +97,8 @@ typedef struct moe_desc {
 /* Expert weights of one layer (device pointers).  Packed layouts follow the
  * runtime layout of [HF-MoE] "Рефакторинг загрузки весов": gate_up_proj holds,
  * per expert, the gate projection rows (w1) followed by the up projection rows
- * (w3); down_proj holds w2. */
+ * (w3); down_proj holds w2.  Zero-initialise the struct, so that the optional
+ * fields at its end are NULL unless set. */
 typedef struct moe_weights {
   const void *w_router;         /* [E, d] */
   const void *w_gate_up;        /* [E, 2f, d]: rows 0..f-1 gate, f..2f-1 up */
