@@ -385,3 +385,49 @@ def test_aux_loss_uniform_is_alpha():
     lg[np.arange(T), np.arange(T) % E] = 1e-3  # round-robin choice, nearly uniform probabilities
     loss, _ = _aux_gpu(lg, 1, alpha=0.02)
     assert loss == pytest.approx(0.02, rel=1e-3)
+
+
+def _tiled_reference(w, rows_per_tile_gate, n_rows, K, swiglu):
+    """The tile-major layout as include/moe.h documents it, built with NumPy from row-major
+    weights w [E, rows, K] (uint16 view): per expert, tile nt and K step kt a block of 256 rows
+    x 32 values, 16-byte chunk c of row r stored at chunk position c ^ ((r >> 2) & 3), rows past
+    the matrix zero; gate_up tiles hold 128 gate rows then the matching up rows (n_rows apart)."""
+    E = w.shape[0]
+    ntiles = -(-n_rows // rows_per_tile_gate)
+    out = np.zeros((E, ntiles, K // 32, 256, 4, 8), dtype=np.uint16)
+    for e in range(E):
+        for nt in range(ntiles):
+            for r in range(256):
+                if swiglu:
+                    col = nt * 128 + (r & 127)
+                    if col >= n_rows:
+                        continue
+                    src = col if r < 128 else n_rows + col
+                else:
+                    src = nt * 256 + r
+                    if src >= n_rows:
+                        continue
+                chunks = w[e, src].reshape(K // 32, 4, 8)
+                for c in range(4):
+                    out[e, nt, :, r, c ^ ((r >> 2) & 3), :] = chunks[:, c, :]
+    return out.reshape(-1)
+
+
+def test_tile_major_weights_layout_is_the_documented_one():
+    """moe_tile_expert_weights writes exactly the layout its declaration describes (ragged
+    tiles: f = 192 is 1.5 gate_up tiles of 128, d = 64 is a quarter of a down tile)."""
+    E, d, f = 3, 64, 192
+    say("tile-major weight layout, E=3 d=64 f=192")
+    g = torch.Generator(device=DEV).manual_seed(21)
+    w_gu = torch.randn((E, 2 * f, d), generator=g, device=DEV).to(torch.bfloat16)
+    w_dn = torch.randn((E, d, f), generator=g, device=DEV).to(torch.bfloat16)
+    desc = ops.make_desc(64, d, f, E, 1, None, 0, torch.bfloat16)
+    gu_t, dn_t = ops.tiled_weights(desc, w_gu, w_dn)
+    torch.cuda.synchronize()
+    got_gu = gu_t.cpu().numpy().view(np.uint16)
+    got_dn = dn_t.cpu().numpy().view(np.uint16)
+    want_gu = _tiled_reference(w_gu.cpu().view(torch.int16).numpy().view(np.uint16), 128, f, d, True)
+    want_dn = _tiled_reference(w_dn.cpu().view(torch.int16).numpy().view(np.uint16), 256, d, f, False)
+    assert got_gu.shape == want_gu.shape and got_dn.shape == want_dn.shape
+    assert np.array_equal(got_gu, want_gu)
+    assert np.array_equal(got_dn, want_dn)
