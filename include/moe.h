@@ -164,6 +164,22 @@ const char *moe_status_string(moe_status status);
 /* Detail of the last failure in the calling thread ("" if none). */
 const char *moe_last_error(void);
 
+/* The ids precondition of moe_dispatch_permute, moe_dispatch_reroute and
+ * moe_combine_unpermute, checked on a HOST copy of the ids ([SMoE] "Роутер и top-k
+ * gating": each id names one of the E experts): every topk_ids_host[t][j], [T, k] int32,
+ * lies in [0, E).  Returns MOE_OK, or MOE_ERR_INVALID with moe_last_error() naming the
+ * first entry outside the range.  Host only, no device access.
+ * Release builds do not check ids on the device: an id outside [0, E) is treated as no
+ * expert (slot -1, not counted, never indexes a table).  The debug build of the library
+ * (libmoe_debug.so, compiled with MOE_DEBUG_CHECKS) runs this check inside those three
+ * calls on a synchronous copy of the device ids, before it enqueues any work, and returns
+ * its MOE_ERR_INVALID. */
+moe_status moe_check_topk_ids(const moe_desc *desc, const int32_t *topk_ids_host);
+
+/* 1 in the debug build (MOE_DEBUG_CHECKS: host checks of device-side preconditions, which
+ * synchronise the stream), 0 otherwise. */
+int32_t moe_debug_checks(void);
+
 /* ---------------------------------------------------------------- hot path */
 
 /* Router linear ([SMoE] "Роутер и top-k gating": logits from a linear layer
@@ -191,7 +207,8 @@ moe_status moe_router_topk(const moe_desc *desc, const float *logits, int32_t *t
  * rank-major: j outer, t inner), each takes the next free slot of its expert while
  * fewer than C are taken; later ones are dropped.  desc->overflow must be
  * MOE_OVERFLOW_DROP (MOE_ERR_INVALID otherwise; redirection is moe_dispatch_reroute).
- *   topk_ids       [T, k] int32, each in [0, E) (precondition, not checked on device)
+ *   topk_ids       [T, k] int32, each in [0, E) (precondition; see moe_check_topk_ids: an id
+ *                  outside the range is treated as dropped, slot -1, and not counted)
  *   x              [T, d] dtype, or NULL when x_perm is NULL
  *   expert_counts  [E]   int32, written: demand per expert
  *   expert_offsets [E+1] int32, written: offsets[0] = 0, offsets[e+1] - offsets[e] =
@@ -281,7 +298,8 @@ moe_status moe_grouped_down(int32_t num_groups, int64_t rows_max, int32_t group_
  *            y_perm[expert_offsets[topk_ids[t,j]] + slot[t,j]], summed in float in
  *            order j = 0..k-1, then rounded to dtype.
  *   topk_ids: the expert serving each assignment -- the router's ids, or the
- *   assigned_ids of moe_dispatch_reroute when overflow is redirected.
+ *   assigned_ids of moe_dispatch_reroute when overflow is redirected; each in [0, E)
+ *   (precondition, see moe_check_topk_ids: an id outside the range adds nothing).
  *   y_perm [R_max, d] dtype; shared_out [T, d] dtype or NULL; out [T, d] dtype */
 moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const int32_t *topk_ids,
                                  const float *topk_gates, const int32_t *slot,

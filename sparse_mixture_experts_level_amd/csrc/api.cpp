@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -110,6 +111,32 @@ moe_status check_desc(const moe_desc *desc) {
     return fail(MOE_ERR_UNSUPPORTED, "x must be smaller than 2 GiB (32-bit row gather offsets)");
   return check_dtype_dims(D.dtype, D.d_model, D.d_ff, D.d_ff_shared);
 }
+
+// The ids precondition of the dispatch and combine calls, on a host copy: every entry in
+// [0, E).  Names the first entry outside the range.
+moe_status check_ids_host(const moe_desc &D, const int32_t *ids) {
+  const int64_t n = (int64_t)D.num_tokens * D.top_k;
+  for (int64_t q = 0; q < n; ++q)
+    if (ids[q] < 0 || ids[q] >= D.num_experts)
+      return fail(MOE_ERR_INVALID, "topk_ids[%lld][%d] = %d is outside [0, %d)", (long long)(q / D.top_k),
+                  (int)(q % D.top_k), (int)ids[q], D.num_experts);
+  return MOE_OK;
+}
+
+#ifdef MOE_DEBUG_CHECKS
+// Debug builds: the same check on a synchronous copy of the device ids, before any launch.
+moe_status debug_check_ids(const moe_desc &D, const int32_t *ids_dev, hipStream_t s) {
+  std::vector<int32_t> h((size_t)D.num_tokens * D.top_k);
+  if (h.empty()) return MOE_OK;
+  MOE_TRY_HIP(hipMemcpyAsync(h.data(), ids_dev, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+              "debug check: copy topk_ids to the host");
+  MOE_TRY_HIP(hipStreamSynchronize(s), "debug check: synchronise");
+  return check_ids_host(D, h.data());
+}
+#define MOE_DEBUG_CHECK_IDS(D, ids, s) MOE_TRY(debug_check_ids((D), (ids), (s)))
+#else
+#define MOE_DEBUG_CHECK_IDS(D, ids, s) ((void)0)
+#endif
 
 int64_t max_rows(const moe_desc &D) {
   const int64_t tk = (int64_t)D.num_tokens * D.top_k;
@@ -351,6 +378,22 @@ const char *moe_status_string(moe_status status) {
 
 const char *moe_last_error(void) { return g_last_error.c_str(); }
 
+moe_status moe_check_topk_ids(const moe_desc *desc, const int32_t *topk_ids_host) {
+  MOE_TRY(check_desc(desc));
+  if (desc->num_tokens == 0) return ok();
+  if (!topk_ids_host) return fail(MOE_ERR_INVALID, "topk_ids_host is NULL");
+  MOE_TRY(check_ids_host(*desc, topk_ids_host));
+  return ok();
+}
+
+int32_t moe_debug_checks(void) {
+#ifdef MOE_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 moe_status moe_router_logits(const moe_desc *desc, const void *x, const void *w_router, const float *logit_offset,
                              float *logits, hipStream_t stream) {
   MOE_TRY(check_desc(desc));
@@ -402,6 +445,7 @@ moe_status moe_dispatch_permute(const moe_desc *desc, const int32_t *topk_ids, c
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
   MOE_TRY(check_ptr(ws, "ws"));
+  MOE_DEBUG_CHECK_IDS(D, topk_ids, stream);
   MOE_TRY_HIP(moe::launch_dispatch(topk_ids, D.num_tokens, D.top_k, D.num_experts, D.capacity,
                                    D.fill_order == MOE_FILL_RANK_MAJOR, expert_counts, expert_offsets, slot, row_token,
                                    static_cast<int32_t *>(ws), stream),
@@ -433,6 +477,7 @@ moe_status moe_dispatch_reroute(const moe_desc *desc, const float *logits, const
     return fail(MOE_ERR_WORKSPACE, "dispatch with redirection needs %zu workspace bytes, got %zu", need,
                 ws ? ws_bytes : (size_t)0);
   MOE_TRY(check_ptr(ws, "ws"));
+  MOE_DEBUG_CHECK_IDS(D, topk_ids, stream);
   const bool rank_major = D.fill_order == MOE_FILL_RANK_MAJOR;
   if (D.capacity == MOE_NO_CAPACITY) {  // nothing overflows
     MOE_TRY_HIP(moe::launch_dispatch(topk_ids, T, k, E, D.capacity, rank_major, expert_counts, expert_offsets, slot,
@@ -523,8 +568,10 @@ moe_status moe_combine_unpermute(const moe_desc *desc, const void *y_perm, const
   MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
   MOE_TRY(check_opt_ptr(shared_out, "shared_out"));
   MOE_TRY(check_ptr(out, "out"));
+  MOE_DEBUG_CHECK_IDS(D, topk_ids, stream);
+  // ids outside [0, E) add nothing (with a slot >= 0 they would index past expert_offsets)
   MOE_TRY_HIP(moe::launch_combine(y_perm, topk_ids, topk_gates, slot, expert_offsets, shared_out, out, D.num_tokens,
-                                  D.d_model, D.top_k, D.dtype == MOE_DTYPE_BF16, stream),
+                                  D.d_model, D.top_k, D.dtype == MOE_DTYPE_BF16, stream, 0, D.num_experts),
               "combine");
   return ok();
 }

@@ -45,7 +45,9 @@ __device__ __forceinline__ int64_t fill_q(int64_t p, int T, int k, bool rank_maj
   return (p - j * T) * k + j;
 }
 
-// Histogram of the experts of this block's positions; negative entries are skipped.
+// Histogram of the experts of this block's positions; entries outside [0, E) are skipped
+// (negative ones mark "no expert"; larger ones break the caller's precondition and are
+// treated as dropped rather than indexing past the tables).
 __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(const int32_t *__restrict__ ids, int T, int k,
                                                                     int E, int64_t per_block, int rank_major,
                                                                     int32_t *__restrict__ hist) {
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(const int32_
   const int64_t p0 = (int64_t)b * per_block, p1 = min(p0 + per_block, n);
   for (int64_t p = p0 + threadIdx.x; p < p1; p += DP_THREADS) {
     const int e = ids[fill_q(p, T, k, rank_major != 0)];
-    if (e >= 0) atomicAdd(&s_hist[e], 1);
+    if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += DP_THREADS) hist[(size_t)b * E + e] = s_hist[e];
@@ -133,20 +135,23 @@ struct RankLds {
 };
 
 // Walks the block's positions [p0, p1) in order, 256 per chunk, and calls
-// on_rank(q, e, s_run[e] + rank) for every element whose expert e = sel[q] is >= 0,
+// on_rank(q, e, s_run[e] + rank) for every element whose expert e = sel[q] is in [0, E),
 // where rank counts the earlier elements of the walk with the same expert (earlier
-// waves of the chunk plus lower lanes of the own wave).  s_run[e] then advances by the
-// chunk's count.  s_run and the tags must be set up by the caller (tags to -1).
-template <class F>
-__device__ __forceinline__ void rank_walk(const int32_t *__restrict__ sel, int T, int k, bool rank_major, int64_t p0,
-                                          int64_t p1, int nbits, RankLds &L, int32_t *s_run, F on_rank) {
+// waves of the chunk plus lower lanes of the own wave), and on_skip(q) for every other
+// element.  s_run[e] then advances by the chunk's count.  s_run and the tags must be set
+// up by the caller (tags to -1).
+template <class F, class G>
+__device__ __forceinline__ void rank_walk(const int32_t *__restrict__ sel, int T, int k, int E, bool rank_major,
+                                          int64_t p0, int64_t p1, int nbits, RankLds &L, int32_t *s_run, F on_rank,
+                                          G on_skip) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int chunk = 0;
   for (int64_t c0 = p0; c0 < p1; c0 += DP_THREADS, ++chunk) {
     const int64_t p = c0 + tid;
     const int64_t q = p < p1 ? fill_q(p, T, k, rank_major) : 0;
     const int ev = p < p1 ? sel[q] : -1;
-    const bool valid = ev >= 0;
+    const bool valid = ev >= 0 && ev < E;
+    if (p < p1 && !valid) on_skip(q);
     const int e = valid ? ev : 0;
     const uint64_t m = match_any(e, valid, nbits);
     const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
@@ -204,14 +209,17 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_assign_kernel(
   }
   const int64_t n = (int64_t)T * k;
   const int64_t p0 = (int64_t)b * per_block, p1 = min(p0 + per_block, n);
-  rank_walk(ids, T, k, rank_major != 0, p0, p1, bits_for(E), L, s_base, [&](int64_t q, int e, int sl) {
-    if (cap < 0 || sl < cap) {
-      slot[q] = sl;
-      if constexpr (WRITE_ROWS) row_token[s_off[e] + sl] = int32_t(q / k);
-    } else {
-      slot[q] = -1;
-    }
-  });
+  rank_walk(
+      ids, T, k, E, rank_major != 0, p0, p1, bits_for(E), L, s_base,
+      [&](int64_t q, int e, int sl) {
+        if (cap < 0 || sl < cap) {
+          slot[q] = sl;
+          if constexpr (WRITE_ROWS) row_token[s_off[e] + sl] = int32_t(q / k);
+        } else {
+          slot[q] = -1;
+        }
+      },
+      [&](int64_t q) { slot[q] = -1; });  // an id outside [0, E): no expert, dropped
 }
 
 // Offers of the two-pass fill: the i-th overflowing assignment of token t (in rank
@@ -265,19 +273,23 @@ __global__ __launch_bounds__(DP_THREADS) void reroute_assign_kernel(
   }
   const int64_t n = (int64_t)T * k;
   const int64_t p0 = (int64_t)b * per_block, p1 = min(p0 + per_block, n);
-  rank_walk(offer, T, k, rank_major != 0, p0, p1, bits_for(E), L, s_base, [&](int64_t q, int e, int sl) {
-    if (sl < cap) {
-      slot[q] = sl;
-      assigned[q] = e;
-      row_token[s_off[e] + sl] = int32_t(q / k);
-    } else {
-      assigned[q] = ids[q];
-    }
-  });
+  rank_walk(
+      offer, T, k, E, rank_major != 0, p0, p1, bits_for(E), L, s_base,
+      [&](int64_t q, int e, int sl) {
+        if (sl < cap) {
+          slot[q] = sl;
+          assigned[q] = e;
+          row_token[s_off[e] + sl] = int32_t(q / k);
+        } else {
+          assigned[q] = ids[q];
+        }
+      },
+      [](int64_t) {});  // no offer: handled below
   // assignments without an offer: kept by the first pass, or dropped with nothing to offer
   for (int64_t p = p0 + tid; p < p1; p += DP_THREADS) {
     const int64_t q = fill_q(p, T, k, rank_major != 0);
-    if (offer[q] >= 0) continue;
+    const int o = offer[q];
+    if (o >= 0 && o < E) continue;
     const int e = ids[q];
     assigned[q] = e;
     const int sl = slot[q];

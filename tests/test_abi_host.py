@@ -194,3 +194,36 @@ def test_tiled_weights_sizes_and_argument_checks():
     W = ops.MoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE)
     st = L.moe_forward(ctypes.byref(ds), ctypes.byref(W), FAKE, None, FAKE, None, FAKE, 1 << 40, None)
     assert st == ops.MOE_ERR_INVALID and b"w_shared_gate_up_tiled" in L.moe_last_error()
+
+
+# --------------------------------------------------------------------------------------------
+# The ids precondition of the dispatch and combine calls (each id names one of the E experts)
+# --------------------------------------------------------------------------------------------
+
+def test_check_topk_ids_accepts_valid_and_names_the_first_bad_entry():
+    import numpy as np
+
+    desc = _desc(num_tokens=5, num_experts=8, top_k=2)
+    ids = np.array([[0, 7], [3, 4], [1, 2], [6, 5], [0, 1]], dtype=np.int32)
+    ops.moe_check_topk_ids(desc, ids)
+    for t, j, bad in [(3, 1, 8), (0, 0, -1), (4, 1, 1 << 30)]:
+        wrong = ids.copy()
+        wrong[t, j] = bad
+        with pytest.raises(ops.MoEError) as ei:
+            ops.moe_check_topk_ids(desc, wrong)
+        assert ei.value.status == ops.MOE_ERR_INVALID
+        assert f"topk_ids[{t}][{j}] = {bad}" in str(ei.value)
+    assert L.moe_check_topk_ids(ctypes.byref(desc), None) == ops.MOE_ERR_INVALID
+    assert L.moe_check_topk_ids(ctypes.byref(_desc(num_tokens=0)), None) == ops.MOE_OK
+
+
+def test_debug_build_flag():
+    assert L.moe_debug_checks() == 0
+    D = ops.debug_lib()
+    assert D.moe_debug_checks() == 1
+    for n in ops.SYMBOLS:
+        assert hasattr(D, n), n
+    # the debug library validates arguments like the release one before its ids check
+    desc = _desc(num_tokens=5, num_experts=8, top_k=2)
+    st = D.moe_dispatch_permute(ctypes.byref(desc), None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None)
+    assert st == ops.MOE_ERR_INVALID and b"topk_ids" in D.moe_last_error()

@@ -2,15 +2,14 @@
 
 Sizes span several tiles and ragged tails while the oracle still finishes in seconds.
 """
-import json
 import math
-import os
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from tests.demo_inputs import demo2_fixture, demo2_router_logits
 from tests.moe_testlib import (GATE_TOL, HostExperts, check_dispatch_exact, row_rel_err, say, to_np, tol_for)
 
 pytestmark = pytest.mark.gpu
@@ -96,6 +95,100 @@ def test_dispatch_bitexact(T, E, k, cap, skew):
     _dispatch_case(_ids(rng, T, E, k, skew), E, cap)
 
 
+def _ids_with_strays(seed, T=700, E=16, k=2):
+    """Routing ids with one entry outside [0, E) in about 5% of the tokens; also the same ids
+    with every stray entry replaced by a phantom expert E, ordered after all real ones, and the
+    valid ids the strays replaced."""
+    rng = np.random.default_rng(seed)
+    ids = _ids(rng, T, E, k, 0.5)
+    toks = np.nonzero(rng.random(T) < 0.05)[0]
+    js = rng.integers(0, k, size=toks.size)
+    bad = ids.copy()
+    bad[toks, js] = rng.choice([-1, -5, E, E + 3, 1 << 20, -(1 << 30)], size=toks.size)
+    phantom = ids.copy()
+    phantom[toks, js] = E
+    return bad, phantom, (toks, js), ids
+
+
+def test_dispatch_ids_outside_the_range_are_dropped():
+    """An id outside [0, E) (a broken precondition) is no expert: slot -1, not counted, no row.
+    The expected tables are the oracle's fill with such ids sent to a phantom expert E placed
+    after every real one (its rows come last, so no real expert's slots or offsets move)."""
+    T, E, k, cap = 700, 16, 2, 60
+    bad, phantom, stray, _ = _ids_with_strays(5, T, E, k)
+    say(f"dispatch with stray ids T={T} E={E} k={k} cap={cap}")
+    desc = _desc(T, E, k, cap, dtype=torch.bfloat16)
+    R = ops.moe_max_rows(desc)
+    ids = torch.from_numpy(bad).to(DEV)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    row_token = torch.full((max(R, 1),), -7, dtype=torch.int32, device=DEV)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    ops.moe_dispatch_permute(desc, ids, None, counts, offsets, slot, row_token, None, ws)
+    torch.cuda.synchronize()
+    ref = oracle.capacity_fill(phantom, E + 1, cap)
+    want_slot = ref["slot"].copy()
+    want_slot[stray] = -1
+    assert np.array_equal(to_np(counts), ref["counts"][:E])
+    assert np.array_equal(to_np(offsets), ref["offsets"][:E + 1])
+    assert np.array_equal(to_np(slot), want_slot)
+    Rk = int(ref["offsets"][E])
+    assert np.array_equal(to_np(row_token)[:Rk], ref["row_token"][:Rk])
+
+    # the combine adds nothing for an id outside [0, E), even with a slot >= 0 beside it
+    d = 64
+    y_perm = torch.randn((max(R, 1), d), device=DEV).to(torch.bfloat16)
+    gates = torch.rand((T, k), device=DEV)
+    slot_good = slot.clone()
+    toks, js = stray
+    good_ids = torch.from_numpy(np.where(phantom == E, 0, phantom).astype(np.int32)).to(DEV)
+    slot_good[torch.from_numpy(toks).long().to(DEV), torch.from_numpy(js).long().to(DEV)] = 0
+    out_bad = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    out_ref = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    ops.moe_combine_unpermute(desc, y_perm, ids, gates, slot_good, offsets, None, out_bad)
+    ops.moe_combine_unpermute(desc, y_perm, good_ids, gates, slot, offsets, None, out_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out_bad, out_ref)
+
+
+def test_debug_library_rejects_ids_outside_the_range():
+    """libmoe_debug.so checks the ids precondition on the host before any launch: a stray id
+    gives MOE_ERR_INVALID and leaves every output untouched; valid ids give the release
+    library's tables."""
+    T, E, k, cap = 700, 16, 2, 60
+    bad, _, stray, good = _ids_with_strays(6, T, E, k)
+    D = ops.debug_lib()
+    desc = _desc(T, E, k, cap, dtype=torch.bfloat16)
+    R = ops.moe_max_rows(desc)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+
+    def run(ids_np, L):
+        tabs = [torch.full(n, -7, dtype=torch.int32, device=DEV) for n in ((E,), (E + 1,), (T, k), (max(R, 1),))]
+        ops.moe_dispatch_permute(desc, torch.from_numpy(ids_np).to(DEV), None, *tabs, None, ws, L=L)
+        torch.cuda.synchronize()
+        return [to_np(t) for t in tabs]
+
+    say("debug library: stray id rejected")
+    with pytest.raises(ops.MoEError) as ei:
+        run(bad, D)
+    assert ei.value.status == ops.MOE_ERR_INVALID
+    t0, j0 = int(stray[0][0]), int(stray[1][0])
+    assert f"topk_ids[{t0}][{j0}]" in str(ei.value)
+    say("debug library: valid ids accepted, same tables as the release library")
+    got, want = run(good, D), run(good, ops.lib())
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+    y_perm = torch.zeros((max(R, 1), 64), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((T, 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ops.MoEError):
+        ops.moe_combine_unpermute(desc, y_perm, torch.from_numpy(bad).to(DEV), torch.ones((T, k), device=DEV),
+                                  torch.zeros((T, k), dtype=torch.int32, device=DEV),
+                                  torch.zeros(E + 1, dtype=torch.int32, device=DEV), None, out, L=D)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
 def _variant_case(logits_np, k, cap, order, reroute, tag=""):
     """Rank-major fill and/or redirection of overflow on the GPU vs the oracle, bit-exact.  The
     ids come from the GPU's top-k of float32 logits, and the oracle takes the same float32
@@ -155,17 +248,11 @@ def test_dispatch_float_rows_and_everyone_on_one_expert():
 
 def test_demo_worked_example_on_gpu():
     """The page's demo: drops 8/5 (balanced) and 11/9 (collapsed) at C = 4/5."""
-    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "demo2_capacity_dropping.json")))
-    torch.manual_seed(42)
-    x = torch.randn(32, 64)
-    balanced = torch.nn.Linear(64, 8, bias=False)
-    collapsed = torch.nn.Linear(64, 8, bias=False)
-    with torch.no_grad():
-        collapsed.weight[0] += 5.0
-        logits = {"balanced": balanced(x), "collapsed": collapsed(x)}
+    g = demo2_fixture()
+    logits = demo2_router_logits()
     for name, lg in logits.items():
         say(f"demo {name}")
-        lg = lg.float().contiguous().to(DEV)
+        lg = torch.from_numpy(lg.astype(np.float32)).to(DEV)
         ids = torch.empty((32, 1), dtype=torch.int32, device=DEV)
         gates = torch.empty((32, 1), dtype=torch.float32, device=DEV)
         ops.moe_router_topk(_desc(32, 8, 1), lg, ids, gates)
@@ -355,15 +442,9 @@ def _aux_gpu(logits_np, k, alpha=0.01, cap=None):
 
 def test_aux_loss_reproduces_the_demo():
     """The page's demo prints 0.010505 (balanced router) and 0.019086 (collapsed)."""
-    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "demo2_capacity_dropping.json")))
-    torch.manual_seed(42)
-    x = torch.randn(32, 64)
-    balanced = torch.nn.Linear(64, 8, bias=False)
-    collapsed = torch.nn.Linear(64, 8, bias=False)
-    with torch.no_grad():
-        collapsed.weight[0] += 5.0
-        lb, lc = balanced(x).numpy(), collapsed(x).numpy()
-    for name, lg in (("balanced", lb), ("collapsed", lc)):
+    g = demo2_fixture()
+    logits = demo2_router_logits()
+    for name, lg in logits.items():
         say(f"aux loss demo {name}")
         loss, _ = _aux_gpu(lg.astype(np.float64), 1, cap=ops.moe_capacity(32, 8, 1.0))
         assert round(loss, 6) == g[name]["aux_loss"]

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests.demo_inputs import demo2_router_logits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -28,25 +29,8 @@ def _load(name):
 # --------------------------------------------------------------------------------------------
 
 def _demo2_logits():
-    """Regenerates the demo's inputs with torch's CPU generator (the page's seeded draw),
-    then returns the router logits it would compute, as float32 values."""
-    torch = pytest.importorskip("torch")
-    torch.manual_seed(42)
-    x = torch.randn(32, 64)
-    balanced = torch.nn.Linear(64, 8, bias=False)
-    collapsed = torch.nn.Linear(64, 8, bias=False)
-    with torch.no_grad():
-        collapsed.weight[0] += 5.0
-        lb = balanced(x)
-        lc = collapsed(x)
-    # Guard: the page warns the draw may change between torch versions.  If the generator
-    # no longer reproduces the printed balanced aux loss, the fixture does not apply.
-    p = torch.softmax(lb, dim=-1)
-    f = torch.bincount(p.argmax(dim=-1), minlength=8).float() / 32
-    guard = float(0.01 * 8 * (f * p.mean(dim=0)).sum())
-    if round(guard, 6) != 0.010505:
-        pytest.skip("torch's seeded draw differs from the page's; demo fixture not reproducible")
-    return lb.numpy().astype(np.float64), lc.numpy().astype(np.float64)
+    lg = demo2_router_logits()
+    return lg["balanced"], lg["collapsed"]
 
 
 def test_demo2_capacity_drops_counts_aux():
