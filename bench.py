@@ -1,13 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MoE layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload switch_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload deepseek_v3_bf16]
 
 One step = one moe_forward call over the whole batch (router linear, top-k,
-dispatch, gate_up + SwiGLU grouped GEMM, down grouped GEMM, combine) with inputs
-and weights already resident in HBM.  Prints one JSON line: tokens/s for the
-workload, the roofline of the dominant kernel (timed live with HIP events on the
-library's stream), and the CPU oracle timed on a bounded sample on this host.
+dispatch, gate_up + SwiGLU grouped GEMM, down grouped GEMM, shared expert,
+combine) with inputs and weights already resident in HBM.  Before every step
+(warm-up and timed) an untimed 512 MiB scratch write evicts the last-level cache;
+each step is bracketed by HIP events on the library's stream and the median
+step is reported.  Prints one JSON line: tokens/s for the workload, the roofline
+of the dominant kernel (its launches timed live between the events that
+moe_forward_staged records around the very launches moe_forward makes), the
+routed and shared phases against their own rooflines, and the CPU oracle timed
+on a bounded sample on this host.
 """
 from __future__ import annotations
 
@@ -15,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -25,17 +31,25 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "MoE-layer fwd tokens/sec on 1 MI355X; % of MFMA bf16 / HBM peak"
-DOMINANT_SOURCES = ["sparse_mixture_experts_level_amd/csrc/gemm_stream.hip",
-                    "sparse_mixture_experts_level_amd/csrc/common.hpp"]
+# sources of the grouped-GEMM kernels: counter records are used only while these are unchanged
+GEMM_SOURCES = ["sparse_mixture_experts_level_amd/csrc/gemm_stream.hip",
+                "sparse_mixture_experts_level_amd/csrc/gemm_big.hip",
+                "sparse_mixture_experts_level_amd/csrc/common.hpp"]
+# the largest configuration that fits one GPU
+DEFAULT_WORKLOAD = "deepseek_v3_bf16"
+CPU_SAMPLE = {"tiny_f32": 64, "switch_bf16": 8192, "mixtral_bf16": 64, "gptoss_decode_bf16": 16,
+              "deepseek_v3_bf16": 16}
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="switch_bf16")
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="untimed scratch write before every step, in MiB (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle's sample (0: pick by workload)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -50,7 +64,7 @@ def parse():
     p.add_argument("--ep-shards", type=int, default=1, metavar="N",
                    help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
                         "contiguous ranges, every range timed on this GPU, the slowest one reported")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 def source_hash(paths) -> str:
@@ -68,8 +82,73 @@ def weight_layout(args):
     return f"row-major plus tile-major copies of the {' and '.join(which)} expert weights, prepared once before timing"
 
 
-def main():
-    args = parse()
+def big_regime(rows_max, groups, group_rows_max):
+    """The library's regime rule: groups averaging >= 256 rows that can reach 256 rows run on
+    the large-tile kernel, the others on the streaming one."""
+    return groups > 0 and rows_max // groups >= 256 and group_rows_max >= 256
+
+
+def tail_rows(rows, n_out_min):
+    """Rows the large-tile launch leaves to its tail launch: a group's last partial 256-row tile
+    of at most 128 rows, when the tail launch (groups x 64-column tiles) reaches 512 workgroups."""
+    if len(rows) * ((n_out_min + 63) // 64) < 512:
+        return 0
+    return int(sum(r % 256 for r in rows if 0 < r % 256 <= 128))
+
+
+def stage_work(w, R, E_t, kept, T, s_bytes, cap, rmax):
+    """Algorithmic bytes and FLOP of the main launch of each GEMM stage (what the method must
+    move and compute: touched weights once, activation rows read once, outputs written once)."""
+    d, f, fs, E = w.d_model, w.d_ff, w.d_ff_shared, w.num_experts
+    grm = T if cap is None else min(T, cap)
+    work = {}
+    routed_big = w.dtype == "bf16" and big_regime(rmax, E, grm)
+    Rm = R - (tail_rows(kept, min(d, f)) if routed_big else 0)
+    work["gate_up"] = {"bytes": s_bytes * (E_t * 2 * f * d + Rm * d + Rm * f), "flop": 4.0 * Rm * d * f,
+                       "kernel": "grouped_gemm_big_kernel (gate_up + SwiGLU)" if routed_big
+                       else "grouped_gemm_stream_kernel (gate_up + SwiGLU)"}
+    work["down"] = {"bytes": s_bytes * (E_t * d * f + Rm * f + Rm * d), "flop": 2.0 * Rm * d * f,
+                    "kernel": "grouped_gemm_big_kernel (down)" if routed_big else "grouped_gemm_stream_kernel (down)"}
+    if fs:
+        sh_big = w.dtype == "bf16" and big_regime(T, 1, T)
+        Ts = T - (tail_rows([T], min(d, fs)) if sh_big else 0)
+        kind = "grouped_gemm_big_kernel" if sh_big else "grouped_gemm_stream_kernel"
+        work["shared_gate_up"] = {"bytes": s_bytes * (2 * fs * d + Ts * d + Ts * fs), "flop": 4.0 * Ts * d * fs,
+                                  "kernel": f"{kind} (shared expert gate_up + SwiGLU)"}
+        work["shared_down"] = {"bytes": s_bytes * (d * fs + Ts * fs + Ts * d), "flop": 2.0 * Ts * d * fs,
+                               "kernel": f"{kind} (shared expert down)"}
+    return work
+
+
+def roofline_of(work, dur_us, s_bytes):
+    """Bound by the kernel's own intensity against the ridge (peak FLOP/s / peak bytes/s)."""
+    peak_flops = (MFMA_BF16_PEAK_TFLOPS if s_bytes == 2 else MFMA_F32_PEAK_TFLOPS) * 1e12
+    ridge = peak_flops / (HBM_PEAK_GBS * 1e9)
+    if work["flop"] / work["bytes"] < ridge:
+        achieved = work["bytes"] / (dur_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = work["flop"] / (dur_us * 1e-6) / 1e12
+    peak = peak_flops / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4)}
+
+
+def counter_traffic(workload, stage):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE record of this
+    kernel on this workload, while the GEMM sources are those the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tj = json.load(fh)
+    if tj.get("source_hash") != source_hash(GEMM_SOURCES):
+        return None
+    return tj.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs the layer on a "
               f"single MI355X and has no multi-GPU path", file=sys.stderr)
@@ -83,13 +162,13 @@ def main():
 
     dev = "cuda"
     w = wl.get_workload(args.workload)
+    print(f"[bench] {w.name}: drawing inputs", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed=args.seed, device=dev)
     cap = ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor)
     T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
-    # The library's regime rule: groups averaging >= 256 rows (R_max / E) that can reach 256
-    # rows (min(T, C)) run on the large-tile kernel, which reads tile-major copies when given.
     desc = ops.make_desc(T, d, f, E, k, cap, fs, w.torch_dtype)
-    large_tiles = ops.moe_max_rows(desc) // E >= 256 and (T if cap is None else min(T, cap)) >= 256
+    rmax = ops.moe_max_rows(desc)
+    large_tiles = big_regime(rmax, E, T if cap is None else min(T, cap))
     args.use_tiles = w.dtype == "bf16" and (args.tiled == "on" or (args.tiled == "auto" and large_tiles))
     # the shared expert, one group of all T tokens, takes the large-tile regime from 256 tokens
     args.use_shared_tiles = w.dtype == "bf16" and fs > 0 and (args.tiled == "on" or (args.tiled == "auto" and T >= 256))
@@ -100,17 +179,30 @@ def main():
     if args.backward:
         return backward_bench(args, w, inp, cap, layer, s_bytes)
 
-    # ---------------------------------------------------------------- whole-path timing
-    for _ in range(args.warmup):
+    scratch = torch.empty(max(args.flush_mib, 1) << 20, dtype=torch.uint8, device=dev)
+
+    def flush(i):
+        if args.flush_mib:
+            scratch.fill_(i & 0xFF)  # untimed: evicts x and the weights from the last-level cache
+
+    # ---------------------------------------------------------------- whole-layer timing
+    for i in range(args.warmup):
+        flush(i)
         layer.forward(with_routing=False)
     torch.cuda.synchronize()
+    print(f"[bench] {w.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i, (a, b) in enumerate(marks):
+        flush(i)
+        a.record()
         layer.forward(with_routing=False)
+        b.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = T * args.steps / (t1 - t0)
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in marks]
+    ms_per_step = statistics.median(step_ms)
+    tokens_per_s = T / (ms_per_step * 1e-3)
 
     # ---------------------------------------------------------------- routing facts of this batch
     layer.forward(with_routing=True)
@@ -120,127 +212,68 @@ def main():
     R = int(off[-1])
     E_t = int((kept > 0).sum())
 
-    # ---------------------------------------------------------------- per-stage HIP-event timing
-    # The same kernels as moe_forward, called stage by stage through the C ABI, with events on
-    # the stream the library launches on (torch's current stream).  As in moe_forward, the
-    # gate_up projection gathers token rows from x through row_token (no x_perm).
-    r = layer.routing
-    desc = layer.desc
-    Rmax = ops.moe_max_rows(desc)
-    hid = torch.empty((max(Rmax, 1), f), dtype=inp.x.dtype, device=dev)
-    y_perm = torch.empty((max(Rmax, 1), d), dtype=inp.x.dtype, device=dev)
-    out = torch.empty_like(inp.x)
-    grm = max(1, min(T, cap) if cap is not None else T)
-    stages = ["router_logits", "router_topk", "dispatch_permute", "gate_up_swiglu", "down", "combine"]
-    ev = {s: [] for s in stages}
-
-    def staged_step(record):
-        marks = []
-
-        def mark():
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record()
-                marks.append(e)
-
-        mark()
-        ops.moe_router_logits(desc, inp.x, inp.w_router, inp.logit_offset, r["logits"])
-        mark()
-        ops.moe_router_topk(desc, r["logits"], r["topk_ids"], r["topk_gates"])
-        mark()
-        ops.moe_dispatch_permute(desc, r["topk_ids"], None, r["expert_counts"], r["expert_offsets"], r["slot"],
-                                 r["row_token"], None, layer.ws)
-        mark()
-        ops.moe_grouped_gate_up_swiglu(E, Rmax, grm, d, f, inp.x.dtype, inp.x, r["expert_offsets"], inp.w_gate_up,
-                                       hid, row_index=r["row_token"])
-        mark()
-        ops.moe_grouped_down(E, Rmax, grm, d, f, inp.x.dtype, hid, r["expert_offsets"], inp.w_down, y_perm)
-        mark()
-        ops.moe_combine_unpermute(desc, y_perm, r["topk_ids"], r["topk_gates"], r["slot"], r["expert_offsets"], None,
-                                  out)
-        mark()
-        return marks
-
-    if fs:
-        # the shared expert: the same grouped GEMMs with one group of all T tokens
-        stages += ["shared_gate_up", "shared_down"]
-        ev.update({"shared_gate_up": [], "shared_down": []})
-        sh_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
-        sh_hid = torch.empty((T, fs), dtype=inp.x.dtype, device=dev)
-        sh_out = torch.empty_like(inp.x)
-
-    def staged_shared(marks, record):
-        def mark():
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record()
-                marks.append(e)
-        ops.moe_grouped_gate_up_swiglu(1, T, T, d, fs, inp.x.dtype, inp.x, sh_off, inp.w_shared_gate_up, sh_hid)
-        mark()
-        ops.moe_grouped_down(1, T, T, d, fs, inp.x.dtype, sh_hid, sh_off, inp.w_shared_down, sh_out)
-        mark()
-
-    for _ in range(args.warmup):
-        m = staged_step(False)
-        if fs:
-            staged_shared(m, False)
-    all_marks = []
-    for _ in range(args.steps):
-        m = staged_step(True)
-        if fs:
-            staged_shared(m, True)
-        all_marks.append(m)
+    # ---------------------------------------------------------------- per-stage timing of moe_forward's own launches
+    evsets = [ops.stage_events() for _ in range(args.steps)]
+    for i, evs in enumerate(evsets):
+        flush(i)
+        layer.forward_staged(evs)
     torch.cuda.synchronize()
-    for marks in all_marks:
-        for i, s in enumerate(stages):
-            ev[s].append(marks[i].elapsed_time(marks[i + 1]) * 1e3)  # us
-    stage_us = {s: float(np.mean(v)) for s, v in ev.items()}
+    per_stage = {s: [] for s in ops.STAGES}
+    for evs in evsets:
+        for i, s in enumerate(ops.STAGES):
+            per_stage[s].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)  # us
+    stage_us = {s: statistics.median(v) for s, v in per_stage.items()}
 
     # ---------------------------------------------------------------- roofline of the dominant kernel
-    gate_up_bytes = E_t * 2 * f * d * s_bytes + R * d * s_bytes + R * f * s_bytes
-    gate_up_flop = 2.0 * R * d * 2 * f
-    down_bytes = E_t * d * f * s_bytes + R * f * s_bytes + R * d * s_bytes
-    dom = "gate_up_swiglu"
-    dur = stage_us.get(dom)
-    roofline = None
-    if dur:
-        intensity = gate_up_flop / gate_up_bytes
-        peak_flops = (MFMA_BF16_PEAK_TFLOPS if s_bytes == 2 else MFMA_F32_PEAK_TFLOPS) * 1e12
-        ridge = peak_flops / (HBM_PEAK_GBS * 1e9)
-        if intensity < ridge:
-            achieved = gate_up_bytes / (dur * 1e-6) / 1e9
-            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        else:
-            achieved = gate_up_flop / (dur * 1e-6) / 1e12
-            peak = peak_flops / 1e12
-            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(achieved / peak, 4)}
-        roofline["kernel"] = "grouped_gemm_stream_kernel (gate_up + SwiGLU)" if grm <= 512 else "grouped gate_up GEMM"
-        roofline["avg_launch_us"] = round(dur, 2)
-        roofline["algorithmic_bytes"] = int(gate_up_bytes)
-        roofline["algorithmic_flop"] = int(gate_up_flop)
-        traffic = None
-        tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{args.workload}.json")
-        if os.path.exists(tfile):
-            with open(tfile) as fh:
-                tj = json.load(fh)
-            if tj.get("source_hash") == source_hash(DOMINANT_SOURCES):
-                traffic = tj.get("hbm_bytes_per_launch")
-        roofline["traffic"] = traffic
+    work = stage_work(w, R, E_t, kept.tolist(), T, s_bytes, cap, rmax)
+    dom = max(work, key=lambda s: stage_us[s])
+    roofline = roofline_of(work[dom], stage_us[dom], s_bytes)
+    roofline.update({"kernel": work[dom]["kernel"], "stage": dom, "avg_launch_us": round(stage_us[dom], 2),
+                     "launch_us_statistic": "median over the timed steps",
+                     "algorithmic_bytes": int(work[dom]["bytes"]), "algorithmic_flop": int(work[dom]["flop"]),
+                     "traffic": counter_traffic(w.name, dom)})
+    kernels = {}
+    for s, wk in work.items():
+        if stage_us[s] > 0:
+            r = roofline_of(wk, stage_us[s], s_bytes)
+            kernels[s] = {"us": round(stage_us[s], 2), "bound": r["bound"], "achieved": r["achieved"],
+                          "unit": r["unit"], "frac": r["frac"]}
 
-    # whole-layer algorithmic work (for context next to the kernel roofline)
+    # ---------------------------------------------------------------- whole layer and its phases
+    def rt(flop, nbytes):
+        return max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)) * 1e3  # ms
+
     flop = 2.0 * T * d * E + 6.0 * R * d * f + 6.0 * T * d * fs
     layer_bytes = s_bytes * (T * d + E * d + E_t * 3 * d * f + 3 * d * fs + T * d)
-    rt = max(flop / (MFMA_BF16_PEAK_TFLOPS * 1e12), layer_bytes / (HBM_PEAK_GBS * 1e9))
-    layer_roofline = {"algorithmic_flop": flop, "algorithmic_bytes": layer_bytes, "roofline_ms": round(rt * 1e3, 4),
-                      "frac_of_roofline": round(rt * 1e3 / ms_per_step, 4),
+    layer_rt = rt(flop, layer_bytes)
+    layer_roofline = {"algorithmic_flop": flop, "algorithmic_bytes": layer_bytes, "roofline_ms": round(layer_rt, 4),
+                      "frac_of_roofline": round(layer_rt / ms_per_step, 4),
                       "hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                       "mfma_frac": round(flop / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)}
+    phases = None
+    if fs:
+        shared_st = [s for s in ops.STAGES if s.startswith("shared_")]
+        routed_st = [s for s in ops.STAGES if s not in shared_st]
+        r_flop, r_bytes = 2.0 * T * d * E + 6.0 * R * d * f, s_bytes * (T * d + E * d + E_t * 3 * d * f + T * d)
+        s_flop, s_bytes_ = 6.0 * T * d * fs, s_bytes * 3 * d * fs
+        r_ms = sum(stage_us[s] for s in routed_st) / 1e3
+        s_ms = sum(stage_us[s] for s in shared_st) / 1e3
+        r_rt, s_rt = rt(r_flop, r_bytes), rt(s_flop, s_bytes_)
+        phases = {
+            "routed": {"stages": routed_st, "ms": round(r_ms, 4), "bound": "hbm" if r_flop / r_bytes < 312.5 else "mfma",
+                       "roofline_ms": round(r_rt, 4), "frac_of_roofline": round(r_rt / r_ms, 4),
+                       "algorithmic_bytes": r_bytes, "algorithmic_flop": r_flop},
+            "shared": {"stages": shared_st, "ms": round(s_ms, 4), "bound": "hbm" if s_flop / s_bytes_ < 312.5 else "mfma",
+                       "roofline_ms": round(s_rt, 4), "frac_of_roofline": round(s_rt / s_ms, 4),
+                       "algorithmic_bytes": s_bytes_, "algorithmic_flop": s_flop},
+            "phase_sum_roofline_ms": round(r_rt + s_rt, 4), "overlapped_roofline_ms": round(layer_rt, 4),
+            "step_frac_of_phase_sum_roofline": round((r_rt + s_rt) / ms_per_step, 4),
+        }
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
+        print(f"[bench] {w.name}: CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, cap, args.cpu_sample)
 
     line = {
@@ -260,8 +293,15 @@ def main():
                    "num_experts": E, "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap,
                    "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R),
                    "weight_layout": weight_layout(args)},
+        "timing": {"statistic": "median", "step_ms_min": round(min(step_ms), 4), "step_ms_max": round(max(step_ms), 4),
+                   "step_ms_mean": round(statistics.mean(step_ms), 4),
+                   "wall_ms_per_step_with_flush": round(wall * 1e3 / args.steps, 4),
+                   "method": f"HIP events around each moe_forward on the library's stream; an untimed "
+                             f"{args.flush_mib} MiB scratch write before every step"},
         "roofline": roofline,
+        "kernels": kernels,
         "layer_roofline": layer_roofline,
+        "phases": phases,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
         "cpu_baseline": cpu,
     }
@@ -434,7 +474,7 @@ def cpu_baseline(inp, cap, sample, min_seconds=10.0):
     import oracle
 
     w = inp.workload
-    sample = sample or {"switch_bf16": w.num_tokens, "tiny_f32": w.num_tokens}.get(w.name, 64)
+    sample = sample or CPU_SAMPLE.get(w.name, 64)
     sample = min(sample, w.num_tokens)
     h = lambda t: None if t is None else t.float().cpu().numpy()
     x, wr, off = h(inp.x), h(inp.w_router), h(inp.logit_offset)

@@ -332,6 +332,37 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
                        const float *logit_offset, void *out, moe_routing *routing, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Stages of moe_forward in launch order, as moe_forward_staged marks them. */
+typedef enum moe_stage {
+  MOE_STAGE_ROUTER = 0,                /* router linear and top-k (the next k ranks too when redirecting) */
+  MOE_STAGE_DISPATCH = 1,              /* capacity fill: counts, offsets, slots, row order */
+  MOE_STAGE_PACK_ROWS = 2,             /* large-tile regime: gathered x rows copied to the packed tile layout */
+  MOE_STAGE_GATE_UP = 3,               /* routed gate_up + SwiGLU grouped GEMM, main launch */
+  MOE_STAGE_GATE_UP_TAILS = 4,         /* large-tile regime: the groups' tail rows, streaming launch */
+  MOE_STAGE_DOWN = 5,                  /* routed down grouped GEMM, main launch (and its K-split sum) */
+  MOE_STAGE_DOWN_TAILS = 6,            /* large-tile regime: tail rows of the down projection */
+  MOE_STAGE_SHARED_PACK_ROWS = 7,      /* shared expert: its row offsets (large-tile regime), packed x rows */
+  MOE_STAGE_SHARED_GATE_UP = 8,        /* shared expert gate_up + SwiGLU, main launch */
+  MOE_STAGE_SHARED_GATE_UP_TAILS = 9,  /* shared expert: tail rows */
+  MOE_STAGE_SHARED_DOWN = 10,          /* shared expert down projection, main launch */
+  MOE_STAGE_SHARED_DOWN_TAILS = 11,    /* shared expert: tail rows of the down projection */
+  MOE_STAGE_COMBINE = 12,              /* gate-weighted combine into out */
+  MOE_NUM_STAGES = 13
+} moe_stage;
+
+/* moe_forward with HIP events recorded on `stream` between its launches, so that a caller
+ * can time each stage of the very launches moe_forward makes (same kernels, arguments and
+ * order; the records add only event markers to the stream).
+ *   stage_events  host array of MOE_NUM_STAGES + 1 events created by the caller (hipEventCreate,
+ *                 timing enabled): stage_events[0] is recorded before the first launch and
+ *                 stage_events[s + 1] after the launches of stage s; a stage that launches
+ *                 nothing (absent shared expert, streaming regime without tails, ...) ends where
+ *                 the previous one ended.  NULL entries: MOE_ERR_INVALID.
+ * Other arguments, results and errors as for moe_forward. */
+moe_status moe_forward_staged(const moe_desc *desc, const moe_weights *weights, const void *x,
+                              const float *logit_offset, void *out, moe_routing *routing, void *ws,
+                              size_t ws_bytes, hipStream_t stream, hipEvent_t *stage_events);
+
 /* Weight gradients of moe_backward (device pointers). */
 typedef struct moe_grads {
   void *dw_router;         /* [E, d] float */

@@ -278,12 +278,54 @@ moe_status check_projection(int32_t G, int64_t rows_max, int32_t group_rows_max,
   return check_dtype_dims(dtype, d, f, 0);
 }
 
+// Events of moe_forward_staged: ev[0] before the first launch, ev[s + 1] after the launches of
+// stage s (moe_stage order).  A stage that launches nothing ends where the previous one did.
+struct StageMarks {
+  hipEvent_t *ev = nullptr;
+  hipStream_t stream = nullptr;
+  int next = 0;  // first stage whose end is not yet recorded
+  hipError_t err = hipSuccess;
+  void start() {
+    if (ev && err == hipSuccess) err = hipEventRecord(ev[0], stream);
+  }
+  void end(int stage) {
+    if (!ev) return;
+    for (; next <= stage; ++next)
+      if (err == hipSuccess) err = hipEventRecord(ev[next + 1], stream);
+  }
+};
+
+void mark_end(StageMarks *m, int stage) {
+  if (m) m->end(stage);
+}
+
+// The stages of one grouped FFN (routed experts or the shared expert) as moe_stage values.
+struct FfnStages {
+  int pack, gate_up, gate_up_tails, down, down_tails;
+};
+constexpr FfnStages kRoutedStages{MOE_STAGE_PACK_ROWS, MOE_STAGE_GATE_UP, MOE_STAGE_GATE_UP_TAILS, MOE_STAGE_DOWN,
+                                  MOE_STAGE_DOWN_TAILS};
+constexpr FfnStages kSharedStages{MOE_STAGE_SHARED_PACK_ROWS, MOE_STAGE_SHARED_GATE_UP,
+                                  MOE_STAGE_SHARED_GATE_UP_TAILS, MOE_STAGE_SHARED_DOWN,
+                                  MOE_STAGE_SHARED_DOWN_TAILS};
+
+struct AfterMain {
+  StageMarks *marks;
+  int stage;
+  static void call(void *ctx) {
+    auto *a = static_cast<AfterMain *>(ctx);
+    mark_end(a->marks, a->stage);
+  }
+};
+
 moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, int32_t d, int32_t f, int32_t dtype,
                            const void *x_rows, const int32_t *offsets, const void *w_gate_up, const void *w_down,
                            void *y_rows, void *hidden, hipStream_t s, const int32_t *row_index = nullptr,
                            int64_t x_row_count = 0, float *split_ws = nullptr, void *x_packed = nullptr,
                            void *hidden_tail = nullptr, const void *w_gate_up_tiled = nullptr,
-                           const void *w_down_tiled = nullptr) {
+                           const void *w_down_tiled = nullptr, StageMarks *marks = nullptr,
+                           const FfnStages &st = kRoutedStages) {
+  AfterMain gu_main{marks, st.gate_up}, dn_main{marks, st.down};
   if (hidden_tail && dtype == MOE_DTYPE_BF16 && moe::grouped_gemm_big_regime(rows_max, G, group_rows_max)) {
     // Large-tile regime: the gate_up projection writes H in the packed tile layout, so that
     // every stage of the down projection loads one contiguous 16 KB block; with x_packed the
@@ -295,6 +337,7 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     const bool pack_x = x_packed != nullptr;
     if (pack_x)
       MOE_TRY_HIP(moe::launch_pack_rows(x_rows, row_index, offsets, G, rows_max, d, x_packed, s, tail), "pack x rows");
+    mark_end(marks, st.pack);
     moe::GroupedGemmArgs gu = pack_x ? projection_args(G, rows_max, group_rows_max, d, f, x_packed, offsets, w_gate_up,
                                                        hidden, true, nullptr, xb)
                                      : projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up,
@@ -307,7 +350,10 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     gu.tail_a_rows = row_index ? x_row_count : rows_max;
     gu.tail_out = hidden_tail;
     gu.W_packed = w_gate_up_tiled;
+    gu.after_main = AfterMain::call;
+    gu.after_main_ctx = &gu_main;
     MOE_TRY(run_projection(gu, dtype, s, "gate_up grouped GEMM"));
+    mark_end(marks, st.gate_up_tails);
     moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows,
                                                 false, nullptr, hb);
     down.a_packed = true;
@@ -316,15 +362,24 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     down.tail_a_rows = rows_max;
     down.split_ws = split_ws;
     down.W_packed = w_down_tiled;
+    down.after_main = AfterMain::call;
+    down.after_main_ctx = &dn_main;
     MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
+    mark_end(marks, st.down_tails);
     return MOE_OK;
   }
-  MOE_TRY(run_projection(projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden, true,
-                                         row_index, x_row_count),
-                         dtype, s, "gate_up grouped GEMM"));
+  moe::GroupedGemmArgs gu = projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden,
+                                            true, row_index, x_row_count);
+  gu.after_main = AfterMain::call;
+  gu.after_main_ctx = &gu_main;
+  MOE_TRY(run_projection(gu, dtype, s, "gate_up grouped GEMM"));
+  mark_end(marks, st.gate_up_tails);
   moe::GroupedGemmArgs down = projection_args(G, rows_max, group_rows_max, d, f, hidden, offsets, w_down, y_rows, false);
   down.split_ws = split_ws;  // lets the large-tile kernel cut few tiles along K
+  down.after_main = AfterMain::call;
+  down.after_main_ctx = &dn_main;
   MOE_TRY(run_projection(down, dtype, s, "down grouped GEMM"));
+  mark_end(marks, st.down_tails);
   return MOE_OK;
 }
 
@@ -604,7 +659,7 @@ namespace {
 // contributions, plus the shared expert when add_shared.
 moe_status forward_range(const moe_desc &D, const moe_weights *weights, const void *x, const float *logit_offset,
                          void *out, moe_routing *routing, void *ws, size_t ws_bytes, hipStream_t stream,
-                         int32_t e_begin, int32_t e_end, bool add_shared) {
+                         int32_t e_begin, int32_t e_end, bool add_shared, StageMarks *marks = nullptr) {
   if (!weights) return fail(MOE_ERR_INVALID, "weights is NULL");
   if (D.num_tokens == 0) return ok();
   MOE_TRY(check_ptr(x, "x"));
@@ -651,6 +706,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
   const int64_t rmax = max_rows(D);
   void *y_perm = at<void>(ws, L.y_perm);
 
+  if (marks) marks->start();
   if (!bf)
     MOE_TRY_HIP(moe::launch_router_logits_f32(static_cast<const float *>(x),
                                               static_cast<const float *>(weights->w_router), logit_offset, logits, T,
@@ -670,12 +726,14 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
     int32_t *spare = at<int32_t>(ws, L.spare);
     int32_t *assigned = R.assigned_ids ? R.assigned_ids : at<int32_t>(ws, L.assigned);
     MOE_TRY(router(spare));
+    mark_end(marks, MOE_STAGE_ROUTER);
     MOE_TRY_HIP(moe::launch_dispatch_reroute(ids, spare, T, k, E, D.capacity, rank_major, counts, offsets, slot,
                                              assigned, row_token, at<int32_t>(ws, L.hist), stream),
                 "dispatch with redirection");
     serving = assigned;
   } else {
     MOE_TRY(router(nullptr));
+    mark_end(marks, MOE_STAGE_ROUTER);
     MOE_TRY_HIP(moe::launch_dispatch(ids, T, k, E, D.capacity, rank_major, counts, offsets, slot, row_token,
                                      at<int32_t>(ws, L.hist), stream),
                 "dispatch");
@@ -683,6 +741,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
       MOE_TRY_HIP(hipMemcpyAsync(R.assigned_ids, ids, (size_t)T * k * 4, hipMemcpyDeviceToDevice, stream),
                   "assigned ids");
   }
+  mark_end(marks, MOE_STAGE_DISPATCH);
   if (rmax > 0 && any_local) {
     // the gate_up projection gathers each expert's token rows from x through row_token,
     // so the permuted copy of x is never materialised; a range of experts is the slice
@@ -692,7 +751,7 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
                             stream, row_token, T, down_split_bytes(D) ? at<float>(ws, L.down_split) : nullptr,
                             packable(D) && pack_rows_wins(f) ? at<void>(ws, L.x_packed) : nullptr,
                             packable(D) ? at<void>(ws, L.hidden_tail) : nullptr, weights->w_gate_up_tiled,
-                            weights->w_down_tiled));
+                            weights->w_down_tiled, marks, kRoutedStages));
   }
   const void *shared = nullptr;
   if (fs > 0 && add_shared) {
@@ -703,12 +762,16 @@ moe_status forward_range(const moe_desc &D, const moe_weights *weights, const vo
                             at<void>(ws, L.sh_out), at<void>(ws, L.sh_hidden), stream, nullptr, 0, nullptr,
                             sp && pack_rows_wins(fs) ? at<void>(ws, L.sh_x_packed) : nullptr,
                             sp ? at<void>(ws, L.sh_hidden_tail) : nullptr,
-                            weights->w_shared_gate_up_tiled, weights->w_shared_down_tiled));
+                            weights->w_shared_gate_up_tiled, weights->w_shared_down_tiled, marks,
+                            kSharedStages));
     shared = at<void>(ws, L.sh_out);
   }
+  mark_end(marks, MOE_STAGE_SHARED_DOWN_TAILS);
   MOE_TRY_HIP(moe::launch_combine(y_perm, serving, gates, slot, offsets, shared, out, T, d, k, bf, stream, e_begin,
                                   any_local ? e_end : e_begin),
               "combine");
+  mark_end(marks, MOE_STAGE_COMBINE);
+  if (marks && marks->err != hipSuccess) return hip_status(marks->err, "stage event record");
   return ok();
 }
 
@@ -721,6 +784,25 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
   MOE_TRY(check_desc(desc));
   return forward_range(*desc, weights, x, logit_offset, out, routing, ws, ws_bytes, stream, 0, desc->num_experts,
                        true);
+}
+
+moe_status moe_forward_staged(const moe_desc *desc, const moe_weights *weights, const void *x,
+                              const float *logit_offset, void *out, moe_routing *routing, void *ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t *stage_events) {
+  MOE_TRY(check_desc(desc));
+  if (!stage_events) return fail(MOE_ERR_INVALID, "stage_events is NULL");
+  for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+    if (!stage_events[i]) return fail(MOE_ERR_INVALID, "stage_events[%d] is NULL", i);
+  StageMarks marks;
+  marks.ev = stage_events;
+  marks.stream = stream;
+  if (desc->num_tokens == 0) {  // nothing to launch: every stage is empty
+    marks.start();
+    marks.end(MOE_NUM_STAGES - 1);
+    if (marks.err != hipSuccess) return hip_status(marks.err, "stage event record");
+  }
+  return forward_range(*desc, weights, x, logit_offset, out, routing, ws, ws_bytes, stream, 0, desc->num_experts,
+                       true, &marks);
 }
 
 size_t moe_tiled_weights_bytes(const moe_desc *desc, int32_t num_experts, int32_t which) {

@@ -804,7 +804,9 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a0, int64_t rows_
   if (a.tail != 0 && a.tail != kBigTailRows) return hipErrorInvalidValue;
   if (a.tail && ((a.a_packed && !a.tail_A) || (a.out_packed && !a.tail_out))) return hipErrorInvalidValue;
   hipError_t e = launch_big_tiles(a, rows_total_max, s);
-  if (e != hipSuccess || !a.tail) return e;
+  if (e != hipSuccess) return e;
+  if (a.after_main) a.after_main(a.after_main_ctx);
+  if (!a.tail) return e;
   GroupedGemmArgs t = a;
   t.tails_only = true;
   t.group_rows_max = std::min(a.group_rows_max, kBigTailRows);

@@ -110,6 +110,10 @@ struct GroupedGemmArgs {
   // large-tile kernel then reads them with the packed activations or the SwiGLU backward
   // epilogue; the streaming kernel (tails included) reads W.
   const void *W_packed = nullptr;
+  // Called on the host after the large-tile launch (and its K-split sum) is enqueued,
+  // before the tail launch: lets the caller mark the stream between the two.
+  void (*after_main)(void *ctx) = nullptr;
+  void *after_main_ctx = nullptr;
 };
 
 // Large-tile row tiles and the tail rows left to the streaming kernel.

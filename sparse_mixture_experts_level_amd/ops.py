@@ -32,8 +32,12 @@ SYMBOLS = [
     "moe_dispatch_permute", "moe_dispatch_reroute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
     "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
     "moe_backward_workspace_size", "moe_backward", "moe_tiled_weights_bytes", "moe_tile_expert_weights",
-    "moe_check_topk_ids", "moe_debug_checks",
+    "moe_check_topk_ids", "moe_debug_checks", "moe_forward_staged",
 ]
+
+# moe_stage: the stages moe_forward_staged marks, in launch order
+STAGES = ["router", "dispatch", "pack_rows", "gate_up", "gate_up_tails", "down", "down_tails", "shared_pack_rows",
+          "shared_gate_up", "shared_gate_up_tails", "shared_down", "shared_down_tails", "combine"]
 
 
 class MoEError(RuntimeError):
@@ -118,6 +122,9 @@ def _load(path: str) -> ctypes.CDLL:
     L.moe_router_aux_loss.restype = st
     L.moe_forward.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward.restype = st
+    L.moe_forward_staged.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz,
+                                     vp, ctypes.POINTER(vp)]
+    L.moe_forward_staged.restype = st
     L.moe_forward_expert_shard.argtypes = [dp, ctypes.POINTER(MoeWeights), i32, i32, i32, vp, vp, vp,
                                            ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward_expert_shard.restype = st
@@ -334,6 +341,32 @@ def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, rou
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
 
 
+def stage_events():
+    """MOE_NUM_STAGES + 1 timing events for moe_forward_staged (torch events, created by
+    recording them once on the current stream)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+    for e in evs:
+        e.record()
+    return evs
+
+
+def moe_forward_staged(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, events,
+                       routing: Optional[dict] = None, w_shared_gate_up=None, w_shared_down=None, stream=None,
+                       tiled=None, shared_tiled=None) -> None:
+    """moe_forward with events[s + 1] recorded after stage s (events from stage_events())."""
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled, shared_tiled)
+    R = None
+    if routing is not None:
+        R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
+    if len(events) != len(STAGES) + 1:
+        raise ValueError(f"moe_forward_staged needs {len(STAGES) + 1} events")
+    evs = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check(lib().moe_forward_staged(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(logit_offset), _ptr(out),
+                                    ctypes.byref(R) if R is not None else None, _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream), evs),
+           "moe_forward_staged")
+
+
 def moe_forward_expert_shard(desc, w_router, w_gate_up_local, w_down_local, expert_begin, expert_end, add_shared, x,
                              logit_offset, out_partial, ws, routing: Optional[dict] = None, w_shared_gate_up=None,
                              w_shared_down=None, stream=None, tiled=None, shared_tiled=None) -> None:
@@ -393,6 +426,14 @@ class MoELayer:
         self.tiled = tiled_weights(self.desc, inputs.w_gate_up, inputs.w_down) if tiled else None
         self.shared_tiled = (tiled_shared_weights(self.desc, inputs.w_shared_gate_up, inputs.w_shared_down)
                              if shared_tiled and w.d_ff_shared else None)
+
+    def forward_staged(self, events, with_routing=False, stream=None):
+        i = self.inputs
+        moe_forward_staged(self.desc, i.w_router, i.w_gate_up, i.w_down, i.x, i.logit_offset, self.out, self.ws,
+                           events, routing=self.routing if with_routing else None,
+                           w_shared_gate_up=i.w_shared_gate_up, w_shared_down=i.w_shared_down, stream=stream,
+                           tiled=self.tiled, shared_tiled=self.shared_tiled)
+        return self.out
 
     def forward(self, with_routing=True, stream=None):
         i = self.inputs

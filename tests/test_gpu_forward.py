@@ -141,6 +141,39 @@ def test_forward_is_deterministic():
         assert torch.equal(ra[k], layer.routing[k]), k
 
 
+@pytest.mark.parametrize("T,d,E,k,f,cf,fs,tiled", [
+    (2048, 256, 16, 2, 128, 1.0, 0, False),     # streaming regime, no shared expert
+    (1100, 256, 8, 2, 128, 1.25, 576, False),   # shared expert on large tiles with a streamed tail
+    (2400, 4096, 8, 1, 4096, None, 0, True),    # packed large tiles, tile-major weights, streamed tails
+])
+def test_staged_forward_is_the_forward(T, d, E, k, f, cf, fs, tiled):
+    """moe_forward_staged launches what moe_forward launches: bitwise equal output and routing;
+    its events are ordered and stages that launch nothing take (almost) no time."""
+    w = wl.Workload("staged", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset="boost4")
+    say(f"staged forward T={T} d={d} E={E} k={k} f={f} fs={fs} tiled={tiled}")
+    inp = wl.make_inputs(w, seed=4, device=DEV)
+    cap = ops.moe_capacity(T, E, cf)
+    layer = ops.MoELayer(inp, cap, tiled=tiled, shared_tiled=bool(fs))
+    a = layer.forward().clone()
+    ra = {n: v.clone() for n, v in layer.routing.items()}
+    evs = ops.stage_events()
+    layer.out.zero_()
+    b = layer.forward_staged(evs, with_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for n in ra:
+        assert torch.equal(ra[n], layer.routing[n]), n
+    us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(len(ops.STAGES))]
+    st = dict(zip(ops.STAGES, us))
+    say("  " + ", ".join(f"{n} {v:.1f}" for n, v in st.items()))
+    assert all(v >= 0 for v in us)
+    assert st["router"] > 0 and st["dispatch"] > 0 and st["gate_up"] > 0 and st["down"] > 0 and st["combine"] > 0
+    if not fs:  # back-to-back event records only
+        assert st["shared_gate_up"] < 30 and st["shared_down"] < 30
+    else:
+        assert st["shared_gate_up"] > 0 and st["shared_down"] > 0
+
+
 FULL = [("switch_bf16", 48), ("mixtral_bf16", 24), ("gptoss_decode_bf16", None), ("deepseek_v3_bf16", 12)]
 
 
