@@ -368,6 +368,7 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
     mark_end(marks, st.down_tails);
     return MOE_OK;
   }
+  mark_end(marks, st.pack);  // no row packing in this regime
   moe::GroupedGemmArgs gu = projection_args(G, rows_max, group_rows_max, d, f, x_rows, offsets, w_gate_up, hidden,
                                             true, row_index, x_row_count);
   gu.after_main = AfterMain::call;

@@ -168,6 +168,8 @@ def test_staged_forward_is_the_forward(T, d, E, k, f, cf, fs, tiled):
     say("  " + ", ".join(f"{n} {v:.1f}" for n, v in st.items()))
     assert all(v >= 0 for v in us)
     assert st["router"] > 0 and st["dispatch"] > 0 and st["gate_up"] > 0 and st["down"] > 0 and st["combine"] > 0
+    if not tiled:  # no row packing: the gate_up kernel's time is its own stage's
+        assert st["pack_rows"] < 30 and st["gate_up"] > st["pack_rows"]
     if not fs:  # back-to-back event records only
         assert st["shared_gate_up"] < 30 and st["shared_down"] < 30
     else:
