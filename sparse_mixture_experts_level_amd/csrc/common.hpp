@@ -53,6 +53,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_bytes
 __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// The same load marked non-temporal (cache policy bit nt): for data read once, such as
+// streamed expert weights.  A plain read of a 4 GiB buffer measured 6.7 TB/s with it against
+// 6.0 TB/s without on this GPU.
+constexpr int kCpolNt = 2;
+__device__ __forceinline__ u32x4 buf_ld16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNt);
+}
 // 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
 // lds_wave_base + 16 * i (lds_wave_base must be equal across the wavefront).
 __device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t off, void *lds_wave_base) {

@@ -10,8 +10,14 @@
 // Workgroup = 4 wavefronts = one (expert, column tile).  Each wave owns NSUB
 // 16-column output subtiles; with SwiGLU it loads the matching gate rows and up
 // rows (W rows n and n + n_out) so both accumulators of a column sit in the same
-// lane.  Weight rows go straight from HBM into MFMA B-operand registers (16 bytes
-// per lane per subtile and 32-wide k step).  The expert's token rows (A operand,
+// lane.  Weight rows come from HBM as whole 128-byte lines (one load instruction: 8 rows
+// x 128 bytes of a 64-wide K chunk) marked non-temporal -- each weight byte is read once
+// -- into registers, and pass through a small wave-private LDS region into the MFMA
+// B-operand layout (16 rows x 64 bytes per 32-wide k step).  Loading the operand layout
+// directly splits every line over two instructions; non-temporal loads then fetch each
+// line twice, and without the hint the stream reads slower (measured on this GPU: 7.0
+// TB/s for whole lines with the hint, 6.25 TB/s for the operand layout without it, 5.3
+// TB/s with it).  The expert's token rows (A operand,
 // reused by every column tile of the expert) go straight from memory into LDS with
 // buffer loads that target LDS (no registers), in 64-wide K chunks, XOR-swizzled by
 // row so the 16-lane column reads of the MFMA layout spread over distinct banks.
@@ -78,7 +84,8 @@ __device__ __forceinline__ u32x4 wt_frag(const uint8_t *tile, int s, int wave, i
 template <int BM, int NSUB, bool SWIGLU, int S, int NW, int NA, typename OutT, bool WT, bool GB>
 __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t ares, const uint32_t *boff,
                                              const uint32_t *aoff, uint8_t *sA0, uint8_t *sA1, uint8_t *sA2,
-                                             uint8_t *sA3, uint8_t *const *sW, int nk, int rows, int m0, int ncol0,
+                                             uint8_t *sA3, uint8_t *const *sW, uint8_t *sWt, uint32_t hrow,
+                                             int nk, int rows, int m0, int ncol0,
                                              int nvalid, int n_out, OutT *__restrict__ out, const SwigluBwdOut &gb) {
   static_assert(S == 3 || S == 4, "three or four stages");
   static_assert(!WT || (NSUB == 1 && NW == 4 && !SWIGLU), "K-major weights: one 64-column tile of four waves");
@@ -100,7 +107,15 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 #pragma unroll
       for (int p = 0; p < 2; ++p)
         buf_ld16_lds(wres, boff[p] == kOob ? kOob : boff[p] + (uint32_t)c * wchunk, sW[sl] + (wave * 2 + p) * 1024);
+    } else if constexpr (!GB) {
+      // rows 8 h + lane / 8 of each subtile, 16-byte piece lane % 8 of the chunk's 128 bytes
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) slot[sl][h][b] = buf_ld16_nt(wres, boff[b] + kc + (uint32_t)h * hrow);
     } else {
+      // the SwiGLU backward's recompute (whose epilogue needs the registers): the MFMA operand
+      // layout loaded directly, rows lane % 16, 16-byte piece 4 s + lane / 16
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -115,6 +130,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
   for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 bw[2][NB];  // row-major weights: this step's B fragments (see to_frags)
   auto compute = [&](int sl) {
     const uint8_t *st = stage(sl);
 #pragma unroll
@@ -136,8 +152,34 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
 #pragma unroll
         for (int i = 0; i < MS; ++i)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], slot[sl][s][b], acc[i][b]);
+          for (int b = 0; b < NB; ++b) acc[i][b] = mfma16(a[i], GB ? slot[sl][s][b] : bw[s][b], acc[i][b]);
       }
+    }
+  };
+  // Whole-line weight pieces -> MFMA B fragments through the wave's LDS region: subtile b
+  // is 16 rows x 128 bytes, 16-byte piece c of row r stored at piece c ^ (r & 7) (eight
+  // consecutive lanes write one row, or read eight rows at one logical piece, on distinct
+  // banks).  Fragment of k step s: column lane % 16 (row of the subtile), k = 32 s +
+  // 8 (lane / 16) .. + 7, i.e. piece 4 s + lane / 16.  The wave's LDS operations complete
+  // in order, so a region is rewritten only after its earlier reads.
+  auto to_frags = [&](int sl) {
+    if constexpr (!WT && !GB) {
+      uint8_t *wl = sWt + wave * (NB * 2048);
+      const int wr = lane >> 3;  // row of the subtile written by this lane, minus 8 h
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int r = 8 * h + wr;
+          *reinterpret_cast<u32x4 *>(wl + b * 2048 + r * 128 + (((lane & 7) ^ (r & 7)) << 4)) = slot[sl][h][b];
+        }
+      const int rr = lane & 15;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          bw[s2][b] = *reinterpret_cast<const u32x4 *>(wl + b * 2048 + rr * 128 +
+                                                        ((((4 * s2) + (lane >> 4)) ^ (rr & 7)) << 4));
     }
   };
   auto bar = [&]() {
@@ -159,6 +201,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * LOADS) : "memory");
       bar();
       issue((s + S - 1) % S, c0 + s + S - 1);
+      to_frags(s);
       compute(s);
     }
   }
@@ -170,6 +213,7 @@ __device__ __forceinline__ void stream_block(const rsrc_t wres, const rsrc_t are
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     bar();
     if (c + S - 1 < nk) issue((s + S - 1) % S, c + S - 1);
+    to_frags(s % S);
     compute(s % S);
   }
   // no LDS write may outlive the block, and the next row block refills the stages
@@ -287,6 +331,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
   __shared__ __attribute__((aligned(1024))) uint8_t sW0[WSTAGE], sW1[WSTAGE], sW2[WSTAGE],
       sW3[S > 3 ? WSTAGE : 16];
   uint8_t *const sW[4] = {sW0, sW1, sW2, sW3};
+  // row-major weights: each wave's region for turning whole-line pieces into MFMA fragments
+  __shared__ __attribute__((aligned(1024))) uint8_t sWt[WT || GB ? 16 : NW * NB * 2048];
 
   const int tile = blockIdx.x;
   const int g = tile / n_tiles, nt = tile - g * n_tiles;
@@ -316,12 +362,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
       boff[p] = col < n_out ? ((uint32_t)r * (uint32_t)n_out + (uint32_t)col) * 2u : kOob;
     }
   } else {
-    // byte offset of this lane's 16 bytes in weight subtile b at k = 0
+    // byte offset of this lane's 16 bytes in weight subtile b at k = 0 (rows 0 .. 7 of it)
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int sidx = b % NSUB;
-      const int r = ncol0 + sidx * 16 + (lane & 15) + (b >= NSUB ? n_out : 0);
-      boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane >> 4) * 16u : kOob;
+      if constexpr (GB) {  // MFMA operand layout: row lane % 16, piece lane / 16
+        const int r = ncol0 + sidx * 16 + (lane & 15) + (b >= NSUB ? n_out : 0);
+        boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane >> 4) * 16u : kOob;
+      } else {  // whole lines: row lane / 8 (+ 8 h, hrow bytes further), piece lane % 8
+        const int r = ncol0 + sidx * 16 + (lane >> 3) + (b >= NSUB ? n_out : 0);
+        boff[b] = sidx < nvalid ? (uint32_t)r * kbytes + (uint32_t)(lane & 7) * 16u : kOob;
+      }
     }
   }
   const int nk = K / SG_KC;
@@ -349,7 +400,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void grouped_gemm_stream_
 #define SG_BLOCK(N)                                                                                              \
   if constexpr (N <= A_PER_T) {                                                                                  \
     if (na == N) {                                                                                               \
-      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT, WT, GB>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, sW, nk, rows, \
+      stream_block<BM, NSUB, SWIGLU, S, NW, N, OutT, WT, GB>(wres, ares, boff, aoff, sA0, sA1, sA2, sA3, sW, sWt,     \
+                                                         8u * kbytes, nk, rows,                                    \
                                                          m0, ncol0, nvalid, n_out, out, gb);                      \
       continue;                                                                                                  \
     }                                                                                                            \
