@@ -332,6 +332,26 @@ moe_status moe_forward(const moe_desc *desc, const moe_weights *weights, const v
                        const float *logit_offset, void *out, moe_routing *routing, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the fixed scratch array behind moe_forward_noalloc (per GPU). */
+#define MOE_NOALLOC_WORKSPACE_BYTES (128u << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation: moe_forward with its workspace taken
+ * from a fixed array of MOE_NOALLOC_WORKSPACE_BYTES that the library holds on each GPU it
+ * runs on (until the process ends), instead of a caller workspace.  No allocation: the
+ * call neither allocates nor frees device memory.  Layers whose moe_workspace_size
+ * exceeds MOE_NOALLOC_WORKSPACE_BYTES fail with MOE_ERR_WORKSPACE before any launch (e.g.
+ * decode steps and Switch-style layers fit; the Mixtral- and DeepSeek-shaped layers do
+ * not).  Every call on one GPU uses that GPU's one array: calls that overlap in time on
+ * the same GPU (different streams or threads without ordering) race and give undefined
+ * results; calls ordered on one stream are fine.  Nothing in the array has to start at
+ * zero (every kernel writes what it reads back).  The first call on a device resolves
+ * that device's array address with that device current.  Arguments, results and other
+ * errors as for moe_forward. */
+moe_status moe_forward_noalloc(const moe_desc *desc, const moe_weights *weights, const void *x,
+                               const float *logit_offset, void *out, moe_routing *routing,
+                               hipStream_t stream);
+
 /* Stages of moe_forward in launch order, as moe_forward_staged marks them. */
 typedef enum moe_stage {
   MOE_STAGE_ROUTER = 0,                /* router linear and top-k (the next k ranks too when redirecting) */

@@ -387,6 +387,11 @@ moe_status run_grouped_ffn(int32_t G, int64_t rows_max, int32_t group_rows_max, 
 
 }  // namespace
 
+namespace moe {
+// Failure with a message, for entry points defined in other files of the library.
+moe_status api_fail(moe_status st, const char *what, const char *detail) { return fail(st, "%s: %s", what, detail); }
+}  // namespace moe
+
 extern "C" {
 
 int32_t moe_capacity(int32_t num_tokens, int32_t num_experts, double capacity_factor) {

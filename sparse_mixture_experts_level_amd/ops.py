@@ -32,8 +32,9 @@ SYMBOLS = [
     "moe_dispatch_permute", "moe_dispatch_reroute", "moe_grouped_swiglu_gemm", "moe_grouped_gate_up_swiglu", "moe_grouped_down",
     "moe_combine_unpermute", "moe_router_aux_loss", "moe_forward", "moe_forward_expert_shard",
     "moe_backward_workspace_size", "moe_backward", "moe_tiled_weights_bytes", "moe_tile_expert_weights",
-    "moe_check_topk_ids", "moe_debug_checks", "moe_forward_staged",
+    "moe_check_topk_ids", "moe_debug_checks", "moe_forward_staged", "moe_forward_noalloc",
 ]
+MOE_NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 # moe_stage: the stages moe_forward_staged marks, in launch order
 STAGES = ["router", "dispatch", "pack_rows", "gate_up", "gate_up_tails", "down", "down_tails", "shared_pack_rows",
@@ -125,6 +126,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.moe_forward_staged.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp, sz,
                                      vp, ctypes.POINTER(vp)]
     L.moe_forward_staged.restype = st
+    L.moe_forward_noalloc.argtypes = [dp, ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeRouting), vp]
+    L.moe_forward_noalloc.restype = st
     L.moe_forward_expert_shard.argtypes = [dp, ctypes.POINTER(MoeWeights), i32, i32, i32, vp, vp, vp,
                                            ctypes.POINTER(MoeRouting), vp, sz, vp]
     L.moe_forward_expert_shard.restype = st
@@ -339,6 +342,19 @@ def moe_forward(desc, w_router, w_gate_up, w_down, x, logit_offset, out, ws, rou
     _check(lib().moe_forward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(logit_offset), _ptr(out),
                              ctypes.byref(R) if R is not None else None, _ptr(ws),
                              0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(desc, w_router, w_gate_up, w_down, x, logit_offset, out, routing: Optional[dict] = None,
+                        w_shared_gate_up=None, w_shared_down=None, stream=None, tiled=None,
+                        shared_tiled=None) -> None:
+    """moe_forward with the library's fixed per-GPU scratch array as its workspace."""
+    W = _weights(w_router, w_gate_up, w_down, w_shared_gate_up, w_shared_down, tiled, shared_tiled)
+    R = None
+    if routing is not None:
+        R = MoeRouting(*(_ptr(routing.get(n)) for n, _ in MoeRouting._fields_))
+    _check(lib().moe_forward_noalloc(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(logit_offset), _ptr(out),
+                                     ctypes.byref(R) if R is not None else None, _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def stage_events():
