@@ -42,12 +42,12 @@ constexpr int BG_BM = kBigTileRows, BG_BN = 256;
 // launches of fewer tiles than CUs: the split count (at most 4, at least 64 steps per
 // split) whose blocks fill the 256 CUs' last round best, the larger one on a tie.
 // Evaluated identically by the GEMM and by the reduction that adds the splits.
-__host__ __device__ __forceinline__ int big_ksplit(int tiles, int steps) {
+__host__ __device__ __forceinline__ int big_ksplit(int tiles, int steps, int min_steps = 64) {
   if (tiles <= 0 || tiles >= 256) return 1;
   int best = 1;
   float best_fill = 0.f;
   for (int s = 1; s <= 4; ++s) {
-    if (s > 1 && steps / s < 64) break;
+    if (s > 1 && steps / s < min_steps) break;
     const int blocks = tiles * s;
     const float fill = (float)blocks / (float)(((blocks + 255) / 256) * 256);
     if (fill >= best_fill) {
@@ -57,6 +57,10 @@ __host__ __device__ __forceinline__ int big_ksplit(int tiles, int steps) {
   }
   return best;
 }
+
+// The router linear on this kernel (one group of M rows, no offsets array): splits of at
+// least this many 32-wide steps; the router's top-k kernel adds the float partials.
+constexpr int kRouterMinSteps = 32;
 
 // Sum of the K splits' float partials in order, rounded to bf16, for the rows below
 // offsets[G]; nothing to do when the launch was not split.
@@ -158,8 +162,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     // its float partial sums to split_out + ks * split_stride, and a reduction adds them.
     // Tiles of at most `tail` rows (a group's last partial tile) are left to a streaming
     // launch: they do not exist here.
-    const int tiles = __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G, tail)) * n_tiles;
-    const int ksplit = split_out ? big_ksplit(tiles, K / BK) : 1;
+    // Without an offsets array (the router linear): one group of rows [0, M).
+    const bool one = offsets == nullptr;
+    const int tiles =
+        (one ? (M + BG_BM - 1) / BG_BM : __builtin_amdgcn_readfirstlane(total_row_blocks<BG_BM>(offsets, G, tail))) *
+        n_tiles;
+    const int ksplit = split_out ? big_ksplit(tiles, K / BK, one ? kRouterMinSteps : 64) : 1;
     const int real_blocks = tiles * ksplit;
     if ((int)blockIdx.x >= real_blocks) return;
     const int lin0 = xcd_remap(blockIdx.x, real_blocks);
@@ -169,7 +177,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     int g, mt_first, mt_count;
     // Blocks are numbered group-major: the tiles of group g occupy [mt_first * n_tiles,
     // (mt_first + mt_count) * n_tiles).  Within a group the order is chosen below.
-    find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count, tail);
+    if (one) {
+      g = 0;
+      mt_first = 0;
+      mt_count = (M + BG_BM - 1) / BG_BM;
+    } else {
+      find_row_block<BG_BM>(offsets, G, m_lin, g, mt_first, mt_count, tail);
+    }
     // the scan's results are equal in every lane: keep them (and all that derives from
     // them, like the buffer resources) in scalar registers
     g = __builtin_amdgcn_readfirstlane(g);
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     mt_count = __builtin_amdgcn_readfirstlane(mt_count);
     if (g < 0) return;
     const int local = lin - mt_first * n_tiles;  // 0 .. mt_count * n_tiles - 1
-    const int row_begin = offsets[g], row_end = offsets[g + 1];
+    const int row_begin = one ? 0 : offsets[g], row_end = one ? M : offsets[g + 1];
     const int64_t a_bytes = (int64_t)(row_end - row_begin) * K;
     const int64_t b_bytes = (int64_t)(SWIGLU ? 2 : 1) * n_out * K;
     int mt, nt;
@@ -822,6 +836,32 @@ hipError_t launch_grouped_gemm_big_bf16(const GroupedGemmArgs &a0, int64_t rows_
     t.out_packed = false;
   }
   return launch_grouped_gemm_stream_bf16(t, s);
+}
+
+// The router linear logits = x W_r^T as a GEMM on the large tiles: tokens as rows, the
+// router weights [E, d] as the weight rows, split along d so that the launch fills the GPU;
+// float partial sums [splits][T][E] (without the offset) for the top-k kernel to add.  Used
+// when the tiles of E columns are at least half full and the launch has 192 or more blocks;
+// returns 0 otherwise.
+int router_gemm_splits(int T, int d, int E) {
+  if (E < BG_BN / 2 || E % 8 || T < 1 || d % 32) return 0;  // the epilogue stores runs of 8 columns
+  const int tiles = ((T + BG_BM - 1) / BG_BM) * ((E + BG_BN - 1) / BG_BN);
+  const int ks = big_ksplit(tiles, d / 32, kRouterMinSteps);
+  return tiles * ks >= 192 ? ks : 0;
+}
+
+hipError_t launch_router_gemm(const void *x, const void *w_router, int T, int d, int E, float *partials,
+                              hipStream_t s) {
+  const int ks = router_gemm_splits(T, d, E);
+  if (ks < 1) return hipErrorInvalidValue;
+  const int n_tiles = (E + BG_BN - 1) / BG_BN;
+  const int64_t grid = (int64_t)((T + BG_BM - 1) / BG_BM) * n_tiles * ks;
+  // ks == 1: the kernel stores the float sums through `out` (= partials); else its partials
+  hipLaunchKernelGGL((grouped_gemm_big_kernel<false, float>), dim3((unsigned)grid), dim3(512), 0, s,
+                     static_cast<const bf16_t *>(x), nullptr, (int64_t)0, nullptr, 1,
+                     static_cast<const bf16_t *>(w_router), (int64_t)E * d, E, d, partials, n_tiles, (int64_t)0,
+                     (int64_t)0, T, ks > 1 ? partials : nullptr, (int64_t)T * E, nullptr, SwigluBwdOut{}, 0);
+  return hipGetLastError();
 }
 
 int64_t packed_weights_bytes(int G, int n_out, int K, bool swiglu) {

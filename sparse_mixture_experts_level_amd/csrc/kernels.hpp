@@ -18,6 +18,11 @@ hipError_t launch_router_logits_f32(const float *x, const float *w_router, const
 // split over d into router_splits() parts whose partial sums (router_partials_bytes()
 // of workspace) the top-k kernel adds in order.
 int router_splits(int T, int d, int E);
+// The router linear as a large-tile GEMM (gemm_big.hip) for many tokens and experts: its
+// split count along d (0: not used for this shape) and launch (float partials [S][T][E]).
+int router_gemm_splits(int T, int d, int E);
+hipError_t launch_router_gemm(const void *x, const void *w_router, int T, int d, int E, float *partials,
+                              hipStream_t s);
 size_t router_partials_bytes(int T, int d, int E);
 hipError_t launch_router_bf16(const void *x, const void *w_router, const float *offset, float *logits, int T, int d,
                               int E, int k, int32_t *ids, float *gates, int32_t *spare, float *partials,

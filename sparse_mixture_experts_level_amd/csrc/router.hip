@@ -418,6 +418,8 @@ int router_splits(int T, int d, int E) {
 }
 
 size_t router_partials_bytes(int T, int d, int E) {
+  const int G = router_gemm_splits(T, d, E);
+  if (G > 0) return (size_t)G * T * E * 4;
   const int S = router_splits(T, d, E);
   return S > 1 ? (size_t)S * T * E * 4 : 0;
 }
@@ -431,6 +433,13 @@ hipError_t launch_router_bf16(const void *x, const void *w_router, const float *
     hipLaunchKernelGGL(router_fused_kernel<1>, dim3(grid), dim3(256), 0, s, xp, wp, offset, logits, T, d, E, k, ids,
                        gates, spare);
     return hipGetLastError();
+  }
+  if (const int G = router_gemm_splits(T, d, E)) {
+    // many tokens and experts: the large-tile GEMM, its float partials added (with the
+    // offset) by the top-k kernel
+    hipError_t e = launch_router_gemm(x, w_router, T, d, E, partials, s);
+    if (e != hipSuccess) return e;
+    return router_topk(logits, T, E, k, ids, gates, spare, partials, G, offset, s);
   }
   const int S = router_splits(T, d, E);
   if (S == 1) {

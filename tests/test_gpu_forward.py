@@ -141,6 +141,19 @@ def test_forward_is_deterministic():
         assert torch.equal(ra[k], layer.routing[k]), k
 
 
+@pytest.mark.parametrize("T,d,E,k,fs", [(12288, 4096, 128, 4, 0), (12800, 4096, 192, 2, 128)])
+def test_router_linear_on_large_tiles(T, d, E, k, fs):
+    """Many tokens and experts: the router linear runs on the large-tile GEMM cut along d,
+    its float partials (and the offsets) added in order by the top-k kernel; logits,
+    routing, dispatch and sampled outputs against the oracle (192 experts: a partly filled
+    column tile)."""
+    w = wl.Workload("router-gemm", T, d, E, k, 128, 1.0, "bf16", d_ff_shared=fs, offset="zipf1.1")
+    say(f"router linear on large tiles T={T} d={d} E={E} k={k}")
+    inp = wl.make_inputs(w, seed=9, device=DEV)
+    res = _run_and_check(inp, sample=np.unique(np.concatenate([np.arange(0, T, 997), [T - 1]])))
+    say(f"  max row rel err {res['err']:.3e}, near ties {res['differ']}")
+
+
 @pytest.mark.parametrize("T,d,E,k,f,cf,fs,tiled", [
     (2048, 256, 16, 2, 128, 1.0, 0, False),     # streaming regime, no shared expert
     (1100, 256, 8, 2, 128, 1.25, 576, False),   # shared expert on large tiles with a streamed tail
