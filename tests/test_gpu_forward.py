@@ -141,6 +141,47 @@ def test_forward_is_deterministic():
         assert torch.equal(ra[k], layer.routing[k]), k
 
 
+@pytest.mark.parametrize("T,k", [(1100, 2), (700, 8)])
+def test_forward_equals_its_stages_composed(T, k):
+    """moe_forward with a shared expert on the large tiles (packed H) against the layer composed
+    from the separate entry points -- dispatch with x_perm, grouped FFN of the routed experts on
+    the permuted rows, grouped FFN of the shared expert as one group of all tokens (row-major H),
+    combine with that shared output: the same result bit for bit; the oracle agrees on every
+    token."""
+    d, E, f, fs, cf = 256, 8, 128, 576, 1.25
+    w = wl.Workload("composed", T, d, E, k, f, cf, "bf16", d_ff_shared=fs, offset="boost4")
+    say(f"forward against its stages composed T={T} k={k}")
+    inp = wl.make_inputs(w, seed=12, device=DEV)
+    cap = ops.moe_capacity(T, E, cf)
+    layer = ops.MoELayer(inp, cap)
+    got = layer.forward().clone()
+    r = layer.routing
+    desc = layer.desc
+    R = ops.moe_max_rows(desc)
+    x_perm = torch.empty((R, d), dtype=torch.bfloat16, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    slot = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    row_token = torch.empty(R, dtype=torch.int32, device=DEV)
+    ws = ops.workspace(ops.moe_workspace_size(desc))
+    ops.moe_dispatch_permute(desc, r["topk_ids"], inp.x, counts, offsets, slot, row_token, x_perm, ws)
+    y_perm = torch.empty((R, d), dtype=torch.bfloat16, device=DEV)
+    gws = ops.workspace(ops.moe_grouped_gemm_workspace_size(E, R, f, torch.bfloat16))
+    ops.moe_grouped_swiglu_gemm(E, R, min(T, cap), d, f, torch.bfloat16, x_perm, offsets, inp.w_gate_up, inp.w_down,
+                                y_perm, gws)
+    sh_out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    sh_off = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    sws = ops.workspace(ops.moe_grouped_gemm_workspace_size(1, T, fs, torch.bfloat16))
+    ops.moe_grouped_swiglu_gemm(1, T, T, d, fs, torch.bfloat16, inp.x, sh_off, inp.w_shared_gate_up,
+                                inp.w_shared_down, sh_out, sws)
+    want = torch.empty_like(got)
+    ops.moe_combine_unpermute(desc, y_perm, r["topk_ids"], r["topk_gates"], slot, offsets, sh_out, want)
+    torch.cuda.synchronize()
+    assert torch.equal(slot, r["slot"]) and torch.equal(offsets, r["expert_offsets"])
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    _run_and_check(inp)
+
+
 @pytest.mark.parametrize("T,d,E,k,fs", [(12288, 4096, 128, 4, 0), (12800, 4096, 192, 2, 128)])
 def test_router_linear_on_large_tiles(T, d, E, k, fs):
     """Many tokens and experts: the router linear runs on the large-tile GEMM cut along d,
