@@ -18,7 +18,9 @@ constexpr int CB_TOK = 4;  // wavefronts per workgroup
 // One wavefront per (token, column segment of 64 * U 16-byte vectors).  Lanes j < k
 // fetch assignment j's slot, expert and gate in parallel and resolve its row; the wave
 // then loads JU rows' vectors at a time (more loads in flight) and each lane sums its
-// columns over j in order, so the result does not depend on the segmentation.
+// columns over j in order, so the result does not depend on the segmentation.  Every
+// byte is read or written once, so loads and stores are marked non-temporal (DeepSeek-shaped
+// layer: 147 -> 130 us).
 template <bool BF16, int U, int JU>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y_perm, const int32_t *__restrict__ ids,
                                                       const float *__restrict__ gates,
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
     if (shared && c < nvec)
-      unpack(ldg16(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es), acc[u]);
+      unpack(ldg16_nt(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es), acc[u]);
   }
   for (int j0 = 0; j0 < k; j0 += 64) {
     // lane j holds assignment j0 + j: its row (or -1) and gate
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = v0 + lane + 64 * u;
-          q[jj][u] = (live[jj] && c < nvec) ? ldg16(yr + (size_t)c * VEC * es) : u32x4{0u, 0u, 0u, 0u};
+          q[jj][u] = (live[jj] && c < nvec) ? ldg16_nt(yr + (size_t)c * VEC * es) : u32x4{0u, 0u, 0u, 0u};
         }
       }
 #pragma unroll
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
         q[i] = __float_as_uint(acc[u][i]);
       }
     }
-    stg16(static_cast<uint8_t *>(out) + ((size_t)t * d + (size_t)c * VEC) * es, q);
+    stg16_nt(static_cast<uint8_t *>(out) + ((size_t)t * d + (size_t)c * VEC) * es, q);
   }
 }
 

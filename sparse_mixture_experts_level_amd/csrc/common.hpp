@@ -40,6 +40,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 16-byte vector load/store through the vector memory path.
 __device__ __forceinline__ u32x4 ldg16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void stg16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// The same, marked non-temporal: for data touched once (streamed through, not reused).
+__device__ __forceinline__ u32x4 ldg16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void stg16_nt(void *p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -222,6 +222,54 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_assign_kernel(
       [&](int64_t q) { slot[q] = -1; });  // an id outside [0, E): no expert, dropped
 }
 
+// The plain fill when one block holds every position (few assignments, e.g. a decode
+// step): the histogram, the kept counts' prefix and the ranks in one launch.
+__global__ __launch_bounds__(DP_THREADS) void dispatch_single_kernel(const int32_t *__restrict__ ids, int T, int k,
+                                                                     int E, int cap, int rank_major,
+                                                                     int32_t *__restrict__ counts,
+                                                                     int32_t *__restrict__ offsets,
+                                                                     int32_t *__restrict__ slot,
+                                                                     int32_t *__restrict__ row_token) {
+  __shared__ int32_t s_base[MOE_MAX_EXPERTS_DEV];  // running slot per expert
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS_DEV];   // demand, then kept counts, then their exclusive prefix
+  __shared__ int32_t s_part[DP_THREADS];
+  __shared__ RankLds L;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += DP_THREADS) {
+    s_base[e] = 0;
+    s_off[e] = 0;
+#pragma unroll
+    for (int w = 0; w < DP_NW; ++w) L.wtag[w][e] = -1;
+  }
+  __syncthreads();
+  const int64_t n = (int64_t)T * k;
+  for (int64_t p = tid; p < n; p += DP_THREADS) {
+    const int e = ids[fill_q(p, T, k, rank_major != 0)];
+    if (e >= 0 && e < E) atomicAdd(&s_off[e], 1);  // order-independent count
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += DP_THREADS) {
+    const int total = s_off[e];
+    counts[e] = total;
+    s_off[e] = cap < 0 ? total : min(total, cap);
+  }
+  __syncthreads();
+  const int kept_total = block_exclusive_scan(s_off, E, s_part);
+  for (int e = tid; e < E; e += DP_THREADS) offsets[e] = s_off[e];
+  if (tid == 0) offsets[E] = kept_total;
+  rank_walk(
+      ids, T, k, E, rank_major != 0, 0, n, bits_for(E), L, s_base,
+      [&](int64_t q, int e, int sl) {
+        if (cap < 0 || sl < cap) {
+          slot[q] = sl;
+          row_token[s_off[e] + sl] = int32_t(q / k);
+        } else {
+          slot[q] = -1;
+        }
+      },
+      [&](int64_t q) { slot[q] = -1; });
+}
+
 // Offers of the two-pass fill: the i-th overflowing assignment of token t (in rank
 // order j) is offered to spare[t][i], the expert ranked k + i (-1: none).
 __global__ __launch_bounds__(256) void reroute_offer_kernel(const int32_t *__restrict__ slot,
@@ -338,6 +386,11 @@ hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int cap, boo
                            int32_t *offsets, int32_t *slot, int32_t *row_token, int32_t *ws, hipStream_t s) {
   const DispatchPlan p = dispatch_plan(T, k);
   if (p.num_blocks < 1) return hipSuccess;
+  if (p.num_blocks == 1) {  // every position in one block: a single launch
+    hipLaunchKernelGGL(dispatch_single_kernel, dim3(1), dim3(DP_THREADS), 0, s, ids, T, k, E, cap, (int)rank_major,
+                       counts, offsets, slot, row_token);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(p.num_blocks), dim3(DP_THREADS), 0, s, ids, T, k, E, p.per_block,
                      (int)rank_major, ws);
   hipError_t e = hipGetLastError();
