@@ -153,15 +153,33 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
+// One step of the wavefront maximum: each lane takes the larger of its key and the key
+// of the lane that DPP control CTRL names (rows outside ROW_MASK keep theirs).  DPP moves
+// run in the vector ALU, without the LDS round trip of a lane shuffle.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+  const uint64_t o = (uint64_t(ohi) << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Maximum of a key over the 64 lanes (every lane active), returned to every lane: within
+// each quad (lane ^ 1, lane ^ 2), across the quads of each 8-lane half row (half-row
+// mirror), across the halves of each 16-lane row (row mirror), then row 0 into row 1 and
+// row 2 into row 3 (broadcast of lane 15) and rows 0-1 into rows 2-3 (broadcast of lane
+// 31); lane 63 then holds the maximum of all lanes.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor(uint32_t(v), m, 64);
-    const uint32_t hi = __shfl_xor(uint32_t(v >> 32), m, 64);
-    const uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xb1>(v);       // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4e>(v);       // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141>(v);      // row_half_mirror
+  v = dpp_max_step<0x140>(v);      // row_mirror
+  v = dpp_max_step<0x142, 0xa>(v); // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v); // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return (uint64_t(hi) << 32) | lo;
 }
 
 constexpr int TK_WAVES = 4;
