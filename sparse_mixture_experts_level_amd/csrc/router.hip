@@ -153,38 +153,39 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
-// One step of the wavefront maximum: each lane takes the larger of its key and the key
+// One step of the wavefront maximum: each lane takes the larger of its value and the value
 // of the lane that DPP control CTRL names (rows outside ROW_MASK keep theirs).  DPP moves
 // run in the vector ALU, without the LDS round trip of a lane shuffle.
 template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
-  const uint64_t o = (uint64_t(ohi) << 32) | olo;
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
   return o > v ? o : v;
 }
 
-// Maximum of a key over the 64 lanes (every lane active), returned to every lane: within
+// Maximum of a value over the 64 lanes (every lane active), returned to every lane: within
 // each quad (lane ^ 1, lane ^ 2), across the quads of each 8-lane half row (half-row
 // mirror), across the halves of each 16-lane row (row mirror), then row 0 into row 1 and
 // row 2 into row 3 (broadcast of lane 15) and rows 0-1 into rows 2-3 (broadcast of lane
 // 31); lane 63 then holds the maximum of all lanes.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = dpp_max_step<0xb1>(v);       // quad_perm [1, 0, 3, 2]
   v = dpp_max_step<0x4e>(v);       // quad_perm [2, 3, 0, 1]
   v = dpp_max_step<0x141>(v);      // row_half_mirror
   v = dpp_max_step<0x140>(v);      // row_mirror
   v = dpp_max_step<0x142, 0xa>(v); // row_bcast:15 into rows 1 and 3
   v = dpp_max_step<0x143, 0xc>(v); // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return (uint64_t(hi) << 32) | lo;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 constexpr int TK_WAVES = 4;
 
 // Selection for token t from the keys of its logits (lane holds experts lane + 64 v).
+// Each lane first sorts its VPL keys (descending), so its first key is its candidate.  A
+// round takes the largest candidate of the wavefront: the maximum of the candidates' high
+// words (the logit order) over the lanes; when several lanes hold that maximum (equal
+// logits), the maximum of their low words (the smallest expert) decides.  That is the
+// maximum of the whole 64-bit keys, found with 32-bit lane reductions.  The winning lane
+// then drops its candidate (its next key moves up; 0 ranks below every real key).
 // Every lane follows the k rounds identically (same winner, same running sum of
 // exp(l_j - l_max) in the same order); lane (j mod 64) keeps winner j in register
 // slot j / 64 and writes it at the end.  No LDS and no barriers.  With `spare`, the
@@ -194,6 +195,16 @@ template <int VPL>
 __device__ __forceinline__ void topk_select(uint64_t (&key)[VPL], int E, int k, int64_t t, int lane,
                                             int32_t *__restrict__ ids, float *__restrict__ gates,
                                             int32_t *__restrict__ spare) {
+  // odd-even transposition sort of the lane's keys, descending
+#pragma unroll
+  for (int p = 0; p < VPL; ++p)
+#pragma unroll
+    for (int i = p & 1; i + 1 < VPL; i += 2) {
+      const uint64_t hi = key[i] > key[i + 1] ? key[i] : key[i + 1];
+      const uint64_t lo = key[i] > key[i + 1] ? key[i + 1] : key[i];
+      key[i] = hi;
+      key[i + 1] = lo;
+    }
   int my_id[VPL], my_sp[VPL];
   float my_z[VPL];
 #pragma unroll
@@ -205,14 +216,22 @@ __device__ __forceinline__ void topk_select(uint64_t (&key)[VPL], int E, int k, 
   float m = 0.f, sum = 0.f;
   const int rounds = spare ? min(2 * k, E) : k;
   for (int j = 0; j < rounds; ++j) {
-    uint64_t best = 0;
+    const uint32_t hv = uint32_t(key[0] >> 32), lv = uint32_t(key[0]);
+    const uint32_t hmax = wave_max_u32(hv);
+    const uint64_t tie = __ballot(hv == hmax);
+    uint32_t lmax;
+    if (__popcll(tie) == 1) {
+      lmax = (uint32_t)__builtin_amdgcn_readlane((int)lv, __ffsll((unsigned long long)tie) - 1);
+    } else {
+      lmax = wave_max_u32(hv == hmax ? lv : 0u);
+    }
+    const uint64_t best = (uint64_t(hmax) << 32) | lmax;
+    const int e = 0xffff - int(lmax & 0xffffu);
+    // the winning lane drops its candidate (keys are distinct: exactly one lane matches)
+    const bool win = key[0] == best;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-    best = wave_max_u64(best);
-    const int e = 0xffff - int(best & 0xffffu);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (key[v] == best) key[v] = 0ull;
+    for (int v = 0; v + 1 < VPL; ++v) key[v] = win ? key[v + 1] : key[v];
+    key[VPL - 1] = win ? 0ull : key[VPL - 1];
     if (j < k) {
       const float val = key_value(best);
       if (j == 0) m = val;
@@ -246,10 +265,12 @@ __device__ __forceinline__ void topk_select(uint64_t (&key)[VPL], int E, int k, 
   }
 }
 
-// One wavefront per token: the token's logits (with `partials`, S splits of the router
-// linear, first formed as the splits' sum in order s = 0..S-1 plus the offset, and
-// written to `logits`), then topk_select.
-template <int VPL>
+// One wavefront per token: the token's logits (with `partials`, S <= SMAX splits of the
+// router linear, first formed as the splits' sum in order s = 0..S-1 plus the offset, and
+// written to `logits`), then topk_select.  Every load of a group of up to four splits is
+// issued before the first is used (addresses clamped into the arrays, values past E or S
+// discarded), so a wave waits for memory once per group rather than once per load.
+template <int VPL, int SMAX>  // SMAX = 0: read the logits
 __global__ __launch_bounds__(256) void router_topk_kernel(float *__restrict__ logits, int T, int E, int k,
                                                           int32_t *__restrict__ ids, float *__restrict__ gates,
                                                           int32_t *__restrict__ spare,
@@ -259,22 +280,45 @@ __global__ __launch_bounds__(256) void router_topk_kernel(float *__restrict__ lo
   const int t = blockIdx.x * TK_WAVES + wave;
   if (t >= T) return;
   float *row = logits + (size_t)t * E;
+  int ec[VPL];  // this lane's experts, clamped into [0, E)
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) ec[v] = min(lane + 64 * v, E - 1);
+  float val[VPL];
+  if constexpr (SMAX == 0) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) val[v] = row[ec[v]];
+  } else {
+    constexpr int G = SMAX < 4 ? SMAX : 4;  // splits loaded together
+    float off[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      val[v] = 0.f;
+      off[v] = offset ? offset[ec[v]] : 0.f;
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < SMAX; s0 += G) {
+      float part[G][VPL];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const size_t sp = (size_t)min(s0 + g, S - 1);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) part[g][v] = partials[(sp * T + t) * E + ec[v]];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (s0 + g < S) val[v] += part[g][v];
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if (offset) val[v] += off[v];
+      if (lane + 64 * v < E) row[lane + 64 * v] = val[v];
+    }
+  }
   uint64_t key[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane + 64 * v;
-    float val = 0.f;
-    if (e < E) {
-      if (partials) {
-        for (int sp = 0; sp < S; ++sp) val += partials[((size_t)sp * T + t) * E + e];
-        if (offset) val += offset[e];
-        row[e] = val;
-      } else {
-        val = row[e];
-      }
-    }
-    key[v] = e < E ? topk_key(val, e) : 0ull;  // 0 ranks below every real key
-  }
+  for (int v = 0; v < VPL; ++v) key[v] = lane + 64 * v < E ? topk_key(val[v], lane + 64 * v) : 0ull;  // 0 ranks below every real key
   topk_select<VPL>(key, E, k, t, lane, ids, gates, spare);
 }
 
@@ -392,12 +436,22 @@ hipError_t router_logits_bf16(const void *x, const void *w_router, const float *
 
 hipError_t router_topk(float *logits, int T, int E, int k, int32_t *ids, float *gates, int32_t *spare,
                        const float *partials, int S, const float *offset, hipStream_t s) {
+  if (partials && (S < 1 || S > 8)) return hipErrorInvalidValue;
   const int grid = (T + TK_WAVES - 1) / TK_WAVES;
   const int vpl = (E + 63) / 64;
-#define TK_CASE(V)                                                                                             \
-  case V:                                                                                                      \
-    hipLaunchKernelGGL(router_topk_kernel<V>, dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates, spare, \
-                       partials, S, offset);                                                                   \
+  const int smax = !partials ? 0 : S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : 8;
+#define TK_LAUNCH(V, SM)                                                                                       \
+  hipLaunchKernelGGL((router_topk_kernel<V, SM>), dim3(grid), dim3(256), 0, s, logits, T, E, k, ids, gates,   \
+                     spare, partials, S, offset)
+#define TK_CASE(V)                  \
+  case V:                           \
+    switch (smax) {                 \
+      case 0: TK_LAUNCH(V, 0); break; \
+      case 1: TK_LAUNCH(V, 1); break; \
+      case 2: TK_LAUNCH(V, 2); break; \
+      case 4: TK_LAUNCH(V, 4); break; \
+      default: TK_LAUNCH(V, 8); break; \
+    }                               \
     break;
   switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
     TK_CASE(1)
@@ -407,6 +461,7 @@ hipError_t router_topk(float *logits, int T, int E, int k, int32_t *ids, float *
     TK_CASE(16)
   }
 #undef TK_CASE
+#undef TK_LAUNCH
   return hipGetLastError();
 }
 
