@@ -61,6 +61,10 @@ def parse(argv=None):
     p.add_argument("--tiled", choices=("auto", "on", "off"), default="auto",
                    help="tile-major copies of the routed (shared) expert weights, prepared once before timing "
                         "(auto: when the routed experts (the shared expert) take the large-tile regime)")
+    p.add_argument("--zero-expert-weights", action="store_true",
+                   help="diagnostic: the routed and shared expert weights all zero (routing unchanged, every kernel "
+                        "still runs on the same shapes), to show how the matrix cores' clock depends on operand "
+                        "values; not a throughput figure")
     p.add_argument("--ep-shards", type=int, default=1, metavar="N",
                    help="time one expert-parallel rank's share instead of the whole layer: experts split in N "
                         "contiguous ranges, every range timed on this GPU, the slowest one reported")
@@ -164,6 +168,10 @@ def main(argv=None):
     w = wl.get_workload(args.workload)
     print(f"[bench] {w.name}: drawing inputs", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, seed=args.seed, device=dev)
+    if args.zero_expert_weights:
+        for t in (inp.w_gate_up, inp.w_down, inp.w_shared_gate_up, inp.w_shared_down):
+            if t is not None:
+                t.zero_()
     cap = ops.moe_capacity(w.num_tokens, w.num_experts, w.capacity_factor)
     T, d, E, k, f, fs = w.num_tokens, w.d_model, w.num_experts, w.top_k, w.d_ff, w.d_ff_shared
     desc = ops.make_desc(T, d, f, E, k, cap, fs, w.torch_dtype)
@@ -288,7 +296,8 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic",
+        "data": "synthetic, expert weights all zero (diagnostic, not a throughput figure)" if args.zero_expert_weights
+                else "synthetic",
         "config": {"workload": w.name, "description": w.description, "num_tokens": T, "d_model": d,
                    "num_experts": E, "top_k": k, "d_ff": f, "d_ff_shared": fs, "capacity": cap,
                    "kept_rows": R, "experts_touched": E_t, "drops": int(T * k - R),
