@@ -71,6 +71,13 @@ def parse(argv=None):
     return p.parse_args(argv)
 
 
+def device_info(torch) -> dict:
+    """The GPU the line was measured on, as the runtime reports it."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def source_hash(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -313,6 +320,7 @@ def main(argv=None):
         "phases": phases,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
         "cpu_baseline": cpu,
+        "device": device_info(torch),
     }
     print(json.dumps(line), flush=True)
 

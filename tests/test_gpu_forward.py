@@ -195,6 +195,20 @@ def test_router_linear_on_large_tiles(T, d, E, k, fs):
     say(f"  max row rel err {res['err']:.3e}, near ties {res['differ']}")
 
 
+@pytest.mark.parametrize("d,splits", [(384, 3), (640, 5), (768, 6), (896, 7), (1024, 8)])
+def test_router_split_counts(d, splits):
+    """Few tokens, long rows: the router linear is cut along d into `splits` workgroups per
+    token block and the top-k kernel adds their float partials (in groups of up to four loads
+    issued together; counts that fill a group only in part included) plus the offsets;
+    logits, routing and outputs against the oracle."""
+    T, E = 64, 32
+    assert splits == min(8, (d // 64) // 2)  # the split rule for one 64-token block of <= 256 experts
+    w = wl.Workload("router-splits", T, d, E, 2, 128, None, "bf16", offset="zipf1.1")
+    say(f"router split over d: T={T} d={d} E={E} splits={splits}")
+    inp = wl.make_inputs(w, seed=d, device=DEV)
+    _run_and_check(inp)
+
+
 @pytest.mark.parametrize("T,d,E,k,f,cf,fs,tiled", [
     (2048, 256, 16, 2, 128, 1.0, 0, False),     # streaming regime, no shared expert
     (1100, 256, 8, 2, 128, 1.25, 576, False),   # shared expert on large tiles with a streamed tail
