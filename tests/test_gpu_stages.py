@@ -396,6 +396,10 @@ def test_gate_up_row_gather(sizes, d, f, dtype, hint):
     (300, 8, 2, 40, 256, torch.bfloat16, False), (300, 8, 2, 40, 256, torch.bfloat16, True),
     (100, 64, 1, 2, 1024, torch.bfloat16, False), (50, 32, 8, None, 64, torch.float32, True),
     (10, 4, 4, 1, 30, torch.float32, False),
+    # enough tokens for two 16-byte vectors per lane: rows fetched two at a time, one at a
+    # time (k = 1), and a last column segment only partly filled (130 vectors of 128 + 2)
+    (4096, 16, 2, 600, 1024, torch.bfloat16, True), (4200, 8, 1, None, 512, torch.float32, False),
+    (4096, 8, 3, None, 520, torch.float32, True),
 ])
 def test_combine(T, E, k, cap, d, dtype, shared):
     say(f"combine T={T} E={E} k={k} cap={cap} d={d} {dtype} shared={shared}")
