@@ -72,10 +72,22 @@ def parse(argv=None):
 
 
 def device_info(torch) -> dict:
-    """The GPU the line was measured on, as the runtime reports it."""
+    """The GPU the line was measured on, as the runtime reports it (and rocminfo's maximum
+    engine clock of the first gfx950 agent, when rocminfo is there)."""
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
-            "memory_gib": round(p.total_memory / 2**30, 1)}
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "max_clock_mhz": None}
+    try:
+        import subprocess
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        agent = txt[txt.index("gfx950"):] if "gfx950" in txt else ""
+        for line in agent.splitlines():
+            if "Max Clock Freq" in line:
+                info["max_clock_mhz"] = int(line.split(":")[1].split()[0])
+                break
+    except Exception:  # the clock is context only
+        pass
+    return info
 
 
 def source_hash(paths) -> str:
