@@ -37,9 +37,10 @@ from sparse_mixture_experts_level_amd import workloads as wl  # noqa: E402
 
 
 def test_tail_rows_follows_the_tail_rule():
-    # the Mixtral-shaped layer's routed groups: three last tiles of <= 128 rows (47, 9, 37)
-    rows = [1006, 1021, 1071, 1016, 1009, 1033, 1061, 975]
-    assert bench.tail_rows(rows, 4096) == 47 + 9 + 37
+    # the Mixtral-shaped layer's routed groups (seed 0, drawn on the GPU): five last tiles of
+    # <= 128 rows (11, 54, 32, 30, 27); the 214-, 225- and 175-row ones stay in large tiles
+    rows = [982, 1035, 993, 1078, 943, 1056, 1054, 1051]
+    assert bench.tail_rows(rows, 4096) == 11 + 54 + 32 + 30 + 27
     # a tail launch of 8 groups x 16 column tiles would be too small to run: no tails
     assert bench.tail_rows(rows, 1024) == 0
     assert bench.tail_rows([256, 512, 0], 1 << 20) == 0  # whole tiles and empty groups leave none

@@ -343,6 +343,9 @@ def test_grouped_gemm_bf16_wide():
     # eight groups x 4096 columns: gate_up leaves last tiles of <= 128 rows to a streaming
     # launch (44, 88 and 8 rows; a 40-row group entirely), keeps 188- and 130-row ones
     ([300, 600, 40, 520, 700, 256, 130, 0], 256, 4096),
+    # 72 groups (the tail launch maps workgroups to tail groups only up to 64 groups): in
+    # every eight, tails of 44, 4, 34, 1 and 14 rows and a 144-row last tile kept
+    ([300, 260, 256, 400, 290, 0, 513, 270] * 9, 128, 512),
 ])
 def test_grouped_gemm_bf16_large_groups(sizes, d, f):
     """Average group of >= 256 rows: the 256 x 256 MFMA tile kernel."""
