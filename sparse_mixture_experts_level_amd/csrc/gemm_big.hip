@@ -14,9 +14,10 @@
 // accumulators of a column sit in the same lane.
 //
 // Tiles: each group contributes ceil(rows / 256) row tiles times the column tiles.
-// A block finds its group from the offsets (one wavefront scan), and walks the
-// group's tiles with the larger operand outermost, so the smaller one is reused
-// from cache.
+// A block finds its group from the offsets (one wavefront scan).  When the group's
+// weights are the larger operand, its tiles are walked weight tile outermost, so the row
+// tiles that share a weight tile run together and reuse it from cache; otherwise in bands
+// of four row tiles, weight tile outer within a band.
 #include <algorithm>
 
 #include "common.hpp"

@@ -21,7 +21,8 @@
 // reused by every column tile of the expert) go straight from memory into LDS with
 // buffer loads that target LDS (no registers), in 64-wide K chunks, XOR-swizzled by
 // row so the 16-lane column reads of the MFMA layout spread over distinct banks.
-// Both operands run two chunks ahead through three register slots / LDS stages.
+// Both operands run S - 1 chunks ahead through S register slots / LDS stages (three for
+// gate_up, four for the down projection).  bf16 results leave as whole 16-byte pieces.
 // Row blocks of BM rows are walked in order, so any group size is computed
 // correctly; 16-row subtiles beyond the group's rows skip their MFMAs.
 #include "common.hpp"
