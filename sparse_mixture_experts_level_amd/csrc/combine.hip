@@ -48,26 +48,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
       }
     }
   };
-  float acc[U][VEC];
+  // Lane j < k: assignment j's slot, expert and gate (the first 64), loaded before the
+  // shared expert's row so that the two are in flight together: the wave's chain of
+  // dependent loads is then slots and shared row, the experts' first rows, the rows
+  // (DeepSeek-shaped layer: 94 -> 88 us).  Staging all first rows in LDS per workgroup
+  // instead, to drop the middle link, measured 90-92 us (a barrier per workgroup).
+  auto fetch = [&](int j0, int &sl, int &e, float &gt) {
+    sl = -1;
+    e = 0;
+    gt = 0.f;
+    if (j0 + lane < k) {
+      const size_t q = (size_t)t * k + j0 + lane;
+      sl = slot[q];
+      e = ids[q];
+      gt = gates[q];
+    }
+  };
+  int f_sl, f_e;
+  float f_g;
+  fetch(0, f_sl, f_e, f_g);
+  u32x4 shq[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = v0 + lane + 64 * u;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
-    if (shared && c < nvec)
-      unpack(ldg16_nt(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es), acc[u]);
+    shq[u] = (shared && c < nvec) ? ldg16_nt(static_cast<const uint8_t *>(shared) + ((size_t)t * d + (size_t)c * VEC) * es)
+                                  : u32x4{0u, 0u, 0u, 0u};
   }
+  float acc[U][VEC];
+#pragma unroll
+  for (int u = 0; u < U; ++u) unpack(shq[u], acc[u]);
   for (int j0 = 0; j0 < k; j0 += 64) {
     // lane j holds assignment j0 + j: its row (or -1) and gate
+    if (j0 > 0) fetch(j0, f_sl, f_e, f_g);
     int64_t my_row = -1;
-    float my_gate = 0.f;
-    if (j0 + lane < k) {
-      const size_t q = (size_t)t * k + j0 + lane;
-      const int sl = slot[q];
-      const int e = ids[q];
-      my_gate = gates[q];
-      if (sl >= 0 && e >= e_begin && e < e_end) my_row = (int64_t)offsets[e] + sl;
-    }
+    const float my_gate = f_g;
+    if (f_sl >= 0 && f_e >= e_begin && f_e < e_end) my_row = (int64_t)offsets[f_e] + f_sl;
     const int kn = min(64, k - j0);
     for (int j1 = 0; j1 < kn; j1 += JU) {
       u32x4 q[JU][U];
@@ -153,10 +168,10 @@ hipError_t launch_combine(const void *y_perm, const int32_t *ids, const float *g
   if (d % vec == 0) {
     // Two vectors per lane when there are tokens enough to fill the GPU, else one vector
     // per lane and more wavefronts per token; rows fetched two at a time when a token has
-    // several.  Each wavefront waits through a chain of dependent loads (slot and expert,
-    // then the expert's offset, then the rows), so the kernel lives on many resident
-    // wavefronts: four vectors per lane and four rows at a time (more registers, fewer
-    // wavefronts) took 131 us against 95 us on the DeepSeek-shaped layer.
+    // several.  Each wavefront waits through a chain of dependent loads (slot and expert
+    // with the shared row, then the expert's offset, then the rows), so the kernel lives on
+    // many resident wavefronts: four vectors per lane and four rows at a time (more
+    // registers, fewer wavefronts) took 131 us against 95 us on the DeepSeek-shaped layer.
     const int nvec = d / vec;
     const bool wide = (int64_t)T * ((nvec + 127) / 128) >= 4096;
     const int U = wide && nvec >= 128 ? 2 : 1;
