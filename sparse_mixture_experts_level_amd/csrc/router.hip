@@ -155,10 +155,13 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 // One step of the wavefront maximum: each lane takes the larger of its value and the value
 // of the lane that DPP control CTRL names (rows outside ROW_MASK keep theirs).  DPP moves
-// run in the vector ALU, without the LDS round trip of a lane shuffle.
+// run in the vector ALU, without the LDS round trip of a lane shuffle.  The moved value
+// of a row outside ROW_MASK is 0, the identity of the unsigned maximum, which lets the
+// compiler fold the move into the maximum (one v_max_u32 with a DPP source per step instead
+// of two copies and a maximum).
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
   return o > v ? o : v;
 }
 
