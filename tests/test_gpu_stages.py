@@ -403,6 +403,8 @@ def test_gate_up_row_gather(sizes, d, f, dtype, hint):
     # time (k = 1), and a last column segment only partly filled (130 vectors of 128 + 2)
     (4096, 16, 2, 600, 1024, torch.bfloat16, True), (4200, 8, 1, None, 512, torch.float32, False),
     (4096, 8, 3, None, 520, torch.float32, True),
+    # more than 64 assignments per token: the wave reads a second group of slots
+    (40, 96, 70, 8, 128, torch.bfloat16, True), (30, 80, 66, None, 64, torch.float32, False),
 ])
 def test_combine(T, E, k, cap, d, dtype, shared):
     say(f"combine T={T} E={E} k={k} cap={cap} d={d} {dtype} shared={shared}")
