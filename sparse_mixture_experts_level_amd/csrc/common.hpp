@@ -139,7 +139,11 @@ __device__ __forceinline__ int total_row_blocks(const int32_t *offsets, int G, i
   return sum;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z sigmoid(z), the sigmoid with the hardware reciprocal (about 1 ulp) instead of
+// an IEEE division: the SwiGLU epilogue evaluates it for every output of a large tile while
+// the matrix cores wait (Mixtral-shaped gate_up 1475 -> 1443 us), and its result is rounded
+// to bf16.  z -> -inf gives -0, as the division does.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // sigmoid(z) with the hardware reciprocal (about 1 ulp): for gradients rounded to bf16.
 __device__ __forceinline__ float sigmoid_fast(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
