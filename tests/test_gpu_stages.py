@@ -296,13 +296,13 @@ def test_router_logits(T, d, E, dtype):
 
 # ------------------------------------------------------------------------------------- grouped GEMM
 
-def _gemm_case(sizes, d, f, dtype, hint, seed=0):
+def _gemm_case(sizes, d, f, dtype, hint, seed=0, x_scale=1.0):
     G = len(sizes)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     R = int(offs[-1]) + 5  # spare rows beyond the last group stay untouched
-    say(f"grouped_gemm G={G} sizes={sizes} d={d} f={f} {dtype} hint={hint}")
+    say(f"grouped_gemm G={G} sizes={sizes} d={d} f={f} {dtype} hint={hint} x_scale={x_scale}")
     g = torch.Generator(device=DEV).manual_seed(seed)
-    x = torch.randn((R, d), generator=g, device=DEV).to(dtype)
+    x = (torch.randn((R, d), generator=g, device=DEV) * x_scale).to(dtype)
     wgu = (torch.randn((G, 2 * f, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
     wd = (torch.randn((G, d, f), generator=g, device=DEV) / math.sqrt(f)).to(dtype)
     y = torch.full((R, d), 3.0, dtype=dtype, device=DEV)
@@ -350,6 +350,14 @@ def test_grouped_gemm_bf16_wide():
 def test_grouped_gemm_bf16_large_groups(sizes, d, f):
     """Average group of >= 256 rows: the 256 x 256 MFMA tile kernel."""
     _gemm_case(sizes, d, f, torch.bfloat16, max(sizes), seed=len(sizes))
+
+
+@pytest.mark.parametrize("sizes,hint", [([40, 3, 100], 128), ([600, 0, 300], 600)])
+def test_grouped_gemm_bf16_large_preactivations(sizes, hint):
+    """Gate pre-activations in the hundreds (x scaled by 100): silu saturates to -0 for very
+    negative ones (exp overflows to inf) and to the identity for very positive ones, in the
+    streaming and the large-tile kernels' SwiGLU epilogues."""
+    _gemm_case(sizes, 256, 192, torch.bfloat16, hint, seed=3, x_scale=100.0)
 
 
 @pytest.mark.parametrize("sizes,d,f", [([0, 1, 17, 70, 5], 100, 72), ([10], 128, 256), ([3, 4], 7, 5)])
