@@ -370,17 +370,29 @@ __global__ __launch_bounds__(256) void router_fused_kernel(const bf16_t *__restr
   for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < P - 1; ++s) issue(s, c_lo + s);
-  for (int c0 = c_lo; c0 < c_hi; c0 += P) {
+  // Main loop, P chunks per trip, while every chunk it issues lies inside the wave's range:
+  // no exit inside the trip, so the loads stay in flight across its back edge.
+  int c0 = c_lo;
+  for (; c0 + 2 * P - 2 < c_hi; c0 += P) {
 #pragma unroll
     for (int s = 0; s < P; ++s) {
-      const int c = c0 + s;
-      if (c >= c_hi) break;
-      issue((s + P - 1) % P, c + P - 1);
+      issue((s + P - 1) % P, c0 + s + P - 1);
 #pragma unroll
       for (int n = 0; n < NSUB; ++n)
 #pragma unroll
         for (int h = 0; h < 2; ++h) acc[n] = mfma16(sa[s][h], sw[s][n][h], acc[n]);
     }
+  }
+  // the last chunks (fewer than 2P - 1)
+#pragma unroll
+  for (int s = 0; s < 2 * P - 1; ++s) {
+    const int c = c0 + s;
+    if (c >= c_hi) break;
+    if (c + P - 1 < c_hi) issue((s + P - 1) % P, c + P - 1);
+#pragma unroll
+    for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[n] = mfma16(sa[s % P][h], sw[s % P][n][h], acc[n]);
   }
   // C layout: lane holds expert n * 16 + (lane & 15), tokens 4 (lane >> 4) + i
 #pragma unroll
