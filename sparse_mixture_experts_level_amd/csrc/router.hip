@@ -83,27 +83,34 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const bf16_t *_
   for (int s = 0; s < P - 1; ++s) issue(slot[s], s);
   stage(slot[0], 0);
   __syncthreads();
-  for (int c0 = 0; c0 < nk; c0 += P) {
+  // one chunk: issue chunk it + P - 1 into the slot chunk it - 1 used, multiply chunk it,
+  // stage chunk it + 1's router weights in the other LDS buffer
+  auto step = [&](int it, int s) {
+    issue(slot[(s + P - 1) % P], it + P - 1);
+    const int buf = it & 1;
 #pragma unroll
-    for (int s = 0; s < P; ++s) {
-      const int it = c0 + s;
-      if (it >= nk) break;
-      issue(slot[(s + P - 1) % P], it + P - 1);
-      const int buf = it & 1;
+    for (int n = 0; n < NSUB; ++n) {
+      const int row = n * 16 + (lane & 15);
 #pragma unroll
-      for (int n = 0; n < NSUB; ++n) {
-        const int row = n * 16 + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c = ks * 4 + (lane >> 4);
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]);
-          acc[n] = mfma16(slot[s].a[ks], b, acc[n]);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + (lane >> 4);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(&lds[buf][(row * 8 + (c ^ (row & 7))) * 16]);
+        acc[n] = mfma16(slot[s].a[ks], b, acc[n]);
       }
-      if (it + 1 < nk) stage(slot[(s + 1) % P], (it + 1) & 1);
-      __syncthreads();
     }
+    if (it + 1 < nk) stage(slot[(s + 1) % P], (it + 1) & 1);
+    __syncthreads();
+  };
+  // Main loop, P chunks per trip with no exit inside a trip, so the loads in flight stay in
+  // flight across its back edge (with an exit the compiler drained them at every trip).
+  int c0 = 0;
+  for (; c0 + P <= nk; c0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) step(c0 + s, s);
   }
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s)
+    if (c0 + s < nk) step(c0 + s, s);
 
   // C layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4) + i.
 #pragma unroll
