@@ -435,16 +435,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_big_kernel(const bf16_t *
     wait_next();
     bar();
     if (second) bar();
-    for (int k0 = 0; k0 < nk; k0 += NBUF) {
+    // Whole trips of NBUF steps, then the rest: with an exit inside the trip the compiler
+    // lost track, at the loop head, of which stage each in-flight load fills, and waited
+    // there for all but the newest step's loads before the first fragment read.
+    int k0 = 0;
+    for (; k0 + NBUF <= nk; k0 += NBUF) {
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
-        const int kt = k0 + b;
-        if (kt >= nk) break;
-        mem(kt, b);
+        mem(k0 + b, b);
         bar();
         comp();
         bar();
       }
+    }
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) {
+      if (k0 + b >= nk) break;
+      mem(k0 + b, b);
+      bar();
+      comp();
+      bar();
     }
     if (!second) bar();
   }
