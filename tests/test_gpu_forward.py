@@ -346,6 +346,7 @@ def test_large_tile_tails_in_the_packed_forward():
 @pytest.mark.parametrize("T,d,E,k,f", [
     (2400, 4096, 8, 1, 4096),  # both packed projections, with streamed tails
     (2048, 320, 4, 2, 704),    # ragged weight tiles: 5.5 gate_up tiles of 128, 1.25 down tiles of 256
+    (2048, 320, 4, 2, 4096),   # packed x rows over 10 K steps: row packing in spans of 4, 4 and 2
 ])
 def test_tile_major_weights_give_the_same_forward(T, d, E, k, f):
     """The large-tile regime reading the routed weights' tile-major copies computes exactly
